@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the Mamba-2 SSD chunked forward pass on one MI355X.
+
+One step = one whole forward (chunk cumsum, state pass, chunk output) over the
+16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints one
+JSON line:  tokens/s of ``ssd_forward``; per-stage durations from HIP events
+recorded on the launch stream; the roofline of the dominant kernel from its
+algorithmic bytes and flops; and the fp64 CPU oracle timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def algorithmic(w):
+    """Bytes and flops each kernel must move/compute for workload w (one launch).
+
+    Per (token, head), e = input element bytes, s = snapshot element bytes:
+      cumsum:     e (dt) + 8 (G2 and dtT written, fp32)
+      state pass: e*P (x) + 8 (G2, dtT) + e*N*G/H (B, shared by a group) + s*P*N/Q (S written)
+                  + 8*P*N per (batch, head) for h0 and hT;  flops 2*N*P
+      chunk out:  2*e*P (x, y) + 8 (G2, dtT) + 2*e*N*G/H (B, C) + s*P*N/Q (S read);
+                  flops 2*N*P + (Q+1)*P + (Q+1)*N*G/H  (causal lower triangle, C B^T once per group)
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    s = e
+    P, N, Q, G, H = w.headdim, w.dstate, w.chunk, w.ngroups, w.nheads
+    th = w.batch * w.seqlen * H          # (token, head) pairs
+    bh = w.batch * H
+    return {
+        "chunk_cumsum": {"bytes": th * (e + 8), "flops": 2 * th},
+        "state_pass": {"bytes": th * (e * P + 8 + e * N * G / H + s * P * N / Q)
+                       + (8 * P * N * bh if w.has_h0 else 4 * P * N * bh),
+                       "flops": th * 2 * N * P},
+        "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),
+                      "flops": th * (2 * N * P + (Q + 1) * P + (Q + 1) * N * G / H)},
+    }
+
+
+def cpu_baseline(w, inp, budget_s=20.0):
+    """Time the fp64 oracle (as it stands) on this host over a sample of (batch, head) units."""
+    import oracle
+    nthr = oracle.default_threads()
+    units_all = w.batch * w.nheads
+    # calibrate on one unit, then size the sample to roughly budget_s of wall time
+    t0 = time.perf_counter()
+    oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                   units=[0], want_y=True, nthreads=1)
+    one = time.perf_counter() - t0
+    n_units = max(1, min(units_all, int(budget_s / max(one, 1e-6) * min(nthr, units_all))))
+    threads = min(nthr, n_units)
+    units = list(range(n_units))
+    t0 = time.perf_counter()
+    oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                   units=units, want_y=True, nthreads=threads)
+    el = time.perf_counter() - t0
+    tok = w.batch * w.seqlen * n_units / units_all
+    return {"value": tok / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_units} of {units_all} (batch, head) units over all {w.seqlen} tokens "
+                      f"(fp64 sequential recurrence, y and hT); tokens/s = tokens x sampled "
+                      f"fraction of heads / wall time {el:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import state_space_sequence_cumsum_amd as ssd
+    from state_space_sequence_cumsum_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w, seed=0)
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    io = d["x"].dtype
+    y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, device=dev, dtype=io)
+    hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev, dtype=torch.float32)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    ws = ssd.workspace_for(prob, dev)
+    g2_off, dtt_off, s_off = ssd.ssd_workspace_layout(prob)
+    nc, Lp = w.nchunks, w.nchunks * w.chunk
+    G2 = ws[g2_off:g2_off + 4 * w.batch * w.nheads * Lp].view(torch.float32).view(w.batch, w.nheads, Lp)
+    dtT = ws[dtt_off:dtt_off + 4 * w.batch * w.nheads * Lp].view(torch.float32).view(w.batch, w.nheads, Lp)
+    es = 2 if w.dtype == "bf16" else 4
+    S = ws[s_off:s_off + es * w.batch * w.nheads * nc * w.headdim * w.dstate]
+    S = S.view(io).view(w.batch, w.nheads, nc, w.headdim, w.dstate)
+    stream = torch.cuda.current_stream(dev)
+
+    def forward():
+        ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                        y=y, hT=hT, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+
+    # --- timed region: K whole forwards through the C ABI ---
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        forward()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # --- the same K steps, stage by stage, HIP events on the launch stream ---
+    names = ["chunk_cumsum", "state_pass", "chunk_out"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        e = evs[k]
+        e[0].record(stream)
+        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, stream=stream)
+        e[1].record(stream)
+        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"], S, hT, stream=stream)
+        e[2].record(stream)
+        ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"], y, stream=stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)]
+           for i, n in enumerate(names)}   # microseconds
+    kern = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
+                "min_us": min(v)} for n, v in per.items()}
+
+    alg = algorithmic(w)
+    for n in names:
+        t = kern[n]["mean_us"] * 1e-6
+        kern[n]["GB_s"] = alg[n]["bytes"] / t / 1e9
+        kern[n]["TFLOP_s"] = alg[n]["flops"] / t / 1e12
+        kern[n]["frac_hbm"] = kern[n]["GB_s"] / HBM_PEAK_GBS
+        peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+        if n != "chunk_cumsum":
+            kern[n]["frac_mfma"] = kern[n]["TFLOP_s"] / peak
+    dom = max(("state_pass", "chunk_out"), key=lambda n: kern[n]["mean_us"])
+    roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["GB_s"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": int(alg[dom]["bytes"]),
+            "mean_launch_us": round(kern[dom]["mean_us"], 2)}
+
+    ms = elapsed / args.steps * 1e3
+    tokens = w.batch * w.seqlen
+    out = {
+        "metric": "SSD forward tokens/s at L=16K, N=256; % of MFMA/HBM roofline per kernel",
+        "value": tokens * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "initial_state": w.has_h0, "accumulate": "fp32"},
+        "kernels": {n: {k: round(v, 4) for k, v in kern[n].items()} for n in names},
+        "stage_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

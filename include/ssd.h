@@ -1,0 +1,130 @@
+/*
+ * ssd.h -- C ABI of libssd, the MI355X (gfx950) Mamba-2 SSD chunked forward pass.
+ *
+ * The method (source: dbyun.net, "基于 NVIDIA CUDA Tile 加速 Mamba-2 高性能前向传播内核"):
+ * the recurrence of section "Mamba-2 架构",
+ *     h_t = exp(A dt_t) h_{t-1} + dt_t x_t (outer) B_t,   y_t = h_t . C_t + D x_t,
+ * is evaluated chunk by chunk in three stages (end of section "Mamba-2 架构"):
+ *   1. ssd_chunk_cumsum  -- section "Kernel 1": chunk-local cumsum of A*dt, times log2(e);
+ *   2. ssd_state_pass    -- section "Kernel 2: fwd_pass_state": the state at every chunk
+ *                           start, by the jump h_next = exp(G_last) h + (exp(G_last - G) dt B)^T X;
+ *   3. ssd_chunk_out     -- section "Kernel 3：compute_out": per chunk
+ *                           Y = exp(G) C h^T + (exp(G_i - G_j) (C B^T) causal-mask) (dt X) + D X.
+ * ssd_forward runs the three in order on one stream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes use b = batch, L = seqlen, H = nheads, G = ngroups, P = headdim, N = dstate,
+ * Q = chunk, nc = ceil(L / Q), Lp = nc * Q.  All arrays are dense, row-major and
+ * contiguous, in *device* memory owned by the caller:
+ *     x, y    [b, L, H, P]      element type `dtype`
+ *     dt      [b, L, H]         element type `dtype`
+ *     B, C    [b, L, G, N]      element type `dtype`; head h reads group h / (H / G)
+ *     A, D    [H]               float32 (per-head decay rate and skip weight)
+ *     h0, hT  [b, H, P, N]      float32 (initial and final state)
+ *     G2, dtT [b, H, Lp]        float32 (stage-1 outputs, token-contiguous per head)
+ *     S       [b, H, nc, P, N]  bfloat16 when dtype is SSD_BF16, float32 when SSD_F32
+ * `problem` is a host pointer.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Every call validates its arguments on the host before any launch and returns a
+ * status; nothing is launched when it is not SSD_OK.  The library never allocates
+ * memory, never synchronises and keeps no global mutable state apart from the
+ * thread-local HIP error code.  Work is asynchronous on `stream`; buffers must stay
+ * valid until it completes.  Inputs and outputs must not overlap, except that
+ * h0 and hT may be the same buffer.
+ *
+ * Supported set: dtype SSD_F32 or SSD_BF16; headdim 64; dstate a multiple of 64
+ * up to 512; chunk 64, 128 or 256; any seqlen >= 1 (a partial last chunk is
+ * zero-padded, which is exact: a token with dt = 0 and x = B = C = 0 changes
+ * nothing).  Other shapes return SSD_ERR_UNSUPPORTED.
+ *
+ * Numerics: for SSD_BF16 the matrix products take bf16 operands with fp32
+ * accumulation, the running state is fp32, the chunk-start states S are stored in
+ * bf16 (the output stage reads them in the input precision) and y is rounded to
+ * bf16 (round to nearest even).  For SSD_F32 everything stays fp32.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,     /* a required pointer is NULL                          */
+    SSD_ERR_BAD_SHAPE = 2,    /* a dimension <= 0, or nheads not divisible by ngroups */
+    SSD_ERR_UNSUPPORTED = 3,  /* outside the supported dtype / headdim / dstate / chunk set */
+    SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than ssd_workspace_bytes() */
+    SSD_ERR_HIP = 5           /* a HIP launch failed; see ssd_last_hip_error()        */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch, seqlen, nheads, ngroups, headdim, dstate, chunk;
+    int32_t dtype;            /* an ssd_dtype value */
+} ssd_problem;
+
+/* Host-only checks of `problem` (dimensions, divisibility, supported set).  No GPU. */
+ssd_status ssd_validate(const ssd_problem *problem);
+
+/* Bytes of device workspace ssd_forward needs (G2, dtT and S, each 256-byte aligned);
+ * 0 if `problem` is not valid.  Host-only. */
+size_t ssd_workspace_bytes(const ssd_problem *problem);
+
+/* Stage 1 (section "Kernel 1：计算累积和"): for each (b, h) and token t of chunk c,
+ *     G2[b,h,t]  = log2(e) * sum_{k = cQ .. t} A[h] * dt[b,k,h]     (fp32 sum, then scaled)
+ *     dtT[b,h,t] = float(dt[b,t,h])
+ * For padded positions t >= L: dtT = 0 and G2 repeats the chunk's last valid value.
+ * Reads dt, A; writes G2 and dtT ([b, H, Lp]). */
+ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A,
+                            float *G2, float *dtT, void *stream);
+
+/* Stage 2 (section "Kernel 2: fwd_pass_state", the decayed chunk jump): serially over
+ * chunks c, S[b,h,c] = h (the state at the chunk start, h = h0 or 0 for c = 0), then
+ *     h <- exp2(G2_last) h + X_c^T W_c,   W_c[t,n] = round(dt_t exp2(G2_last - G2_t) B[t,n])
+ * (W rounded to the input type).  After the last chunk hT = h (skipped when hT is NULL).
+ * h0 may be NULL (zero initial state).  Reads x, B, G2, dtT, h0; writes S, hT. */
+ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
+                          const float *G2, const float *dtT, const float *h0, void *S,
+                          float *hT, void *stream);
+
+/* Stage 3 (section "Kernel 3：compute_out", the decayed chunk output): for each chunk,
+ *     y_i = exp2(G2_i) C_i . S_c^T
+ *         + sum_{j <= i in the chunk} exp2(G2_i - G2_j) (C_i . B_j) dt_j x_j
+ *         + D[h] x_i
+ * with the causal mask applied by selection (masked exponents never reach the sum).
+ * C B^T, the decay matrix and C S^T live only in registers and LDS.  Reads x, B, C,
+ * G2, dtT, S, D; writes y. */
+ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *B,
+                         const void *C, const float *G2, const float *dtT, const void *S,
+                         const float *D, void *y, void *stream);
+
+/* The whole forward pass: stage 1, 2 and 3 on `stream`, no host synchronisation.
+ * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds G2, dtT and S;
+ * its contents on return are those intermediates.  h0 may be NULL; hT may be NULL
+ * (final state not wanted).  Writes y and hT. */
+ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
+                       const float *A, const void *B, const void *C, const float *D,
+                       const float *h0, void *y, float *hT, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Offsets (bytes) of G2, dtT and S inside an ssd_forward workspace.  Host-only. */
+ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
+                                size_t *off_S);
+
+/* Static text for a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* hipError_t of the last SSD_ERR_HIP returned on this thread (0 if none). */
+int ssd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

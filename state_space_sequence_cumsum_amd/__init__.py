@@ -1,1 +1,16 @@
-"""MI355X-native (gfx950) Mamba-2 SSD chunked forward pass."""
+"""MI355X-native (gfx950) Mamba-2 SSD chunked forward pass.
+
+The compute path is libssd.so (hand-written HIP kernels behind the C ABI of
+include/ssd.h); :mod:`.binding` marshals torch tensors into it.  Importing this
+package does not load the library; the first call does, and raises if it is
+missing.
+"""
+from .binding import (SSD_BF16, SSD_F32, SsdError, SsdProblem, make_problem, problem_of,
+                      ssd_chunk_cumsum, ssd_chunk_out, ssd_forward, ssd_state_pass,
+                      ssd_status_string, ssd_validate, ssd_workspace_bytes, ssd_workspace_layout,
+                      workspace_for)
+
+__all__ = ["SSD_BF16", "SSD_F32", "SsdError", "SsdProblem", "make_problem", "problem_of",
+           "ssd_chunk_cumsum", "ssd_chunk_out", "ssd_forward", "ssd_state_pass",
+           "ssd_status_string", "ssd_validate", "ssd_workspace_bytes", "ssd_workspace_layout",
+           "workspace_for"]

@@ -1,0 +1,257 @@
+"""ctypes binding of libssd (include/ssd.h).
+
+Argument marshalling only: every function checks tensor placement, dtype, shape
+and contiguity, turns tensors into device pointers and calls the C entry point
+of the same name on the current (or given) HIP stream.  Outputs that the caller
+does not pass are allocated with ``torch.empty`` on the inputs' device.  There is
+no CPU or PyTorch fallback: when libssd.so is missing or a call fails, this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libssd.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
+          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP"}
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({detail})")
+
+
+class SsdProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("SsdProblem(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
+
+    @property
+    def nchunks(self) -> int:
+        return -(-self.seqlen // self.chunk)
+
+
+_lib = None
+
+
+def lib():
+    """Load libssd.so (built in-tree by build.py); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it first (python -m "
+                               "state_space_sequence_cumsum_amd.build or __graft_entry__.build())")
+        L = ctypes.CDLL(LIBRARY)
+        P, vp, st = ctypes.POINTER(SsdProblem), ctypes.c_void_p, ctypes.c_int
+        L.ssd_validate.argtypes, L.ssd_validate.restype = [P], st
+        L.ssd_workspace_bytes.argtypes, L.ssd_workspace_bytes.restype = [P], ctypes.c_size_t
+        L.ssd_workspace_layout.argtypes = [P, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_workspace_layout.restype = st
+        L.ssd_chunk_cumsum.argtypes, L.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp, vp], st
+        L.ssd_state_pass.argtypes, L.ssd_state_pass.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp], st
+        L.ssd_chunk_out.argtypes, L.ssd_chunk_out.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
+        L.ssd_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ssd_forward.restype = st
+        L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
+        L.ssd_last_hip_error.argtypes, L.ssd_last_hip_error.restype = [], ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/ssd.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def _raise(status: int, what: str):
+    if status != 0:
+        L = lib()
+        detail = L.ssd_status_string(status).decode()
+        if status == 5:
+            detail += f"; hipError_t {L.ssd_last_hip_error()}"
+        raise SsdError(status, what, detail)
+
+
+# ---------------------------------------------------------------------------
+# problem descriptors (host only)
+# ---------------------------------------------------------------------------
+def make_problem(batch, seqlen, nheads, ngroups, headdim, dstate, chunk, dtype) -> SsdProblem:
+    code = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16, "fp32": SSD_F32, "bf16": SSD_BF16}
+    return SsdProblem(int(batch), int(seqlen), int(nheads), int(ngroups), int(headdim), int(dstate),
+                      int(chunk), code.get(dtype, dtype) if not isinstance(dtype, int) else dtype)
+
+
+def problem_of(x: torch.Tensor, B: torch.Tensor, chunk: int) -> SsdProblem:
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return make_problem(b, L, H, G, P, N, chunk, x.dtype)
+
+
+def ssd_validate(problem: SsdProblem) -> int:
+    return lib().ssd_validate(ctypes.byref(problem))
+
+
+def ssd_workspace_bytes(problem: SsdProblem) -> int:
+    return lib().ssd_workspace_bytes(ctypes.byref(problem))
+
+
+def ssd_workspace_layout(problem: SsdProblem) -> tuple[int, int, int]:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _raise(lib().ssd_workspace_layout(ctypes.byref(problem), ctypes.byref(a), ctypes.byref(b),
+                                      ctypes.byref(c)), "ssd_workspace_layout")
+    return a.value, b.value, c.value
+
+
+def ssd_status_string(status: int) -> str:
+    return lib().ssd_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+def _dev(t, name, dtype, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dims(p: SsdProblem):
+    return p.batch, p.seqlen, p.nheads, p.ngroups, p.headdim, p.dstate, p.chunk, p.nchunks
+
+
+def _io_dtype(p: SsdProblem):
+    return torch.bfloat16 if p.dtype == SSD_BF16 else torch.float32
+
+
+def ssd_chunk_cumsum(problem: SsdProblem, dt, A, G2=None, dtT=None, stream=None):
+    """Stage 1.  Returns (G2, dtT), both float32 [b, H, nc*Q]."""
+    b, L, H, G, P, N, Q, nc = _dims(problem)
+    dev = dt.device
+    _dev(dt, "dt", _io_dtype(problem), (b, L, H), None)
+    _dev(A, "A", torch.float32, (H,), dev)
+    if G2 is None:
+        G2 = torch.empty(b, H, nc * Q, device=dev, dtype=torch.float32)
+    if dtT is None:
+        dtT = torch.empty(b, H, nc * Q, device=dev, dtype=torch.float32)
+    _dev(G2, "G2", torch.float32, (b, H, nc * Q), dev)
+    _dev(dtT, "dtT", torch.float32, (b, H, nc * Q), dev)
+    _raise(lib().ssd_chunk_cumsum(ctypes.byref(problem), _ptr(dt), _ptr(A), _ptr(G2), _ptr(dtT),
+                                  _stream(stream, dev)), "ssd_chunk_cumsum")
+    return G2, dtT
+
+
+def ssd_state_pass(problem: SsdProblem, x, B, G2, dtT, h0=None, S=None, hT=None, want_final=True,
+                   stream=None):
+    """Stage 2.  Returns (S [b,H,nc,P,N] in the input dtype, hT [b,H,P,N] float32 or None)."""
+    b, L, H, G, P, N, Q, nc = _dims(problem)
+    io = _io_dtype(problem)
+    dev = x.device
+    _dev(x, "x", io, (b, L, H, P), None)
+    _dev(B, "B", io, (b, L, G, N), dev)
+    _dev(G2, "G2", torch.float32, (b, H, nc * Q), dev)
+    _dev(dtT, "dtT", torch.float32, (b, H, nc * Q), dev)
+    _dev(h0, "h0", torch.float32, (b, H, P, N), dev)
+    if S is None:
+        S = torch.empty(b, H, nc, P, N, device=dev, dtype=io)
+    if hT is None and want_final:
+        hT = torch.empty(b, H, P, N, device=dev, dtype=torch.float32)
+    _dev(S, "S", io, (b, H, nc, P, N), dev)
+    _dev(hT, "hT", torch.float32, (b, H, P, N), dev)
+    _raise(lib().ssd_state_pass(ctypes.byref(problem), _ptr(x), _ptr(B), _ptr(G2), _ptr(dtT),
+                                _ptr(h0), _ptr(S), _ptr(hT), _stream(stream, dev)), "ssd_state_pass")
+    return S, hT
+
+
+def ssd_chunk_out(problem: SsdProblem, x, B, C, G2, dtT, S, D, y=None, stream=None):
+    """Stage 3.  Returns y [b, L, H, P] in the input dtype."""
+    b, L, H, G, P, N, Q, nc = _dims(problem)
+    io = _io_dtype(problem)
+    dev = x.device
+    _dev(x, "x", io, (b, L, H, P), None)
+    _dev(B, "B", io, (b, L, G, N), dev)
+    _dev(C, "C", io, (b, L, G, N), dev)
+    _dev(G2, "G2", torch.float32, (b, H, nc * Q), dev)
+    _dev(dtT, "dtT", torch.float32, (b, H, nc * Q), dev)
+    _dev(S, "S", io, (b, H, nc, P, N), dev)
+    _dev(D, "D", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty(b, L, H, P, device=dev, dtype=io)
+    _dev(y, "y", io, (b, L, H, P), dev)
+    _raise(lib().ssd_chunk_out(ctypes.byref(problem), _ptr(x), _ptr(B), _ptr(C), _ptr(G2),
+                               _ptr(dtT), _ptr(S), _ptr(D), _ptr(y), _stream(stream, dev)),
+           "ssd_chunk_out")
+    return y
+
+
+def workspace_for(problem: SsdProblem, device) -> torch.Tensor:
+    n = ssd_workspace_bytes(problem)
+    if n == 0:
+        _raise(ssd_validate(problem) or 3, "ssd_workspace_bytes")
+    return torch.empty(n, device=device, dtype=torch.uint8)
+
+
+def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want_final=True,
+                workspace=None, stream=None):
+    """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None)."""
+    problem = problem_of(x, B, chunk)
+    b, L, H, G, P, N, Q, nc = _dims(problem)
+    io = _io_dtype(problem)
+    dev = x.device
+    _dev(x, "x", io, (b, L, H, P), None)
+    _dev(dt, "dt", io, (b, L, H), dev)
+    _dev(A, "A", torch.float32, (H,), dev)
+    _dev(B, "B", io, (b, L, G, N), dev)
+    _dev(C, "C", io, (b, L, G, N), dev)
+    _dev(D, "D", torch.float32, (H,), dev)
+    _dev(h0, "h0", torch.float32, (b, H, P, N), dev)
+    if y is None:
+        y = torch.empty(b, L, H, P, device=dev, dtype=io)
+    if hT is None and want_final:
+        hT = torch.empty(b, H, P, N, device=dev, dtype=torch.float32)
+    _dev(y, "y", io, (b, L, H, P), dev)
+    _dev(hT, "hT", torch.float32, (b, H, P, N), dev)
+    if workspace is None:
+        workspace = workspace_for(problem, dev)
+    if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise(lib().ssd_forward(ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                             _ptr(D), _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace), nbytes,
+                             _stream(stream, dev)), "ssd_forward")
+    return y, hT

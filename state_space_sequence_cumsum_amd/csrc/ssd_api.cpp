@@ -1,0 +1,164 @@
+// ssd_api.cpp -- the C ABI declared in include/ssd.h: host-side validation,
+// workspace layout and the three-stage forward on one stream.
+#include "../../include/ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include "ssd_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+ssd_status check_shape(const ssd_problem *p)
+{
+    if (p == nullptr) return SSD_ERR_NULL_ARG;
+    if (p->batch <= 0 || p->seqlen <= 0 || p->nheads <= 0 || p->ngroups <= 0 || p->headdim <= 0 ||
+        p->dstate <= 0 || p->chunk <= 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (p->headdim != 64) return SSD_ERR_UNSUPPORTED;
+    if (p->dstate % 64 != 0 || p->dstate > 512) return SSD_ERR_UNSUPPORTED;
+    if (p->chunk != 64 && p->chunk != 128 && p->chunk != 256) return SSD_ERR_UNSUPPORTED;
+    // 32-bit grid and index limits of the kernels
+    if (p->batch * p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
+    if (p->seqlen > (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
+    if (p->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd::Shape make_shape(const ssd_problem *p)
+{
+    ssd::Shape s;
+    s.b = p->batch; s.L = p->seqlen; s.H = p->nheads; s.G = p->ngroups;
+    s.P = p->headdim; s.N = p->dstate; s.Q = p->chunk;
+    s.nc = (s.L + s.Q - 1) / s.Q;
+    s.Lp = s.nc * s.Q;
+    s.bf16 = p->dtype == SSD_BF16;
+    return s;
+}
+
+struct Layout {
+    size_t g2, dtt, S, total;
+};
+
+Layout layout_of(const ssd::Shape &s)
+{
+    const size_t cum = size_t(s.b) * s.H * s.Lp * sizeof(float);
+    const size_t snap = size_t(s.b) * s.H * s.nc * s.P * s.N * (s.bf16 ? 2 : 4);
+    Layout l;
+    l.g2 = 0;
+    l.dtt = align_up(cum);
+    l.S = l.dtt + align_up(cum);
+    l.total = l.S + align_up(snap);
+    return l;
+}
+
+ssd_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return SSD_OK;
+    g_last_hip_error = int(e);
+    return SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_validate(const ssd_problem *problem) { return check_shape(problem); }
+
+size_t ssd_workspace_bytes(const ssd_problem *problem)
+{
+    if (check_shape(problem) != SSD_OK) return 0;
+    return layout_of(make_shape(problem)).total;
+}
+
+ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
+                                size_t *off_S)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!off_G2 || !off_dtT || !off_S) return SSD_ERR_NULL_ARG;
+    const Layout l = layout_of(make_shape(problem));
+    *off_G2 = l.g2;
+    *off_dtT = l.dtt;
+    *off_S = l.S;
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A, float *G2,
+                            float *dtT, void *stream)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!dt || !A || !G2 || !dtT) return SSD_ERR_NULL_ARG;
+    return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT,
+                                               (hipStream_t)stream));
+}
+
+ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
+                          const float *G2, const float *dtT, const float *h0, void *S, float *hT,
+                          void *stream)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!x || !B || !G2 || !dtT || !S) return SSD_ERR_NULL_ARG;
+    return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, dtT, h0, S, hT,
+                                             (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *B, const void *C,
+                         const float *G2, const float *dtT, const void *S, const float *D, void *y,
+                         void *stream)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!x || !B || !C || !G2 || !dtT || !S || !D || !y) return SSD_ERR_NULL_ARG;
+    return hip_status(ssd::launch_chunk_out(make_shape(problem), x, B, C, G2, dtT, S, D, y,
+                                            (hipStream_t)stream));
+}
+
+ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *h0, void *y,
+                       float *hT, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
+    const ssd::Shape s = make_shape(problem);
+    const Layout l = layout_of(s);
+    if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *G2 = reinterpret_cast<float *>(ws + l.g2);
+    float *dtT = reinterpret_cast<float *>(ws + l.dtt);
+    void *S = ws + l.S;
+    hipStream_t hs = (hipStream_t)stream;
+
+    ssd_status r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, hs));
+    if (r != SSD_OK) return r;
+    r = hip_status(ssd::launch_state_pass(s, x, B, G2, dtT, h0, S, hT, hs));
+    if (r != SSD_OK) return r;
+    return hip_status(ssd::launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, hs));
+}
+
+const char *ssd_status_string(ssd_status status)
+{
+    switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SSD_ERR_BAD_SHAPE: return "bad shape (dimension <= 0 or nheads not divisible by ngroups)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported dtype/headdim/dstate/chunk";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int ssd_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// ssd_device.h -- gfx950 device helpers shared by the SSD kernels: element types,
+// MFMA wrappers and the 32x32 accumulator lane layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// v_exp_f32: base-2 exponential on the transcendental unit.  Large positive
+// arguments give +inf and large negative ones give 0, which is what the masked
+// decay factors need.
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// ---------------------------------------------------------------------------
+// Element traits.  A "fragment" is the 8 values one lane contributes to one
+// 32x32 MFMA tile for a 16-deep slice of the contraction index.  For bf16 that
+// is one v_mfma_f32_32x32x16_bf16 operand.  For fp32 it is eight
+// v_mfma_f32_32x32x2_f32 operands: in the e-th of those instructions lane l
+// supplies element e, which the hardware places at contraction index l / 32.
+// Because every operand of a product uses the same (lane, element) -> index
+// assignment, any fixed assignment of the 16 logical indices to the pairs
+// (l / 32, e) contracts correctly.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16> {
+    typedef bf16x8 frag;
+    typedef bf16x4 half;
+    static __device__ __forceinline__ bf16 from_f32(float v) { return (bf16)v; }
+};
+
+template <> struct Elem<float> {
+    typedef f32x8 frag;
+    typedef f32x4 half;
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+
+__device__ __forceinline__ void mma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(f32x16 &acc, const f32x8 &a, const f32x8 &b)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc, 0, 0, 0);
+}
+
+// Eight consecutive elements; p must be 16-byte aligned.
+template <typename T> __device__ __forceinline__ typename Elem<T>::frag load_frag(const T *p);
+
+template <> __device__ __forceinline__ bf16x8 load_frag<bf16>(const bf16 *p)
+{
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+template <> __device__ __forceinline__ f32x8 load_frag<float>(const float *p)
+{
+    const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f[e] = lo[e]; f[4 + e] = hi[e]; }
+    return f;
+}
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag zero_frag()
+{
+    typename Elem<T>::frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (T)0.0f;
+    return f;
+}
+
+// 32x32 fp32 accumulator layout: element v of lane l holds row
+// 8*(v/4) + 4*(l/32) + v%4 and column l%32.
+__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+__device__ __forceinline__ f32x16 zero_acc()
+{
+    f32x16 a;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) a[v] = 0.0f;
+    return a;
+}
+
+}  // namespace ssd

@@ -1,0 +1,367 @@
+// ssd_kernels.hip -- the three gfx950 kernels of the Mamba-2 SSD chunked forward pass.
+//
+// Method: dbyun.net, "基于 NVIDIA CUDA Tile 加速 Mamba-2 高性能前向传播内核".
+//   chunk_cumsum_kernel  section "Kernel 1：计算累积和"
+//   state_pass_kernel    section "Kernel 2: fwd_pass_state" (the decayed chunk jump)
+//   chunk_out_kernel     section "Kernel 3：compute_out"   (the decayed chunk output)
+//
+// All products run on MFMA: bf16 operands with fp32 accumulation for bf16 inputs,
+// fp32 operands for fp32 inputs.  Decays use base-2 exponentials of the
+// log2(e)-scaled cumsum (same page, section "Kernel 1").
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ===========================================================================
+// Stage 1: chunk-local cumsum of A*dt, times log2(e), transposed to [b, H, Lp].
+// One workgroup per (chunk, block of 32 heads, batch).  The [Q x 32] dt tile is
+// read row by row (heads contiguous) into LDS, then each wave scans one head's
+// Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane shuffle scan
+// adds the lane prefixes, and the results are written token-contiguous.
+// ===========================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__ dt,
+                                                           const float *__restrict__ A,
+                                                           float *__restrict__ G2,
+                                                           float *__restrict__ dtT, int L, int H,
+                                                           int Q, int Lp)
+{
+    __shared__ float tile[256][33];
+    const int c = blockIdx.x, hb = blockIdx.y * 32, b = blockIdx.z;
+    const int nh = min(32, H - hb);
+    const int t0 = c * Q;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int idx = tid; idx < Q * 32; idx += 256) {
+        const int t = idx >> 5, hh = idx & 31;
+        float v = 0.0f;
+        if (hh < nh && t0 + t < L) v = (float)dt[((int64_t)b * L + t0 + t) * H + hb + hh];
+        tile[t][hh] = v;
+    }
+    __syncthreads();
+
+    const int per = Q >> 6;  // tokens per lane: 1, 2 or 4
+    for (int hh = wave; hh < nh; hh += 4) {
+        const float a = A[hb + hh];
+        float part[4], run = 0.0f;
+        for (int j = 0; j < per; ++j) {
+            run += a * tile[lane * per + j][hh];
+            part[j] = run;
+        }
+        float incl = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += up;
+        }
+        float excl = __shfl_up(incl, 1, 64);
+        if (lane == 0) excl = 0.0f;
+        const int64_t base = ((int64_t)b * H + hb + hh) * Lp + t0 + lane * per;
+        for (int j = 0; j < per; ++j) {
+            G2[base + j] = (excl + part[j]) * kLog2e;
+            dtT[base + j] = tile[lane * per + j][hh];
+        }
+    }
+}
+
+// ===========================================================================
+// Stage 2: chunk-start states.  One workgroup per (N tile of 64, batch*head),
+// four waves, each owning a 32x32 (P x N) quarter of the fp32 state in MFMA
+// accumulators.  Serially over chunks: stage X_c^T and W_c^T = (w * B_c)^T into
+// LDS (token-contiguous rows, so MFMA fragments are 8 consecutive tokens),
+// store the chunk-start state, scale it by exp2(G_last) and accumulate X^T W.
+// ===========================================================================
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void state_pass_kernel(
+    const T *__restrict__ x, const T *__restrict__ Bm, const float *__restrict__ G2,
+    const float *__restrict__ dtT, const float *__restrict__ h0, T *__restrict__ S,
+    float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp)
+{
+    constexpr int P = 64, NT = 64;
+    constexpr int PITCH = Q + 16 / (int)sizeof(T);  // row pitch in elements; rows 16 B aligned
+    __shared__ __attribute__((aligned(16))) T XT[P * PITCH];
+    __shared__ __attribute__((aligned(16))) T WT[NT * PITCH];
+    __shared__ float wsh[Q];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ph = wave & 1, nh = wave >> 1;
+    const int n_base = blockIdx.x * NT;
+    const int bh = blockIdx.y, b = bh / H, h = bh % H, g = h / (H / G);
+    const int col = n_base + nh * 32 + (lane & 31);
+
+    const int64_t st_off = (int64_t)bh * P * N;
+    f32x16 acc = zero_acc();
+    if (h0 != nullptr) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = h0[st_off + (int64_t)(ph * 32 + acc_row(v, lane)) * N + col];
+    }
+
+    const float *Gh = G2 + (int64_t)bh * Lp;
+    const float *dh = dtT + (int64_t)bh * Lp;
+    const int64_t xrow = (int64_t)H * P;   // x token stride
+    const int64_t brow = (int64_t)G * N;   // B token stride
+
+    for (int c = 0; c < nc; ++c) {
+        const int t0 = c * Q;
+        const float glast = Gh[t0 + Q - 1];
+        for (int t = tid; t < Q; t += 256) wsh[t] = dh[t0 + t] * fast_exp2(glast - Gh[t0 + t]);
+        __syncthreads();
+
+        // X_c [Q x 64] -> XT[p][t]
+        {
+            typename Elem<T>::frag f[Q / 32];
+#pragma unroll
+            for (int r = 0; r < Q / 32; ++r) {
+                const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
+                f[r] = (t0 + t < L)
+                           ? load_frag<T>(x + ((int64_t)b * L + t0 + t) * xrow + (int64_t)h * P + oct * 8)
+                           : zero_frag<T>();
+            }
+#pragma unroll
+            for (int r = 0; r < Q / 32; ++r) {
+                const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) XT[(oct * 8 + e) * PITCH + t] = f[r][e];
+            }
+        }
+        // W_c = round(w * B_c) [Q x 64] -> WT[n][t]
+        {
+            typename Elem<T>::frag f[Q / 32];
+#pragma unroll
+            for (int r = 0; r < Q / 32; ++r) {
+                const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
+                f[r] = (t0 + t < L)
+                           ? load_frag<T>(Bm + ((int64_t)b * L + t0 + t) * brow + (int64_t)g * N + n_base + oct * 8)
+                           : zero_frag<T>();
+            }
+#pragma unroll
+            for (int r = 0; r < Q / 32; ++r) {
+                const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
+                const float w = wsh[t];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) WT[(oct * 8 + e) * PITCH + t] = Elem<T>::from_f32((float)f[r][e] * w);
+            }
+        }
+        __syncthreads();
+
+        // chunk-start state, then h <- exp2(G_last) h + X^T W
+        T *Sc = S + ((int64_t)bh * nc + c) * P * N;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Sc[(int64_t)(ph * 32 + acc_row(v, lane)) * N + col] = Elem<T>::from_f32(acc[v]);
+        const float alpha = fast_exp2(glast);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] *= alpha;
+
+        const T *arow = XT + (ph * 32 + (lane & 31)) * PITCH + 8 * (lane >> 5);
+        const T *brw = WT + (nh * 32 + (lane & 31)) * PITCH + 8 * (lane >> 5);
+#pragma unroll 4
+        for (int ks = 0; ks < Q / 16; ++ks) mma(acc, load_frag<T>(arow + ks * 16), load_frag<T>(brw + ks * 16));
+        __syncthreads();
+    }
+
+    if (hT != nullptr) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) hT[st_off + (int64_t)(ph * 32 + acc_row(v, lane)) * N + col] = acc[v];
+    }
+}
+
+// ===========================================================================
+// Stage 3: chunk output.  One workgroup per (chunk, batch*head) with Q/64 waves.
+// The chunk has Q/32 row tiles of 32 tokens; wave w takes tiles w and Q/32-1-w so
+// every wave does the same number of causal tile pairs.  The output is built
+// transposed, Y^T [P x 32 tokens], so that
+//   * C S^T:   A = S rows (p, n), B = C rows (i, n) -- both n-contiguous in HBM;
+//   * C B^T:   computed as (B C^T) with A = B rows (j, n), B = C rows (i, n); its
+//              accumulator holds column i and rows j, which is exactly the lane
+//              layout the next product wants for its B operand;
+//   * M (dt X): A = (dt X)^T from LDS (p rows, token-contiguous), B = M straight
+//              from registers after the decay, causal select and rounding.
+// ===========================================================================
+template <typename T, int Q>
+__global__ __launch_bounds__(Q) void chunk_out_kernel(
+    const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
+    const float *__restrict__ G2, const float *__restrict__ dtT, const T *__restrict__ S,
+    const float *__restrict__ D, T *__restrict__ y, int L, int H, int G, int N, int nc, int Lp)
+{
+    constexpr int P = 64, NI = Q / 32, NTHR = Q;  // Q/64 waves
+    constexpr int PITCH = Q + 16 / (int)sizeof(T);
+    __shared__ __attribute__((aligned(16))) T XdT[P * PITCH];
+    __shared__ float Gs[Q];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H, g = h / (H / G);
+    const int t0 = c * Q;
+    const int64_t xrow = (int64_t)H * P, crow = (int64_t)G * N;
+    const float *Gh = G2 + (int64_t)bh * Lp + t0;
+    const float *dh = dtT + (int64_t)bh * Lp + t0;
+
+    for (int t = tid; t < Q; t += NTHR) Gs[t] = Gh[t];
+    for (int idx = tid; idx < Q * 8; idx += NTHR) {
+        const int t = idx >> 3, oct = idx & 7;
+        typename Elem<T>::frag f =
+            (t0 + t < L) ? load_frag<T>(x + ((int64_t)b * L + t0 + t) * xrow + (int64_t)h * P + oct * 8)
+                         : zero_frag<T>();
+        const float d = dh[t];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) XdT[(oct * 8 + e) * PITCH + t] = Elem<T>::from_f32((float)f[e] * d);
+    }
+    __syncthreads();
+
+    const float Dh = D[h];
+    const T *Cc = Cm + ((int64_t)b * L + t0) * crow + (int64_t)g * N;
+    const T *Bc = Bm + ((int64_t)b * L + t0) * crow + (int64_t)g * N;
+    const T *Sc = S + ((int64_t)bh * nc + c) * P * N;
+    const int kq = 8 * (lane >> 5);
+
+    for (int pass = 0; pass < 2; ++pass) {
+        const int I = pass == 0 ? wave : NI - 1 - wave;
+        const int i_loc = I * 32 + (lane & 31);
+        const bool ivalid = t0 + i_loc < L;
+        const T *crow_i = Cc + (int64_t)i_loc * crow + kq;
+
+        // inter-chunk term: Y^T = S C^T, then scale column i by exp2(G_i)
+        f32x16 acc0 = zero_acc(), acc1 = zero_acc();
+        for (int k = 0; k < N; k += 16) {
+            const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
+            mma(acc0, load_frag<T>(Sc + (int64_t)(lane & 31) * N + kq + k), cf);
+            mma(acc1, load_frag<T>(Sc + (int64_t)(32 + (lane & 31)) * N + kq + k), cf);
+        }
+        const float gi = Gs[i_loc];
+        const float si = fast_exp2(gi);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { acc0[v] *= si; acc1[v] *= si; }
+
+        // intra-chunk term over causal tiles J <= I
+        for (int J = 0; J <= I; ++J) {
+            const int j_loc = J * 32 + (lane & 31);
+            const bool jvalid = t0 + j_loc < L;
+            const T *brow_j = Bc + (int64_t)j_loc * crow + kq;
+            f32x16 cb = zero_acc();
+            for (int k = 0; k < N; k += 16) {
+                const typename Elem<T>::frag bf = jvalid ? load_frag<T>(brow_j + k) : zero_frag<T>();
+                const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
+                mma(cb, bf, cf);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                typename Elem<T>::frag m;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int v = 8 * s + e;
+                    const int jj = J * 32 + acc_row(v, lane);
+                    const float val = (i_loc >= jj) ? cb[v] * fast_exp2(gi - Gs[jj]) : 0.0f;
+                    m[e] = Elem<T>::from_f32(val);
+                }
+                // (dt x)^T fragment with the same token order as m: 4 tokens at
+                // J*32 + 16 s + 4*(lane/32), then 4 more 8 tokens further on.
+                const int jb = J * 32 + 16 * s + 4 * (lane >> 5);
+#pragma unroll
+                for (int ph = 0; ph < 2; ++ph) {
+                    const T *ar = XdT + (ph * 32 + (lane & 31)) * PITCH + jb;
+                    const typename Elem<T>::half lo = *reinterpret_cast<const typename Elem<T>::half *>(ar);
+                    const typename Elem<T>::half hi = *reinterpret_cast<const typename Elem<T>::half *>(ar + 8);
+                    typename Elem<T>::frag a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { a[e] = lo[e]; a[4 + e] = hi[e]; }
+                    if (ph == 0) mma(acc0, a, m); else mma(acc1, a, m);
+                }
+            }
+        }
+
+        // y_i = Y_i + D x_i
+        if (ivalid) {
+            const int64_t yo = ((int64_t)b * L + t0 + i_loc) * xrow + (int64_t)h * P;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int p = acc_row(v, lane);
+                y[yo + p] = Elem<T>::from_f32(acc0[v] + Dh * (float)x[yo + p]);
+                y[yo + 32 + p] = Elem<T>::from_f32(acc1[v] + Dh * (float)x[yo + 32 + p]);
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+template <typename T>
+static hipError_t cumsum_t(const Shape &s, const void *dt, const float *A, float *G2, float *dtT,
+                           hipStream_t st)
+{
+    dim3 grid((unsigned)s.nc, (unsigned)((s.H + 31) / 32), (unsigned)s.b);
+    hipLaunchKernelGGL(chunk_cumsum_kernel<T>, grid, dim3(256), 0, st, (const T *)dt, A, G2, dtT,
+                       (int)s.L, (int)s.H, (int)s.Q, (int)s.Lp);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, float *G2,
+                               float *dtT, hipStream_t st)
+{
+    return s.bf16 ? cumsum_t<bf16>(s, dt, A, G2, dtT, st) : cumsum_t<float>(s, dt, A, G2, dtT, st);
+}
+
+template <typename T, int Q>
+static hipError_t state_pass_tq(const Shape &s, const void *x, const void *B, const float *G2,
+                                const float *dtT, const float *h0, void *S, float *hT,
+                                hipStream_t st)
+{
+    dim3 grid((unsigned)(s.N / 64), (unsigned)(s.b * s.H));
+    hipLaunchKernelGGL((state_pass_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)x, (const T *)B,
+                       G2, dtT, h0, (T *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
+                       (int)s.Lp);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t state_pass_t(const Shape &s, const void *x, const void *B, const float *G2,
+                               const float *dtT, const float *h0, void *S, float *hT, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return state_pass_tq<T, 64>(s, x, B, G2, dtT, h0, S, hT, st);
+    case 128: return state_pass_tq<T, 128>(s, x, B, G2, dtT, h0, S, hT, st);
+    default: return state_pass_tq<T, 256>(s, x, B, G2, dtT, h0, S, hT, st);
+    }
+}
+
+hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const float *G2,
+                             const float *dtT, const float *h0, void *S, float *hT,
+                             hipStream_t st)
+{
+    return s.bf16 ? state_pass_t<bf16>(s, x, B, G2, dtT, h0, S, hT, st)
+                  : state_pass_t<float>(s, x, B, G2, dtT, h0, S, hT, st);
+}
+
+template <typename T, int Q>
+static hipError_t chunk_out_tq(const Shape &s, const void *x, const void *B, const void *C,
+                               const float *G2, const float *dtT, const void *S, const float *D,
+                               void *y, hipStream_t st)
+{
+    dim3 grid((unsigned)s.nc, (unsigned)(s.b * s.H));
+    hipLaunchKernelGGL((chunk_out_kernel<T, Q>), grid, dim3(Q), 0, st, (const T *)x, (const T *)B,
+                       (const T *)C, G2, dtT, (const T *)S, D, (T *)y, (int)s.L, (int)s.H,
+                       (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t chunk_out_t(const Shape &s, const void *x, const void *B, const void *C,
+                              const float *G2, const float *dtT, const void *S, const float *D,
+                              void *y, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return chunk_out_tq<T, 64>(s, x, B, C, G2, dtT, S, D, y, st);
+    case 128: return chunk_out_tq<T, 128>(s, x, B, C, G2, dtT, S, D, y, st);
+    default: return chunk_out_tq<T, 256>(s, x, B, C, G2, dtT, S, D, y, st);
+    }
+}
+
+hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const void *C,
+                            const float *G2, const float *dtT, const void *S, const float *D,
+                            void *y, hipStream_t st)
+{
+    return s.bf16 ? chunk_out_t<bf16>(s, x, B, C, G2, dtT, S, D, y, st)
+                  : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, st);
+}
+
+}  // namespace ssd

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/ssd.h
+declares, and validates arguments before any launch.  No GPU needed."""
+import ctypes
+
+import pytest
+import torch
+
+import state_space_sequence_cumsum_amd as ssd
+from state_space_sequence_cumsum_amd import binding
+
+
+def test_library_exports_every_declared_symbol():
+    names = binding.header_functions()
+    assert {"ssd_chunk_cumsum", "ssd_state_pass", "ssd_chunk_out", "ssd_forward"} <= set(names)
+    lib = binding.lib()
+    for n in names:
+        assert hasattr(lib, n), f"libssd.so does not export {n}"
+
+
+def _p(**kw):
+    base = dict(batch=1, seqlen=16384, nheads=32, ngroups=1, headdim=64, dstate=256, chunk=256,
+                dtype="bf16")
+    base.update(kw)
+    return ssd.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(dtype="fp32", dstate=64, chunk=64), 0),
+    (dict(seqlen=1), 0),
+    (dict(seqlen=1000, chunk=128, dstate=512), 0),
+    (dict(nheads=16, ngroups=2), 0),
+    (dict(batch=0), 2),
+    (dict(seqlen=-1), 2),
+    (dict(nheads=6, ngroups=4), 2),
+    (dict(chunk=0), 2),
+    (dict(headdim=128), 3),
+    (dict(dstate=96), 3),
+    (dict(dstate=1024), 3),
+    (dict(chunk=32), 3),
+    (dict(dtype=7), 3),
+])
+def test_validate(kw, status):
+    assert ssd.ssd_validate(_p(**kw)) == status
+
+
+def test_validate_null_problem():
+    assert binding.lib().ssd_validate(None) == 1
+
+
+def test_workspace_size_and_layout():
+    p = _p()
+    g2, dtt, s = ssd.ssd_workspace_layout(p)
+    cum = 1 * 32 * 64 * 256 * 4          # b*H*Lp fp32
+    snap = 1 * 32 * 64 * 64 * 256 * 2    # b*H*nc*P*N bf16
+    assert (g2, dtt, s) == (0, cum, 2 * cum)
+    assert ssd.ssd_workspace_bytes(p) == 2 * cum + snap
+    assert all(o % 256 == 0 for o in (g2, dtt, s))
+    # ragged length: padded to whole chunks, fp32 snapshots for fp32 problems
+    q = _p(seqlen=1000, chunk=128, dtype="fp32", dstate=64)
+    nc = 8
+    g2, dtt, s = ssd.ssd_workspace_layout(q)
+    assert dtt >= 32 * nc * 128 * 4 and dtt % 256 == 0
+    assert ssd.ssd_workspace_bytes(q) >= s + 32 * nc * 64 * 64 * 4
+    assert ssd.ssd_workspace_bytes(_p(dstate=100)) == 0
+
+
+def test_entry_points_reject_bad_arguments_without_launching():
+    lib = binding.lib()
+    p = _p()
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    # missing pointers
+    assert lib.ssd_chunk_cumsum(ctypes.byref(p), None, fake, fake, fake, None) == 1
+    assert lib.ssd_state_pass(ctypes.byref(p), fake, None, fake, fake, None, fake, None, None) == 1
+    assert lib.ssd_chunk_out(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, None) == 1
+    assert lib.ssd_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None,
+                           fake, 10**12, None) == 1
+    # workspace too small or missing
+    assert lib.ssd_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, None,
+                           fake, 100, None) == 4
+    assert lib.ssd_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, None,
+                           None, 10**12, None) == 4
+    # bad shapes win over everything
+    bad = _p(nheads=6, ngroups=4)
+    assert lib.ssd_forward(ctypes.byref(bad), None, None, None, None, None, None, None, None,
+                           None, None, 0, None) == 2
+    assert lib.ssd_last_hip_error() == 0
+
+
+def test_status_strings():
+    for s in range(6):
+        assert ssd.ssd_status_string(s)
+    assert "unknown" in ssd.ssd_status_string(42)
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    B = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ssd.ssd_forward(x, torch.zeros(1, 64, 2, dtype=torch.bfloat16), torch.zeros(2), B, B,
+                        torch.zeros(2), chunk=64)

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every case draws seeded inputs from the shared recipe, runs libssd on cuda:0
+and compares element by element with the oracle run on the very same stored
+values.  Per tensor the bar is max|out - ref| <= tau * max|ref| with tau = 1e-4
+for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import state_space_sequence_cumsum_amd as ssd
+from state_space_sequence_cumsum_amd.inputs import WORKLOADS, Workload, make_inputs
+from gpu_util import TOL, check, f64, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(name="t", dtype="bf16", b=1, L=256, H=4, P=64, N=64, G=1, Q=64, h0=True, shift=-4.0):
+    return Workload(name, dtype, b, L, H, P, N, G, Q, dt_shift=shift, has_h0=h0)
+
+
+def _gpu_forward(inp, w, dev, poison=True):
+    d = to_dev(inp, dev)
+    io = d["x"].dtype
+    y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, device=dev, dtype=io)
+    hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev, dtype=torch.float32)
+    if poison:
+        y.fill_(float("nan"))
+        hT.fill_(float("nan"))
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    ws = ssd.workspace_for(prob, dev)
+    ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                    y=y, hT=hT, workspace=ws)
+    torch.cuda.synchronize()
+    return y, hT, ws, prob
+
+
+def _workspace_views(ws, prob, w):
+    g2_off, dtt_off, s_off = ssd.ssd_workspace_layout(prob)
+    b, H, nc, Q, P, N = w.batch, w.nheads, w.nchunks, w.chunk, w.headdim, w.dstate
+    cnt = b * H * nc * Q
+    G2 = ws[g2_off:g2_off + 4 * cnt].view(torch.float32).view(b, H, nc * Q)
+    dtT = ws[dtt_off:dtt_off + 4 * cnt].view(torch.float32).view(b, H, nc * Q)
+    es = 2 if w.dtype == "bf16" else 4
+    S = ws[s_off:s_off + es * b * H * nc * P * N]
+    S = S.view(torch.bfloat16 if es == 2 else torch.float32).view(b, H, nc, P, N)
+    return G2, dtT, S
+
+
+def _check_forward(w, seed=0, inp=None, dev=None):
+    dev = dev or require_gpu()
+    inp = inp or make_inputs(w, seed)
+    print(f"case {w} seed={seed}", flush=True)
+    y, hT, ws, prob = _gpu_forward(inp, w, dev)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["h0"], chunk=w.chunk)
+    tol = TOL[w.dtype]
+    check(f64(y), ref["y"], tol, "y")
+    check(f64(hT), ref["hT"], tol, "hT")
+    G2, dtT, S = _workspace_views(ws, prob, w)
+    check(f64(S), ref["snaps"], tol, "chunk-start states")
+    return y, hT, ref
+
+
+# ---------------------------------------------------------------------------
+# stage 1 alone
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,L,H,Q", [("fp32", 256, 4, 64), ("bf16", 2048, 24, 256),
+                                         ("bf16", 200, 33, 64), ("bf16", 1000, 7, 128)])
+def test_chunk_cumsum_parity(dtype, L, H, Q):
+    dev = require_gpu()
+    w = _wl(dtype=dtype, b=2, L=L, H=H, Q=Q)
+    inp = make_inputs(w, 3)
+    prob = ssd.problem_of(inp["x"], inp["B"], Q)
+    G2, dtT = ssd.ssd_chunk_cumsum(prob, inp["dt"].to(dev), inp["A"].to(dev))
+    torch.cuda.synchronize()
+    G2_ref, dt_ref = oracle.chunk_cumsum(inp["dt"], inp["A"], Q)
+    G2g, dtg = f64(G2), f64(dtT)
+    # valid tokens: G2 within the fp32 summation bound, dtT exactly fp32(dt)
+    bound = (Q + 2) * 2.0 ** -24 * max(1.0, np.abs(G2_ref).max())
+    err = np.abs(G2g[:, :, :L] - G2_ref).max()
+    print(f"  G2 max|err| = {err:.3e} (bound {bound:.3e})")
+    assert err <= bound
+    np.testing.assert_array_equal(dtg[:, :, :L], dt_ref)
+    # padded tail: dt = 0 and the cumsum frozen at the last valid token
+    if G2g.shape[2] > L:
+        assert (dtg[:, :, L:] == 0).all()
+        np.testing.assert_array_equal(G2g[:, :, L:], np.repeat(G2g[:, :, L - 1:L], G2g.shape[2] - L, 2))
+
+
+# ---------------------------------------------------------------------------
+# whole forward, small shapes spanning tiles, ragged tails and every template
+# ---------------------------------------------------------------------------
+SMALL_CASES = [
+    _wl("fp32_small", "fp32", 1, 256, 4, 64, 64, 1, 64, h0=False),   # the small fp32 workload
+    _wl("fp32_tail", "fp32", 2, 200, 3, 64, 128, 1, 64),
+    _wl("fp32_q128", "fp32", 1, 384, 2, 64, 64, 2, 128),
+    _wl("fp32_q256", "fp32", 1, 300, 2, 64, 64, 1, 256),
+    _wl("bf16_q64_n64", "bf16", 2, 512, 4, 64, 64, 2, 64),
+    _wl("bf16_q128_n128", "bf16", 1, 640, 4, 64, 128, 1, 128),
+    _wl("bf16_q256_n256", "bf16", 1, 1024, 3, 64, 256, 3, 256),
+    _wl("bf16_q128_n512", "bf16", 1, 384, 2, 64, 512, 1, 128),
+    _wl("bf16_tail_q256", "bf16", 2, 700, 2, 64, 192, 1, 256),
+    _wl("bf16_short", "bf16", 1, 37, 2, 64, 64, 1, 128),
+    _wl("bf16_one_token", "bf16", 1, 1, 2, 64, 64, 1, 64),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=[c.name for c in SMALL_CASES])
+def test_forward_parity_small(w):
+    _check_forward(w, seed=0)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_forward_parity_seeds(seed):
+    _check_forward(_wl("bf16_seeds", "bf16", 1, 512, 4, 64, 128, 1, 128), seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# special cases and adversarial numerics
+# ---------------------------------------------------------------------------
+def test_dt_zero_keeps_state_bitwise():
+    dev = require_gpu()
+    w = _wl("dt0", "bf16", 1, 300, 2, 64, 128, 1, 128)
+    inp = make_inputs(w, 4)
+    inp["dt"].zero_()
+    y, hT, _, _ = _gpu_forward(inp, w, dev)
+    torch.testing.assert_close(hT.cpu(), inp["h0"], rtol=0, atol=0)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    check(f64(y), ref["y"], TOL["bf16"], "y (dt = 0)")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_no_decay_linear_attention(dtype):
+    w = _wl("A0", dtype, 1, 320, 2, 64, 64, 1, 64)
+    inp = make_inputs(w, 5)
+    inp["A"].zero_()
+    _check_forward(w, inp=inp)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_masked_exponent_overflow(dtype):
+    """A = -16 and dt near 1: within a chunk |G2| passes 128, so the masked upper
+    triangle holds exp2 of large positive numbers (+inf); selection must drop them."""
+    w = _wl("overflow", dtype, 1, 512, 2, 64, 64, 1, 256)
+    inp = make_inputs(w, 6)
+    inp["A"].fill_(-16.0)
+    inp["dt"] = (0.9 + 0.2 * torch.rand(inp["dt"].shape, generator=torch.Generator().manual_seed(6))).to(inp["dt"].dtype)
+    G2_ref, _ = oracle.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    assert np.abs(G2_ref).max() > 1000
+    _check_forward(w, inp=inp)
+
+
+def test_state_continuation():
+    dev = require_gpu()
+    w = _wl("cont", "fp32", 1, 448, 2, 64, 64, 1, 64)
+    inp = make_inputs(w, 7)
+    y_full, hT_full, _, _ = _gpu_forward(inp, w, dev)
+    for L1 in (192, 100):   # chunk-aligned and unaligned split
+        a = {k: (v[:, :L1].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+        bb = {k: (v[:, L1:].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+        y1, hT1, _, _ = _gpu_forward(a, w.with_(seqlen=L1), dev)
+        bb["h0"] = hT1.cpu()
+        y2, hT2, _, _ = _gpu_forward(bb, w.with_(seqlen=w.seqlen - L1), dev)
+        check(f64(torch.cat([y1, y2], 1)), f64(y_full), TOL["fp32"], f"y split at {L1}")
+        check(f64(hT2), f64(hT_full), TOL["fp32"], f"hT split at {L1}")
+
+
+def test_h0_and_hT_may_alias():
+    dev = require_gpu()
+    w = _wl("alias", "bf16", 1, 256, 2, 64, 128, 1, 128)
+    inp = make_inputs(w, 8)
+    d = to_dev(inp, dev)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    state = d["h0"].clone()
+    y, hT = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], state, chunk=w.chunk,
+                            hT=state)
+    torch.cuda.synchronize()
+    check(f64(state), ref["hT"], TOL["bf16"], "hT written over h0")
+    check(f64(y), ref["y"], TOL["bf16"], "y")
+
+
+def test_deterministic_bitwise():
+    dev = require_gpu()
+    w = _wl("det", "bf16", 1, 1024, 4, 64, 256, 1, 256)
+    inp = make_inputs(w, 9)
+    y1, h1, _, _ = _gpu_forward(inp, w, dev)
+    y2, h2, _, _ = _gpu_forward(inp, w, dev)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_stages_compose_to_forward():
+    dev = require_gpu()
+    w = _wl("stages", "bf16", 2, 320, 4, 64, 128, 2, 64)
+    inp = make_inputs(w, 10)
+    d = to_dev(inp, dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    G2, dtT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"])
+    y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
+    yf, hTf, _, _ = _gpu_forward(inp, w, dev)
+    assert torch.equal(y, yf) and torch.equal(hT, hTf)
+
+
+def test_errors_before_launch():
+    dev = require_gpu()
+    w = _wl("err", "bf16", 1, 128, 2, 64, 64, 1, 64)
+    d = to_dev(make_inputs(w, 11), dev)
+    with pytest.raises(ValueError):
+        ssd.ssd_forward(d["x"].cpu(), d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=64)
+    with pytest.raises(ssd.SsdError) as ei:
+        ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=96)
+    assert ei.value.status == 3
+    prob = ssd.problem_of(d["x"], d["B"], 64)
+    small = torch.empty(16, device=dev, dtype=torch.uint8)
+    with pytest.raises(ssd.SsdError) as ei:
+        ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=64, workspace=small)
+    assert ei.value.status == 4
+
+
+# ---------------------------------------------------------------------------
+# the five study workloads at full size, in the benchmark's launch configuration;
+# the oracle computes a sample of (batch, head) units over the whole sequence
+# ---------------------------------------------------------------------------
+FULL = [(name, units) for name, units in [
+    ("fp32_b1_L256_H4_P64_N64_Q64", None),
+    ("bf16_b2_L2048_H24_P64_N128_Q256", [0, 13, 23, 24, 40, 47]),
+    ("bf16_b1_L16384_H32_P64_N256_Q256", [0, 17, 31]),
+    ("bf16_b1_L65536_H32_P64_N512_Q128", [5, 30]),
+    ("bf16_b1_L262144_H16_G2_P64_N128_Q256", [2, 12]),
+]]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,units", FULL, ids=[n for n, _ in FULL])
+def test_full_workload_sampled(name, units):
+    dev = require_gpu()
+    w = WORKLOADS[name]
+    inp = make_inputs(w, 0)
+    print(f"case {name}: units {units}", flush=True)
+    y, hT, ws, prob = _gpu_forward(inp, w, dev)
+    _, _, S = _workspace_views(ws, prob, w)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                         units=units, chunk=w.chunk)
+    u = ref["units"]
+    b_idx, h_idx = u // w.nheads, u % w.nheads
+    y_s = np.stack([f64(y[b, :, h, :]) for b, h in zip(b_idx, h_idx)])
+    tol = TOL[w.dtype]
+    check(y_s, ref["y"], tol, "y (sampled units)")
+    check(np.stack([f64(hT[b, h]) for b, h in zip(b_idx, h_idx)]), ref["hT"], tol, "hT (sampled units)")
+    check(np.stack([f64(S[b, h]) for b, h in zip(b_idx, h_idx)]), ref["snaps"], tol,
+          "chunk-start states (sampled units)")
+    # every output element was written and is finite
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
