@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libssd.so")
-SOURCES = [os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "ssd_api.cpp")]
+SOURCES = [os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "ssd_bf16.hip"),
+           os.path.join(CSRC, "ssd_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -21,6 +22,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed fp32 VALU ops (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: scaling a running state in place then
+    # needs no accumulator-register round trips
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -1,0 +1,543 @@
+// ssd_bf16.hip -- gfx950 state-pass and chunk-output kernels for bf16 inputs
+// (bf16 MFMA operands, fp32 accumulation, fp32 running state).
+//
+// Method: dbyun.net, "基于 NVIDIA CUDA Tile 加速 Mamba-2 高性能前向传播内核",
+// sections "Kernel 2: fwd_pass_state" (decayed chunk jump) and
+// "Kernel 3：compute_out" (decayed chunk output).
+//
+// Both kernels contract over tokens, which are the strided dimension of every
+// input tensor.  Tiles are copied into LDS in their natural token-major layout
+// with 16-byte writes and the token-packed MFMA operands are read back with
+// the gfx950 LDS transpose read (ds_read_b64_tr_b16), so no element-wise
+// transposition happens on the way in.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+__device__ __forceinline__ bf16x8 ld16(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+__device__ __forceinline__ bf16x8 zero8()
+{
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+    return z;
+}
+
+// WG index -> (major, minor) with all minors of one major on the same XCD when
+// `xcd` is set (workgroups are dealt to the 8 XCDs round-robin by index).
+__device__ __forceinline__ void xcd_split(int id, int n_minor, bool xcd, int &major, int &minor)
+{
+    if (xcd) {
+        const int x = id & 7, slot = id >> 3;
+        major = x + 8 * (slot / n_minor);
+        minor = slot % n_minor;
+    } else {
+        major = id / n_minor;
+        minor = id % n_minor;
+    }
+}
+
+// ===========================================================================
+// State pass.  Workgroup = one (batch*head, N tile of NT columns).  It keeps
+// h^T [NT x 64] in fp32 accumulators: wave (ph, nh, kh) owns rows
+// n in [32 nh, 32 nh + 32) and columns p in [32 ph, 32 ph + 32) for the tokens
+// of K-half kh (KS = 2 splits each chunk's tokens over two wave sets whose
+// partial states are summed through LDS at every chunk boundary).
+// Per chunk c, in order:
+//   * issue the global loads of chunk c+2 (x, B, G2, dtT) into registers;
+//   * store S[c] = h (bf16, [P][N] so every lane writes 4 consecutive n);
+//   * h <- exp2(G_last) h + W_c^T X_c on MFMA, operands transpose-read from LDS;
+//   * write chunk c+1 (loaded one chunk earlier) into the other LDS buffer: x as
+//     is, W = bf16(w * B) with w_t = dt_t exp2(G_last - G_t).
+// ===========================================================================
+template <int Q, int NT, int KS>
+__global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
+    const float *__restrict__ dtT, const float *__restrict__ h0, bf16 *__restrict__ S,
+    float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp, int ntiles, int xcd)
+{
+    constexpr int P = 64;
+    constexpr int NWN = NT / 32, NWAVES = 2 * NWN * KS, NTHR = 64 * NWAVES;
+    constexpr int XP = tr_pitch(P), WP = tr_pitch(NT);
+    constexpr int XPC = Q * (P / 8) / NTHR;   // 16-byte x pieces per thread per chunk
+    constexpr int WPC = Q * (NT / 8) / NTHR;  // 16-byte B pieces per thread per chunk
+    constexpr int KSTEPS = Q / 16 / KS;
+    static_assert(XPC >= 1 && WPC >= 1, "tile too small for the workgroup");
+    static_assert((Q * (P / 8)) % NTHR == 0 && (Q * (NT / 8)) % NTHR == 0, "uneven staging");
+
+    __shared__ __attribute__((aligned(16))) bf16 Xs[2][Q * XP];
+    __shared__ __attribute__((aligned(16))) bf16 Ws[2][Q * WP];
+    __shared__ float red[KS > 1 ? (NWAVES / 2) * 16 * 64 : 1];
+    __shared__ float alph[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ph = wave & 1, nh = (wave >> 1) % NWN, kh = wave / (2 * NWN);
+    int bh, nt;
+    xcd_split(blockIdx.x, ntiles, xcd != 0, bh, nt);
+    const int b = bh / H, h = bh % H, g = h / (H / G);
+    const int n_wave = nt * NT + nh * 32;            // first state column of this wave's rows
+    const int p_col = ph * 32 + (lane & 31);          // this lane's p
+    const int n_lane = n_wave + 4 * (lane >> 5);      // + 8q + r for accumulator element 4q + r
+    const int64_t st_off = (int64_t)bh * P * N;
+    const float *Gh = G2 + (int64_t)bh * Lp;
+    const float *dh = dtT + (int64_t)bh * Lp;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
+    const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + nt * NT;
+
+    f32x16 acc = zero_acc();
+    if (h0 != nullptr && kh == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(h0 + st_off + (int64_t)p_col * N + n_lane + 8 * q);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[4 * q + r] = v[r];
+        }
+    }
+
+    // Loads run two chunks ahead of the MFMAs: two register stages alternate
+    // (the chunk loop is unrolled by two so each stage stays in registers).
+    struct Stage {
+        bf16x8 xr[XPC], br[WPC];
+        float gr[WPC], dr[WPC], glast;
+    };
+    // per-thread element offsets of the staged pieces inside one chunk (32-bit:
+    // below Q * stride), plus a uniform 64-bit chunk base
+    int xo[XPC], bo[WPC], to[WPC];
+#pragma unroll
+    for (int r = 0; r < XPC; ++r) {
+        const int id = tid + NTHR * r;
+        xo[r] = (id >> 3) * (int)xstride + (id & 7) * 8;
+    }
+#pragma unroll
+    for (int r = 0; r < WPC; ++r) {
+        const int id = tid + NTHR * r;
+        to[r] = id / (NT / 8);
+        bo[r] = to[r] * (int)bstride + (id % (NT / 8)) * 8;
+    }
+    auto issue = [&](Stage &st, int c) {
+        const int t0 = c * Q;
+        const bf16 *xc = xb + (int64_t)t0 * xstride;
+        const bf16 *bc = Bb + (int64_t)t0 * bstride;
+        if (t0 + Q <= L) {
+#pragma unroll
+            for (int r = 0; r < XPC; ++r) st.xr[r] = ld16(xc + xo[r]);
+#pragma unroll
+            for (int r = 0; r < WPC; ++r) st.br[r] = ld16(bc + bo[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < XPC; ++r) {
+                const int t = (tid + NTHR * r) >> 3;
+                st.xr[r] = (t0 + t < L) ? ld16(xc + xo[r]) : zero8();
+            }
+#pragma unroll
+            for (int r = 0; r < WPC; ++r) st.br[r] = (t0 + to[r] < L) ? ld16(bc + bo[r]) : zero8();
+        }
+#pragma unroll
+        for (int r = 0; r < WPC; ++r) {
+            st.gr[r] = Gh[t0 + to[r]];
+            st.dr[r] = dh[t0 + to[r]];
+        }
+        st.glast = Gh[t0 + Q - 1];
+    };
+    auto commit = [&](const Stage &st, int buf) {
+#pragma unroll
+        for (int r = 0; r < XPC; ++r) {
+            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+            *reinterpret_cast<bf16x8 *>(&Xs[buf][t * XP + oct * 8]) = st.xr[r];
+        }
+#pragma unroll
+        for (int r = 0; r < WPC; ++r) {
+            const int id = tid + NTHR * r, t = id / (NT / 8), oct = id % (NT / 8);
+            const float w = st.dr[r] * fast_exp2(st.glast - st.gr[r]);
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)st.br[r][e] * w);
+            *reinterpret_cast<bf16x8 *>(&Ws[buf][t * WP + oct * 8]) = o;
+        }
+        if (tid == 0) alph[buf] = fast_exp2(st.glast);
+    };
+
+    const int offW = tr_off_natural(lane, WP) + nh * 32;
+    const int offX = tr_off_natural(lane, XP) + ph * 32;
+
+    // One chunk: refill `refill` with chunk c+2, consume LDS buffer `cur` (chunk
+    // c), then move chunk c+1 from `next` into the other buffer.  Loads and
+    // commits are unconditional (indices clamped to the last chunk; the extra
+    // copies near the end are never read) so the body has no branches and the
+    // compiler's wait counts let the c+2 loads stay in flight across the commit.
+    auto step = [&](int c, int cur, const Stage &next, Stage &refill) {
+        issue(refill, min(c + 2, nc - 1));
+
+        if constexpr (KS > 1) {
+            if (kh == 1) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
+            }
+            __syncthreads();
+            if (kh == 0) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
+            } else {
+                acc = zero_acc();
+            }
+        }
+        if (kh == 0) {
+            bf16 *Sc = S + ((int64_t)bh * nc + c) * P * N + (int64_t)p_col * N + n_lane;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[4 * q + r];
+                *reinterpret_cast<bf16x4 *>(Sc + 8 * q) = o;
+            }
+        }
+        const float a = alph[cur];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] *= a;
+
+        const bf16 *wt = Ws[cur] + offW + kh * (Q / KS) * WP;
+        const bf16 *xt = Xs[cur] + offX + kh * (Q / KS) * XP;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const bf16x8 af = cat8(tr_read4(wt + ks * 16 * WP), tr_read4(wt + (ks * 16 + 4) * WP));
+            const bf16x8 bf = cat8(tr_read4(xt + ks * 16 * XP), tr_read4(xt + (ks * 16 + 4) * XP));
+            mma(acc, af, bf);
+        }
+        commit(next, cur ^ 1);
+        __syncthreads();
+    };
+
+    Stage sa, sb;
+    issue(sa, 0);
+    issue(sb, min(1, nc - 1));
+    commit(sa, 0);
+    __syncthreads();
+    int c = 0;
+    for (; c + 1 < nc; c += 2) {
+        step(c, 0, sb, sa);
+        step(c + 1, 1, sa, sb);
+    }
+    if (c < nc) step(c, 0, sb, sa);
+
+    if constexpr (KS > 1) {
+        if (kh == 1) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
+        }
+        __syncthreads();
+        if (kh == 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
+        }
+    }
+    if (hT != nullptr && kh == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = acc[4 * q + r];
+            *reinterpret_cast<f32x4 *>(hT + st_off + (int64_t)p_col * N + n_lane + 8 * q) = o;
+        }
+    }
+}
+
+// ===========================================================================
+// Chunk output.  Workgroup = one (chunk, batch*head), Q/64 waves; wave w owns
+// row tiles I0 = w and I1 = Q/32-1-w (32 tokens each), so every wave handles
+// the same number (Q/32 + 1) of causal tile pairs (J, I), J <= I.  The output
+// is built transposed, Y^T [64 p x 32 tokens] per row tile.
+//
+// Phase 1 streams N in slices of 64: the slice of B (all chunk rows) and of S
+// (all p) is staged in LDS; each wave reads its C rows from global and
+//   * accumulates (B C^T)[j, i] for its tile pairs (accumulators live across
+//     all slices; slot s <= w is (J = s, I0), slot s > w is (J = s - w - 1, I1));
+//   * accumulates Y^T += S C^T (the inter-chunk term).
+// Phase 2 turns every C B^T tile into the decay matrix
+//   M[j, i] = (i >= j) ? CB[j, i] * exp2(G_i - G_j) : 0      (selection, never a product with a mask)
+// rounded to bf16 and parked in LDS (it reuses the B/S staging space).  Off the
+// diagonal (J < I) the decay factors exactly into exp2(G_i - G_e) * exp2(G_e - G_j)
+// with e the last token of tile J; both factors are <= 1, the second is a
+// per-token table, so such a tile costs one exp2 per lane instead of sixteen.
+// Phase 3, per row tile: scale Y^T column i by exp2(G_i), add M(J, I) (dt x)_J
+// for J <= I with M read back as the B operand and (dt x)^T transpose-read
+// from LDS in the accumulator's token order, then add D x and store.
+// ===========================================================================
+template <int Q>
+__global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+    const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
+    const float *__restrict__ D, bf16 *__restrict__ y, int L, int H, int G, int N, int nc, int Lp,
+    int xcd)
+{
+    constexpr int P = 64, NI = Q / 32, NTHR = Q, NW = Q / 64, NSLOT = NI + 1, NS = 64;
+    constexpr int XP = tr_pitch(P), BP = frag_pitch(NS), SP = frag_pitch(NS);
+    constexpr int BS_EL = Q * BP, SS_EL = P * SP, MB_EL = NW * NSLOT * 2 * 64 * 8;
+    constexpr int U_EL = (BS_EL + SS_EL > MB_EL) ? BS_EL + SS_EL : MB_EL;
+    __shared__ __attribute__((aligned(16))) bf16 Xd[Q * XP];
+    __shared__ __attribute__((aligned(16))) bf16 U[U_EL];
+    __shared__ __attribute__((aligned(16))) float Gs[Q];
+    __shared__ __attribute__((aligned(16))) float We[Q];   // exp2(G_e - G_j), e = end of j's tile
+    bf16 *Bs = U, *Ss = U + BS_EL, *Mb = U;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int bH = gridDim.x / nc;
+    int c, bh;
+    xcd_split(blockIdx.x, bH, xcd != 0, c, bh);
+    const int b = bh / H, h = bh % H, g = h / (H / G);
+    const int t0 = c * Q;
+    const bool full = t0 + Q <= L;
+    const int64_t xstride = (int64_t)H * P, cstride = (int64_t)G * N;
+    const bf16 *xb = x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
+    const bf16 *Bb = Bm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N;
+    const bf16 *Cb = Cm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N;
+    const bf16 *Sb = S + ((int64_t)bh * nc + c) * P * N;
+    const float *Gh = G2 + (int64_t)bh * Lp + t0;
+    const float *dh = dtT + (int64_t)bh * Lp + t0;
+    const int kq = 8 * (lane >> 5);
+    const int I0 = w, I1 = NI - 1 - w;
+
+    const bool v0 = full || t0 + I0 * 32 + (lane & 31) < L;
+    const bool v1 = full || t0 + I1 * 32 + (lane & 31) < L;
+    const bf16 *crow0 = Cb + (I0 * 32 + (lane & 31)) * (int)cstride + kq;
+    const bf16 *crow1 = Cb + (I1 * 32 + (lane & 31)) * (int)cstride + kq;
+
+    // Registers holding the next N slice while the current one is multiplied:
+    // 8 B pieces and P*8/Q S pieces per thread (16 bytes each), 4+4 C fragments.
+    constexpr int SPC = P * 8 / NTHR;
+    bf16x8 bq[8], sq[SPC], c0n[NS / 16], c1n[NS / 16];
+    auto load_slice = [&](int n0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+            bq[r] = (full || t0 + t < L) ? ld16(Bb + t * (int)cstride + n0 + oct * 8) : zero8();
+        }
+#pragma unroll
+        for (int r = 0; r < SPC; ++r) {
+            const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
+            sq[r] = ld16(Sb + p * N + n0 + oct * 8);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NS / 16; ++ks) {
+            c0n[ks] = v0 ? ld16(crow0 + n0 + ks * 16) : zero8();
+            c1n[ks] = v1 ? ld16(crow1 + n0 + ks * 16) : zero8();
+        }
+    };
+
+    // (dt x) tile, token-major, and the chunk's decays; the first N slice is
+    // requested right behind the x tile so both latencies overlap
+    {
+        bf16x8 xv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+            xv[r] = (full || t0 + t < L) ? ld16(xb + t * (int)xstride + oct * 8) : zero8();
+        }
+        const float gt = Gh[tid];
+        const float ge = Gh[tid | 31];
+        float d[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) d[r] = dh[(tid + NTHR * r) >> 3];
+        load_slice(0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+            bf16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)xv[r][e] * d[r]);
+            *reinterpret_cast<bf16x8 *>(&Xd[t * XP + oct * 8]) = o;
+        }
+        Gs[tid] = gt;
+        We[tid] = fast_exp2(ge - gt);
+    }
+
+    f32x16 cb[NSLOT];
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) cb[s] = zero_acc();
+    f32x16 ya[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) { ya[s][0] = zero_acc(); ya[s][1] = zero_acc(); }
+
+    // ---------------- phase 1: C B^T tiles and S C^T over N slices ----------------
+    for (int n0 = 0; n0 < N; n0 += NS) {
+        __syncthreads();   // previous slice consumed; first time: Xd, Gs, We written
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+            *reinterpret_cast<bf16x8 *>(&Bs[t * BP + oct * 8]) = bq[r];
+        }
+#pragma unroll
+        for (int r = 0; r < SPC; ++r) {
+            const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
+            *reinterpret_cast<bf16x8 *>(&Ss[p * SP + oct * 8]) = sq[r];
+        }
+        bf16x8 cf0[NS / 16], cf1[NS / 16];
+#pragma unroll
+        for (int ks = 0; ks < NS / 16; ++ks) { cf0[ks] = c0n[ks]; cf1[ks] = c1n[ks]; }
+        // next slice (the last iteration re-requests the last slice; never used)
+        load_slice(min(n0 + NS, N - NS));
+        __syncthreads();
+
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
+            const bool side0 = s <= w;
+            const int J = side0 ? s : s - w - 1;
+            const bf16 *brow = Bs + (J * 32 + (lane & 31)) * BP + kq;
+            if (side0) {
+#pragma unroll
+                for (int ks = 0; ks < NS / 16; ++ks)
+                    mma(cb[s], *reinterpret_cast<const bf16x8 *>(brow + ks * 16), cf0[ks]);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < NS / 16; ++ks)
+                    mma(cb[s], *reinterpret_cast<const bf16x8 *>(brow + ks * 16), cf1[ks]);
+            }
+        }
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const bf16 *srow = Ss + (pp * 32 + (lane & 31)) * SP + kq;
+#pragma unroll
+            for (int ks = 0; ks < NS / 16; ++ks) {
+                const bf16x8 sf = *reinterpret_cast<const bf16x8 *>(srow + ks * 16);
+                mma(ya[0][pp], sf, cf0[ks]);
+                mma(ya[1][pp], sf, cf1[ks]);
+            }
+        }
+    }
+    __syncthreads();   // B/S staging space becomes the M store
+
+    // ---------------- phase 2: decay, causal selection, bf16, into LDS ----------------
+    const float gi0 = Gs[I0 * 32 + (lane & 31)], gi1 = Gs[I1 * 32 + (lane & 31)];
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+        const bool side0 = s <= w;
+        const int J = side0 ? s : s - w - 1;
+        const int I = side0 ? I0 : I1;
+        const float gi = side0 ? gi0 : gi1;
+        const int jrow = J * 32 + 4 * (lane >> 5);   // + 8q + r for element 4q + r
+        bf16x8 m[2];
+        if (J < I) {
+            const float ci = fast_exp2(gi - Gs[J * 32 + 31]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 we = *reinterpret_cast<const f32x4 *>(&We[jrow + 8 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[q >> 1][4 * (q & 1) + r] = (bf16)(cb[s][4 * q + r] * we[r] * ci);
+            }
+        } else {
+            const int i_loc = I * 32 + (lane & 31);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gs[jrow + 8 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float dec = fast_exp2(gi - gj[r]);
+                    const float val = cb[s][4 * q + r] * dec;
+                    m[q >> 1][4 * (q & 1) + r] = (bf16)((i_loc >= jrow + 8 * q + r) ? val : 0.0f);
+                }
+            }
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+            *reinterpret_cast<bf16x8 *>(&Mb[(((w * NSLOT + s) * 2 + sub) * 64 + lane) * 8]) = m[sub];
+    }
+    // each lane reads back only what it wrote: no barrier needed
+
+    // ---------------- phase 3: Y^T += M (dt x), then D x and store ----------------
+    const int offX = tr_off_accorder(lane, XP);
+    const float Dh = D[h];
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        const int I = side == 0 ? I0 : I1;
+        const int i_loc = I * 32 + (lane & 31);
+        const float si = fast_exp2(side == 0 ? gi0 : gi1);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { ya[side][0][v] *= si; ya[side][1][v] *= si; }
+        const int s0 = side == 0 ? 0 : w + 1;
+        for (int J = 0; J <= I; ++J) {
+            const bf16 *mrow = Mb + (((w * NSLOT + s0 + J) * 2) * 64 + lane) * 8;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                const bf16x8 mf = *reinterpret_cast<const bf16x8 *>(mrow + sub * 64 * 8);
+                const bf16 *xt = Xd + offX + (J * 32 + 16 * sub) * XP;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const bf16x8 af = cat8(tr_read4(xt + pp * 32), tr_read4(xt + pp * 32 + 8 * XP));
+                    mma(ya[side][pp], af, mf);
+                }
+            }
+        }
+        if (full || t0 + i_loc < L) {
+            const int yo = i_loc * (int)xstride;
+            bf16 *yb = y + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
+                    const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xb + yo + p);
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[side][pp][4 * q + r] + Dh * (float)xv[r]);
+                    *reinterpret_cast<bf16x4 *>(yb + yo + p) = o;
+                }
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+template <int Q, int NT, int KS>
+static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
+                            const float *dtT, const float *h0, void *S, float *hT, hipStream_t st)
+{
+    const int ntiles = (int)(s.N / NT);
+    const int bH = (int)(s.b * s.H);
+    const int xcd = (bH % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NT, KS>), dim3((unsigned)(bH * ntiles)),
+                       dim3(64 * 2 * (NT / 32) * KS), 0, st, (const bf16 *)x, (const bf16 *)B, G2,
+                       dtT, h0, (bf16 *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
+                       (int)s.Lp, ntiles, xcd);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
+                                  const float *dtT, const float *h0, void *S, float *hT,
+                                  hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return sp_launch<64, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
+    case 128: return sp_launch<128, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
+    default: return sp_launch<256, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
+    }
+}
+
+template <int Q>
+static hipError_t co_launch(const Shape &s, const void *x, const void *B, const void *C,
+                            const float *G2, const float *dtT, const void *S, const float *D,
+                            void *y, hipStream_t st)
+{
+    const int xcd = (s.nc % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((chunk_out_bf16_kernel<Q>), dim3((unsigned)(s.nc * s.b * s.H)), dim3(Q), 0,
+                       st, (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
+                       (const bf16 *)S, D, (bf16 *)y, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
+                       (int)s.nc, (int)s.Lp, xcd);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
+                                 const float *G2, const float *dtT, const void *S, const float *D,
+                                 void *y, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return co_launch<64>(s, x, B, C, G2, dtT, S, D, y, st);
+    case 128: return co_launch<128>(s, x, B, C, G2, dtT, S, D, y, st);
+    default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, st);
+    }
+}
+
+}  // namespace ssd

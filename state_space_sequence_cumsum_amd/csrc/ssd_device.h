@@ -95,4 +95,61 @@ __device__ __forceinline__ f32x16 zero_acc()
     return a;
 }
 
+// ---------------------------------------------------------------------------
+// LDS transpose reads (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives, for e = 0..3, element i%4 of the 4-element row segment
+// addressed by lane 4e + i/4 of the same group.  So if the 16 lanes address a
+// 4 (k) x 16 (r) block of a k-major tile -- lane m pointing at row m/4, column
+// 4*(m%4) -- lane i gets 4 consecutive k of column i: a k-packed MFMA operand
+// read straight out of a tile stored in its natural (token-major) layout.
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ bf16x4 tr_read4(const bf16 *p)
+{
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-lane element offset of the transpose-read fragment of a k-major tile with
+// row pitch `pitch` (elements).  Natural order: element e of lane l is row
+// 8*(l/32) + e; column l%32.  The second 4-row read sits 4 rows further on.
+__device__ __forceinline__ int tr_off_natural(int lane, int pitch)
+{
+    return (8 * (lane >> 5) + ((lane & 15) >> 2)) * pitch + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
+// Accumulator order: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, the row
+// order in which a 32x32 accumulator hands its 16-deep half to a lane.  The
+// second 4-row read sits 8 rows further on.
+__device__ __forceinline__ int tr_off_accorder(int lane, int pitch)
+{
+    return (4 * (lane >> 5) + ((lane & 15) >> 2)) * pitch + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+}
+
+// Row pitch (elements, bf16) for transpose-read tiles: at least `cols`, a
+// multiple of 8 (16-byte rows), and an odd multiple of 32 bytes modulo 128 so
+// that the four rows one 16-lane group touches fall in distinct bank ranges.
+constexpr int tr_pitch(int cols)
+{
+    int b = (cols * 2 + 31) / 32 * 32;
+    while ((b % 128) != 32 && (b % 128) != 96) b += 32;
+    return b / 2;
+}
+
+// Row pitch (elements, bf16) for tiles read with 16-byte fragments (lane l: row
+// l%32, bytes 16*(l/32) of a 32-byte k-slice): 16 bytes more than a multiple of
+// 128 bytes so 16 consecutive rows hit 16 distinct 16-byte bank groups.
+constexpr int frag_pitch(int cols)
+{
+    int b = (cols * 2 + 127) / 128 * 128 + 16;
+    return b / 2;
+}
+
 }  // namespace ssd

@@ -15,58 +15,69 @@ namespace ssd {
 
 // ===========================================================================
 // Stage 1: chunk-local cumsum of A*dt, times log2(e), transposed to [b, H, Lp].
-// One workgroup per (chunk, block of 32 heads, batch).  The [Q x 32] dt tile is
-// read row by row (heads contiguous) into LDS, then each wave scans one head's
-// Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane shuffle scan
-// adds the lane prefixes, and the results are written token-contiguous.
+// One workgroup per (chunk, block of 4 heads, batch), one wave per head.  The
+// [Q x 4] dt tile is read row by row (heads contiguous) into LDS, then each wave
+// scans its head's Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane
+// shuffle scan adds the lane prefixes, and the results are written
+// token-contiguous.  Padded tokens (last chunk) get dt = 0 and repeat the last
+// valid cumsum value exactly.
 // ===========================================================================
-template <typename T>
+template <typename T, int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__ dt,
                                                            const float *__restrict__ A,
                                                            float *__restrict__ G2,
                                                            float *__restrict__ dtT, int L, int H,
-                                                           int Q, int Lp)
+                                                           int Lp)
 {
-    __shared__ float tile[256][33];
-    const int c = blockIdx.x, hb = blockIdx.y * 32, b = blockIdx.z;
-    const int nh = min(32, H - hb);
+    constexpr int HB = 4, PER = Q / 64;
+    __shared__ float tile[Q][HB + 1];
+    const int c = blockIdx.x, hb = blockIdx.y * HB, b = blockIdx.z;
+    const int nh = min(HB, H - hb);
     const int t0 = c * Q;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int idx = tid; idx < Q * 32; idx += 256) {
-        const int t = idx >> 5, hh = idx & 31;
+    for (int idx = tid; idx < Q * HB; idx += 256) {
+        const int t = idx / HB, hh = idx % HB;
         float v = 0.0f;
         if (hh < nh && t0 + t < L) v = (float)dt[((int64_t)b * L + t0 + t) * H + hb + hh];
         tile[t][hh] = v;
     }
     __syncthreads();
+    if (wave >= nh) return;
 
-    const int per = Q >> 6;  // tokens per lane: 1, 2 or 4
-    for (int hh = wave; hh < nh; hh += 4) {
-        const float a = A[hb + hh];
-        float part[4], run = 0.0f;
-        for (int j = 0; j < per; ++j) {
-            run += a * tile[lane * per + j][hh];
-            part[j] = run;
-        }
-        float incl = run;
+    const int hh = wave;
+    const float a = A[hb + hh];
+    float part[PER], run = 0.0f;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += up;
-        }
-        float excl = __shfl_up(incl, 1, 64);
-        if (lane == 0) excl = 0.0f;
-        const int64_t base = ((int64_t)b * H + hb + hh) * Lp + t0 + lane * per;
-        for (int j = 0; j < per; ++j) {
-            G2[base + j] = (excl + part[j]) * kLog2e;
-            dtT[base + j] = tile[lane * per + j][hh];
-        }
+    for (int j = 0; j < PER; ++j) {
+        run += a * tile[lane * PER + j][hh];
+        part[j] = run;
+    }
+    float incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float up = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += up;
+    }
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0f;
+    const int last = min(L - t0, Q) - 1;
+    float tail = 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (j == last % PER) tail = (excl + part[j]) * kLog2e;
+    tail = __shfl(tail, last / PER, 64);
+    const int64_t base = ((int64_t)b * H + hb + hh) * Lp + t0 + lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int t = lane * PER + j;
+        G2[base + j] = (t <= last) ? (excl + part[j]) * kLog2e : tail;
+        dtT[base + j] = tile[t][hh];
     }
 }
 
 // ===========================================================================
-// Stage 2: chunk-start states.  One workgroup per (N tile of 64, batch*head),
+// Stage 2, fp32 inputs: chunk-start states.  One workgroup per (N tile of 64, batch*head),
 // four waves, each owning a 32x32 (P x N) quarter of the fp32 state in MFMA
 // accumulators.  Serially over chunks: stage X_c^T and W_c^T = (w * B_c)^T into
 // LDS (token-contiguous rows, so MFMA fragments are 8 consecutive tokens),
@@ -167,7 +178,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 }
 
 // ===========================================================================
-// Stage 3: chunk output.  One workgroup per (chunk, batch*head) with Q/64 waves.
+// Stage 3, fp32 inputs: chunk output.  One workgroup per (chunk, batch*head) with Q/64 waves.
 // The chunk has Q/32 row tiles of 32 tokens; wave w takes tiles w and Q/32-1-w so
 // every wave does the same number of causal tile pairs.  The output is built
 // transposed, Y^T [P x 32 tokens], so that
@@ -285,14 +296,25 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
 // ===========================================================================
 // Launchers
 // ===========================================================================
+template <typename T, int Q>
+static hipError_t cumsum_tq(const Shape &s, const void *dt, const float *A, float *G2, float *dtT,
+                            hipStream_t st)
+{
+    dim3 grid((unsigned)s.nc, (unsigned)((s.H + 3) / 4), (unsigned)s.b);
+    hipLaunchKernelGGL((chunk_cumsum_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)dt, A, G2,
+                       dtT, (int)s.L, (int)s.H, (int)s.Lp);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t cumsum_t(const Shape &s, const void *dt, const float *A, float *G2, float *dtT,
                            hipStream_t st)
 {
-    dim3 grid((unsigned)s.nc, (unsigned)((s.H + 31) / 32), (unsigned)s.b);
-    hipLaunchKernelGGL(chunk_cumsum_kernel<T>, grid, dim3(256), 0, st, (const T *)dt, A, G2, dtT,
-                       (int)s.L, (int)s.H, (int)s.Q, (int)s.Lp);
-    return hipGetLastError();
+    switch (s.Q) {
+    case 64: return cumsum_tq<T, 64>(s, dt, A, G2, dtT, st);
+    case 128: return cumsum_tq<T, 128>(s, dt, A, G2, dtT, st);
+    default: return cumsum_tq<T, 256>(s, dt, A, G2, dtT, st);
+    }
 }
 
 hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, float *G2,
@@ -328,7 +350,7 @@ hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const
                              const float *dtT, const float *h0, void *S, float *hT,
                              hipStream_t st)
 {
-    return s.bf16 ? state_pass_t<bf16>(s, x, B, G2, dtT, h0, S, hT, st)
+    return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, dtT, h0, S, hT, st)
                   : state_pass_t<float>(s, x, B, G2, dtT, h0, S, hT, st);
 }
 
@@ -360,7 +382,7 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, hipStream_t st)
 {
-    return s.bf16 ? chunk_out_t<bf16>(s, x, B, C, G2, dtT, S, D, y, st)
+    return s.bf16 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, st)
                   : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, st);
 }
 

@@ -23,4 +23,12 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, hipStream_t st);
 
+// bf16 kernels (ssd_bf16.hip)
+hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
+                                  const float *dtT, const float *h0, void *S, float *hT,
+                                  hipStream_t st);
+hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
+                                 const float *G2, const float *dtT, const void *S, const float *D,
+                                 void *y, hipStream_t st);
+
 }  // namespace ssd
