@@ -30,8 +30,8 @@ def algorithmic(w):
     """Bytes and flops each kernel must move/compute for workload w (one launch).
 
     Per (token, head), e = input element bytes, s = snapshot element bytes:
-      cumsum:     e (dt) + 8 (G2 and dtT written, fp32)
-      state pass: e*P (x) + 8 (G2, dtT) + e*N*G/H (B, shared by a group) + s*P*N/Q (S written)
+      cumsum:     e (dt) + 12 (G2, dtT and wT written, fp32)
+      state pass: e*P (x) + 4 (wT) + e*N*G/H (B, shared by a group) + s*P*N/Q (S written)
                   + 8*P*N per (batch, head) for h0 and hT;  flops 2*N*P
       chunk out:  2*e*P (x, y) + 8 (G2, dtT) + 2*e*N*G/H (B, C) + s*P*N/Q (S read);
                   flops 2*N*P + (Q+1)*P + (Q+1)*N*G/H  (causal lower triangle, C B^T once per group)
@@ -42,8 +42,8 @@ def algorithmic(w):
     th = w.batch * w.seqlen * H          # (token, head) pairs
     bh = w.batch * H
     return {
-        "chunk_cumsum": {"bytes": th * (e + 8), "flops": 2 * th},
-        "state_pass": {"bytes": th * (e * P + 8 + e * N * G / H + s * P * N / Q)
+        "chunk_cumsum": {"bytes": th * (e + 12), "flops": 2 * th},
+        "state_pass": {"bytes": th * (e * P + 4 + e * N * G / H + s * P * N / Q)
                        + (8 * P * N * bh if w.has_h0 else 4 * P * N * bh),
                        "flops": th * 2 * N * P},
         "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),
@@ -103,13 +103,8 @@ def main():
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev, dtype=torch.float32)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
     ws = ssd.workspace_for(prob, dev)
-    g2_off, dtt_off, s_off = ssd.ssd_workspace_layout(prob)
-    nc, Lp = w.nchunks, w.nchunks * w.chunk
-    G2 = ws[g2_off:g2_off + 4 * w.batch * w.nheads * Lp].view(torch.float32).view(w.batch, w.nheads, Lp)
-    dtT = ws[dtt_off:dtt_off + 4 * w.batch * w.nheads * Lp].view(torch.float32).view(w.batch, w.nheads, Lp)
-    es = 2 if w.dtype == "bf16" else 4
-    S = ws[s_off:s_off + es * w.batch * w.nheads * nc * w.headdim * w.dstate]
-    S = S.view(io).view(w.batch, w.nheads, nc, w.headdim, w.dstate)
+    views = ssd.workspace_views(prob, ws)
+    G2, dtT, wT, S = views["G2"], views["dtT"], views["wT"], views["S"]
     stream = torch.cuda.current_stream(dev)
 
     def forward():
@@ -134,9 +129,9 @@ def main():
     for k in range(args.steps):
         e = evs[k]
         e[0].record(stream)
-        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, stream=stream)
+        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, wT, stream=stream)
         e[1].record(stream)
-        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"], S, hT, stream=stream)
+        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"], S, hT, stream=stream)
         e[2].record(stream)
         ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"], y, stream=stream)
         e[3].record(stream)

@@ -22,7 +22,7 @@
  *     B, C    [b, L, G, N]      element type `dtype`; head h reads group h / (H / G)
  *     A, D    [H]               float32 (per-head decay rate and skip weight)
  *     h0, hT  [b, H, P, N]      float32 (initial and final state)
- *     G2, dtT [b, H, Lp]        float32 (stage-1 outputs, token-contiguous per head)
+ *     G2, dtT, wT [b, H, Lp]    float32 (stage-1 outputs, token-contiguous per head)
  *     S       [b, H, nc, P, N]  bfloat16 when dtype is SSD_BF16, float32 when SSD_F32
  * `problem` is a host pointer.  `stream` is a hipStream_t (NULL = the null stream).
  *
@@ -73,25 +73,28 @@ typedef struct {
 /* Host-only checks of `problem` (dimensions, divisibility, supported set).  No GPU. */
 ssd_status ssd_validate(const ssd_problem *problem);
 
-/* Bytes of device workspace ssd_forward needs (G2, dtT and S, each 256-byte aligned);
+/* Bytes of device workspace ssd_forward needs (G2, dtT, wT and S, each 256-byte aligned);
  * 0 if `problem` is not valid.  Host-only. */
 size_t ssd_workspace_bytes(const ssd_problem *problem);
 
 /* Stage 1 (section "Kernel 1：计算累积和"): for each (b, h) and token t of chunk c,
  *     G2[b,h,t]  = log2(e) * sum_{k = cQ .. t} A[h] * dt[b,k,h]     (fp32 sum, then scaled)
  *     dtT[b,h,t] = float(dt[b,t,h])
- * For padded positions t >= L: dtT = 0 and G2 repeats the chunk's last valid value.
- * Reads dt, A; writes G2 and dtT ([b, H, Lp]). */
+ *     wT[b,h,t]  = dtT[b,h,t] * exp2(G2[b,h,cQ+Q-1] - G2[b,h,t])  (the state-pass weight of
+ *                  token t: its dt times the decay from t to the end of its chunk)
+ * For padded positions t >= L: dtT = wT = 0 and G2 repeats the chunk's last valid value.
+ * Reads dt, A; writes G2, dtT and wT ([b, H, Lp]). */
 ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A,
-                            float *G2, float *dtT, void *stream);
+                            float *G2, float *dtT, float *wT, void *stream);
 
 /* Stage 2 (section "Kernel 2: fwd_pass_state", the decayed chunk jump): serially over
  * chunks c, S[b,h,c] = h (the state at the chunk start, h = h0 or 0 for c = 0), then
- *     h <- exp2(G2_last) h + X_c^T W_c,   W_c[t,n] = round(dt_t exp2(G2_last - G2_t) B[t,n])
- * (W rounded to the input type).  After the last chunk hT = h (skipped when hT is NULL).
- * h0 may be NULL (zero initial state).  Reads x, B, G2, dtT, h0; writes S, hT. */
+ *     h <- exp2(G2_last) h + X_c^T W_c,   W_c[t,n] = round(wT_t B[t,n])
+ * with G2_last = G2 at the chunk's last position and W rounded to the input type.
+ * After the last chunk hT = h (skipped when hT is NULL).  h0 may be NULL (zero
+ * initial state).  Reads x, B, G2, wT, h0; writes S, hT. */
 ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
-                          const float *G2, const float *dtT, const float *h0, void *S,
+                          const float *G2, const float *wT, const float *h0, void *S,
                           float *hT, void *stream);
 
 /* Stage 3 (section "Kernel 3：compute_out", the decayed chunk output): for each chunk,
@@ -106,7 +109,7 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
                          const float *D, void *y, void *stream);
 
 /* The whole forward pass: stage 1, 2 and 3 on `stream`, no host synchronisation.
- * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds G2, dtT and S;
+ * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds G2, dtT, wT and S;
  * its contents on return are those intermediates.  h0 may be NULL; hT may be NULL
  * (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
@@ -114,9 +117,9 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
                        const float *h0, void *y, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream);
 
-/* Offsets (bytes) of G2, dtT and S inside an ssd_forward workspace.  Host-only. */
+/* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
-                                size_t *off_S);
+                                size_t *off_wT, size_t *off_S);
 
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -8,9 +8,9 @@ missing.
 from .binding import (SSD_BF16, SSD_F32, SsdError, SsdProblem, make_problem, problem_of,
                       ssd_chunk_cumsum, ssd_chunk_out, ssd_forward, ssd_state_pass,
                       ssd_status_string, ssd_validate, ssd_workspace_bytes, ssd_workspace_layout,
-                      workspace_for)
+                      workspace_for, workspace_views)
 
 __all__ = ["SSD_BF16", "SSD_F32", "SsdError", "SsdProblem", "make_problem", "problem_of",
            "ssd_chunk_cumsum", "ssd_chunk_out", "ssd_forward", "ssd_state_pass",
            "ssd_status_string", "ssd_validate", "ssd_workspace_bytes", "ssd_workspace_layout",
-           "workspace_for"]
+           "workspace_for", "workspace_views"]

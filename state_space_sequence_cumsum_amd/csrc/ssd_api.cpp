@@ -47,7 +47,7 @@ ssd::Shape make_shape(const ssd_problem *p)
 }
 
 struct Layout {
-    size_t g2, dtt, S, total;
+    size_t g2, dtt, wt, S, total;
 };
 
 Layout layout_of(const ssd::Shape &s)
@@ -57,7 +57,8 @@ Layout layout_of(const ssd::Shape &s)
     Layout l;
     l.g2 = 0;
     l.dtt = align_up(cum);
-    l.S = l.dtt + align_up(cum);
+    l.wt = l.dtt + align_up(cum);
+    l.S = l.wt + align_up(cum);
     l.total = l.S + align_up(snap);
     return l;
 }
@@ -82,36 +83,37 @@ size_t ssd_workspace_bytes(const ssd_problem *problem)
 }
 
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
-                                size_t *off_S)
+                                size_t *off_wT, size_t *off_S)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!off_G2 || !off_dtT || !off_S) return SSD_ERR_NULL_ARG;
+    if (!off_G2 || !off_dtT || !off_wT || !off_S) return SSD_ERR_NULL_ARG;
     const Layout l = layout_of(make_shape(problem));
     *off_G2 = l.g2;
     *off_dtT = l.dtt;
+    *off_wT = l.wt;
     *off_S = l.S;
     return SSD_OK;
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A, float *G2,
-                            float *dtT, void *stream)
+                            float *dtT, float *wT, void *stream)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!dt || !A || !G2 || !dtT) return SSD_ERR_NULL_ARG;
-    return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT,
+    if (!dt || !A || !G2 || !dtT || !wT) return SSD_ERR_NULL_ARG;
+    return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT, wT,
                                                (hipStream_t)stream));
 }
 
 ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
-                          const float *G2, const float *dtT, const float *h0, void *S, float *hT,
+                          const float *G2, const float *wT, const float *h0, void *S, float *hT,
                           void *stream)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!x || !B || !G2 || !dtT || !S) return SSD_ERR_NULL_ARG;
-    return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, dtT, h0, S, hT,
+    if (!x || !B || !G2 || !wT || !S) return SSD_ERR_NULL_ARG;
+    return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, wT, h0, S, hT,
                                              (hipStream_t)stream));
 }
 
@@ -139,12 +141,13 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
     char *ws = static_cast<char *>(workspace);
     float *G2 = reinterpret_cast<float *>(ws + l.g2);
     float *dtT = reinterpret_cast<float *>(ws + l.dtt);
+    float *wT = reinterpret_cast<float *>(ws + l.wt);
     void *S = ws + l.S;
     hipStream_t hs = (hipStream_t)stream;
 
-    ssd_status r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, hs));
+    ssd_status r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
     if (r != SSD_OK) return r;
-    r = hip_status(ssd::launch_state_pass(s, x, B, G2, dtT, h0, S, hT, hs));
+    r = hip_status(ssd::launch_state_pass(s, x, B, G2, wT, h0, S, hT, hs));
     if (r != SSD_OK) return r;
     return hip_status(ssd::launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, hs));
 }

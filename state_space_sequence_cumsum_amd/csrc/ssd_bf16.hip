@@ -45,30 +45,42 @@ __device__ __forceinline__ void xcd_split(int id, int n_minor, bool xcd, int &ma
 // n in [32 nh, 32 nh + 32) and columns p in [32 ph, 32 ph + 32) for the tokens
 // of K-half kh (KS = 2 splits each chunk's tokens over two wave sets whose
 // partial states are summed through LDS at every chunk boundary).
+//
+// Operands, both k-packed by token:
+//   * X (B operand): the x tile is copied into LDS as is, token-major
+//     [t][p], with 16-byte writes of whole token rows, and read back with the
+//     LDS transpose read;
+//   * W (A operand): each thread loads an 8-token x WC-column block of B,
+//     scales token t by its weight w_t (from stage 1) and bf16-packs the pairs
+//     (t, t+1) of each column, which is already the k-packed layout WT[n][t];
+//     read back as one 16-byte fragment per MFMA.
+//
 // Per chunk c, in order:
-//   * issue the global loads of chunk c+2 (x, B, G2, dtT) into registers;
+//   * issue the global loads of chunk c+2 (x, B, w, G_last) into registers;
 //   * store S[c] = h (bf16, [P][N] so every lane writes 4 consecutive n);
-//   * h <- exp2(G_last) h + W_c^T X_c on MFMA, operands transpose-read from LDS;
-//   * write chunk c+1 (loaded one chunk earlier) into the other LDS buffer: x as
-//     is, W = bf16(w * B) with w_t = dt_t exp2(G_last - G_t).
+//   * h <- exp2(G_last) h + W_c^T X_c on MFMA;
+//   * write chunk c+1 (loaded one chunk earlier) into the other LDS buffer.
 // ===========================================================================
 template <int Q, int NT, int KS>
 __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ dtT, const float *__restrict__ h0, bf16 *__restrict__ S,
+    const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
     float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp, int ntiles, int xcd)
 {
     constexpr int P = 64;
     constexpr int NWN = NT / 32, NWAVES = 2 * NWN * KS, NTHR = 64 * NWAVES;
-    constexpr int XP = tr_pitch(P), WP = tr_pitch(NT);
-    constexpr int XPC = Q * (P / 8) / NTHR;   // 16-byte x pieces per thread per chunk
-    constexpr int WPC = Q * (NT / 8) / NTHR;  // 16-byte B pieces per thread per chunk
     constexpr int KSTEPS = Q / 16 / KS;
-    static_assert(XPC >= 1 && WPC >= 1, "tile too small for the workgroup");
-    static_assert((Q * (P / 8)) % NTHR == 0 && (Q * (NT / 8)) % NTHR == 0, "uneven staging");
+    constexpr int XP = tr_pitch(P);                  // token-major x rows (elements)
+    constexpr int PT = Q + 8;                        // k-packed W rows (elements)
+    constexpr int XPC = Q * (P / 8) / NTHR;          // 16-byte x pieces per thread
+    constexpr int WC = Q * NT / (8 * NTHR);          // W block: 8 tokens x WC columns
+    constexpr int WD = (WC + 1) / 2;                 // dwords per loaded B row piece
+    static_assert(XPC >= 1 && (Q * (P / 8)) % NTHR == 0, "x staging cover");
+    static_assert(WC == 1 || WC == 2 || WC == 4 || WC == 8, "B staging block width");
+    static_assert((Q / 8) * (NT / WC) == NTHR, "B staging cover");
 
     __shared__ __attribute__((aligned(16))) bf16 Xs[2][Q * XP];
-    __shared__ __attribute__((aligned(16))) bf16 Ws[2][Q * WP];
+    __shared__ __attribute__((aligned(16))) bf16 WT[2][NT * PT];
     __shared__ float red[KS > 1 ? (NWAVES / 2) * 16 * 64 : 1];
     __shared__ float alph[2];
 
@@ -82,7 +94,7 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
     const int n_lane = n_wave + 4 * (lane >> 5);      // + 8q + r for accumulator element 4q + r
     const int64_t st_off = (int64_t)bh * P * N;
     const float *Gh = G2 + (int64_t)bh * Lp;
-    const float *dh = dtT + (int64_t)bh * Lp;
+    const float *wh = wT + (int64_t)bh * Lp;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
     const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + nt * NT;
@@ -97,71 +109,83 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
         }
     }
 
-    // Loads run two chunks ahead of the MFMAs: two register stages alternate
-    // (the chunk loop is unrolled by two so each stage stays in registers).
-    struct Stage {
-        bf16x8 xr[XPC], br[WPC];
-        float gr[WPC], dr[WPC], glast;
-    };
-    // per-thread element offsets of the staged pieces inside one chunk (32-bit:
-    // below Q * stride), plus a uniform 64-bit chunk base
-    int xo[XPC], bo[WPC], to[WPC];
+    // staging assignments: x piece r of this thread is token (tid + NTHR r) / 8,
+    // p octet (tid + NTHR r) % 8; the B block is token group wtg, column group wcg
+    int xo[XPC];
 #pragma unroll
     for (int r = 0; r < XPC; ++r) {
         const int id = tid + NTHR * r;
         xo[r] = (id >> 3) * (int)xstride + (id & 7) * 8;
     }
-#pragma unroll
-    for (int r = 0; r < WPC; ++r) {
-        const int id = tid + NTHR * r;
-        to[r] = id / (NT / 8);
-        bo[r] = to[r] * (int)bstride + (id % (NT / 8)) * 8;
-    }
+    const int wtg = tid / (NT / WC), wcg = tid % (NT / WC);
+    const int bo = wtg * 8 * (int)bstride + wcg * WC;
+
+    struct Stage {
+        bf16x8 xr[XPC];
+        uint32_t br[8][WD];
+        f32x4 w[2];
+        float glast;
+    };
     auto issue = [&](Stage &st, int c) {
         const int t0 = c * Q;
         const bf16 *xc = xb + (int64_t)t0 * xstride;
-        const bf16 *bc = Bb + (int64_t)t0 * bstride;
-        if (t0 + Q <= L) {
+        const bf16 *bc = Bb + (int64_t)t0 * bstride + bo;
+        const bool full = t0 + Q <= L;
 #pragma unroll
-            for (int r = 0; r < XPC; ++r) st.xr[r] = ld16(xc + xo[r]);
+        for (int r = 0; r < XPC; ++r) {
+            const int t = (tid + NTHR * r) >> 3;
+            st.xr[r] = (full || t0 + t < L) ? ld16(xc + xo[r]) : zero8();
+        }
 #pragma unroll
-            for (int r = 0; r < WPC; ++r) st.br[r] = ld16(bc + bo[r]);
-        } else {
+        for (int r = 0; r < 8; ++r) {
+            const bf16 *src = bc + r * (int)bstride;
+            if (full || t0 + wtg * 8 + r < L) {
+                if constexpr (WC == 8) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+                    st.br[r][0] = v[0]; st.br[r][1] = v[1]; st.br[r][2] = v[2]; st.br[r][3] = v[3];
+                } else if constexpr (WC == 4) {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+                    st.br[r][0] = v[0]; st.br[r][1] = v[1];
+                } else if constexpr (WC == 2) {
+                    st.br[r][0] = *reinterpret_cast<const uint32_t *>(src);
+                } else {
+                    st.br[r][0] = *reinterpret_cast<const uint16_t *>(src);
+                }
+            } else {
 #pragma unroll
-            for (int r = 0; r < XPC; ++r) {
-                const int t = (tid + NTHR * r) >> 3;
-                st.xr[r] = (t0 + t < L) ? ld16(xc + xo[r]) : zero8();
+                for (int k = 0; k < WD; ++k) st.br[r][k] = 0u;
             }
-#pragma unroll
-            for (int r = 0; r < WPC; ++r) st.br[r] = (t0 + to[r] < L) ? ld16(bc + bo[r]) : zero8();
         }
-#pragma unroll
-        for (int r = 0; r < WPC; ++r) {
-            st.gr[r] = Gh[t0 + to[r]];
-            st.dr[r] = dh[t0 + to[r]];
-        }
+        const f32x4 *wp = reinterpret_cast<const f32x4 *>(wh + t0 + wtg * 8);
+        st.w[0] = wp[0];
+        st.w[1] = wp[1];
         st.glast = Gh[t0 + Q - 1];
     };
     auto commit = [&](const Stage &st, int buf) {
 #pragma unroll
         for (int r = 0; r < XPC; ++r) {
-            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-            *reinterpret_cast<bf16x8 *>(&Xs[buf][t * XP + oct * 8]) = st.xr[r];
+            const int id = tid + NTHR * r;
+            *reinterpret_cast<bf16x8 *>(&Xs[buf][(id >> 3) * XP + (id & 7) * 8]) = st.xr[r];
         }
+        // W: scale token row r by w_r, then pack the pair (2k, 2k+1) of column j
 #pragma unroll
-        for (int r = 0; r < WPC; ++r) {
-            const int id = tid + NTHR * r, t = id / (NT / 8), oct = id % (NT / 8);
-            const float w = st.dr[r] * fast_exp2(st.glast - st.gr[r]);
-            bf16x8 o;
+        for (int j = 0; j < WC; ++j) {
+            u32x4 o;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)st.br[r][e] * w);
-            *reinterpret_cast<bf16x8 *>(&Ws[buf][t * WP + oct * 8]) = o;
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t a = st.br[2 * k][j >> 1], bb = st.br[2 * k + 1][j >> 1];
+                const float fa = (j & 1) ? bf_hi(a) : bf_lo(a);
+                const float fb = (j & 1) ? bf_hi(bb) : bf_lo(bb);
+                const float wa = st.w[k >> 1][2 * (k & 1)], wb = st.w[k >> 1][2 * (k & 1) + 1];
+                o[k] = pack_bf16(fa * wa, fb * wb);
+            }
+            *reinterpret_cast<u32x4 *>(&WT[buf][(wcg * WC + j) * PT + wtg * 8]) = o;
         }
         if (tid == 0) alph[buf] = fast_exp2(st.glast);
     };
 
-    const int offW = tr_off_natural(lane, WP) + nh * 32;
-    const int offX = tr_off_natural(lane, XP) + ph * 32;
+    const int offW = (nh * 32 + (lane & 31)) * PT + 8 * (lane >> 5) + kh * (Q / KS);
+    const int offX = tr_off_natural(lane, XP) + ph * 32 + kh * (Q / KS) * XP;
 
     // One chunk: refill `refill` with chunk c+2, consume LDS buffer `cur` (chunk
     // c), then move chunk c+1 from `next` into the other buffer.  Loads and
@@ -198,13 +222,12 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] *= a;
 
-        const bf16 *wt = Ws[cur] + offW + kh * (Q / KS) * WP;
-        const bf16 *xt = Xs[cur] + offX + kh * (Q / KS) * XP;
+        const bf16 *wt = WT[cur] + offW;
+        const bf16 *xt = Xs[cur] + offX;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 af = cat8(tr_read4(wt + ks * 16 * WP), tr_read4(wt + (ks * 16 + 4) * WP));
             const bf16x8 bf = cat8(tr_read4(xt + ks * 16 * XP), tr_read4(xt + (ks * 16 + 4) * XP));
-            mma(acc, af, bf);
+            mma(acc, ld16(wt + ks * 16), bf);
         }
         commit(next, cur ^ 1);
         __syncthreads();
@@ -262,8 +285,8 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
 // with e the last token of tile J; both factors are <= 1, the second is a
 // per-token table, so such a tile costs one exp2 per lane instead of sixteen.
 // Phase 3, per row tile: scale Y^T column i by exp2(G_i), add M(J, I) (dt x)_J
-// for J <= I with M read back as the B operand and (dt x)^T transpose-read
-// from LDS in the accumulator's token order, then add D x and store.
+// for J <= I with M read back as the B operand and (dt x)^T read from LDS as
+// 16-byte fragments in the accumulator's token order, then add D x and store.
 // ===========================================================================
 template <int Q>
 __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
@@ -273,10 +296,14 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     int xcd)
 {
     constexpr int P = 64, NI = Q / 32, NTHR = Q, NW = Q / 64, NSLOT = NI + 1, NS = 64;
-    constexpr int XP = tr_pitch(P), BP = frag_pitch(NS), SP = frag_pitch(NS);
+    constexpr int XP = Q + 8, BP = frag_pitch(NS), SP = frag_pitch(NS);
     constexpr int BS_EL = Q * BP, SS_EL = P * SP, MB_EL = NW * NSLOT * 2 * 64 * 8;
     constexpr int U_EL = (BS_EL + SS_EL > MB_EL) ? BS_EL + SS_EL : MB_EL;
-    __shared__ __attribute__((aligned(16))) bf16 Xd[Q * XP];
+    // (dt x)^T [p][position]: within each 16-token group the token at offset o is
+    // kept at position o ^ ((o >> 2 & 1) ^ (o >> 3 & 1)) * 12, i.e. the middle two
+    // 4-token blocks are swapped, so the accumulator token order 4(l/32)+{0..3},
+    // 8+4(l/32)+{0..3} of lane l becomes 8 consecutive positions.
+    __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
     __shared__ __attribute__((aligned(16))) bf16 U[U_EL];
     __shared__ __attribute__((aligned(16))) float Gs[Q];
     __shared__ __attribute__((aligned(16))) float We[Q];   // exp2(G_e - G_j), e = end of j's tile
@@ -326,28 +353,43 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
         }
     };
 
-    // (dt x) tile, token-major, and the chunk's decays; the first N slice is
-    // requested right behind the x tile so both latencies overlap
+    // (dt x)^T tile and the chunk's decays; the first N slice is requested right
+    // behind the x tile so both latencies overlap.  Thread = one 8-token x 8-p
+    // block: rows loaded token-major, scaled by dt, packed per p column.  A wave
+    // covers 8 token groups (lane % 8) x 8 column groups (lane / 8): whole token
+    // rows per load, distinct banks per 16-lane group of LDS writes.
     {
-        bf16x8 xv[8];
+        const int tg = w * 8 + (lane & 7), cg = lane >> 3;
+        u32x4 xv[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-            xv[r] = (full || t0 + t < L) ? ld16(xb + t * (int)xstride + oct * 8) : zero8();
-        }
+        for (int r = 0; r < 8; ++r)
+            xv[r] = (full || t0 + tg * 8 + r < L)
+                        ? *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dh + tg * 8);
+        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dh + tg * 8 + 4);
         const float gt = Gh[tid];
         const float ge = Gh[tid | 31];
-        float d[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) d[r] = dh[(tid + NTHR * r) >> 3];
         load_slice(0);
+        const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        // positions of this block's tokens: 8 tokens at offset 0 or 8 of a 16-group
+        // -> two runs of 4 positions, 8 apart
+        const int pos0 = (tg >> 1) * 16 + ((tg & 1) ? 4 : 0);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-            bf16x8 o;
+        for (int j = 0; j < 8; ++j) {
+            u32x2 lo, hi;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)xv[r][e] * d[r]);
-            *reinterpret_cast<bf16x8 *>(&Xd[t * XP + oct * 8]) = o;
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t a0 = xv[2 * k][j >> 1], a1 = xv[2 * k + 1][j >> 1];
+                lo[k] = pack_bf16(((j & 1) ? bf_hi(a0) : bf_lo(a0)) * d[2 * k],
+                                  ((j & 1) ? bf_hi(a1) : bf_lo(a1)) * d[2 * k + 1]);
+                const uint32_t b0 = xv[4 + 2 * k][j >> 1], b1 = xv[5 + 2 * k][j >> 1];
+                hi[k] = pack_bf16(((j & 1) ? bf_hi(b0) : bf_lo(b0)) * d[4 + 2 * k],
+                                  ((j & 1) ? bf_hi(b1) : bf_lo(b1)) * d[5 + 2 * k]);
+            }
+            bf16 *row = Xd + (cg * 8 + j) * XP + pos0;
+            *reinterpret_cast<u32x2 *>(row) = lo;
+            *reinterpret_cast<u32x2 *>(row + 8) = hi;
         }
         Gs[tid] = gt;
         We[tid] = fast_exp2(ge - gt);
@@ -446,7 +488,7 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     // each lane reads back only what it wrote: no barrier needed
 
     // ---------------- phase 3: Y^T += M (dt x), then D x and store ----------------
-    const int offX = tr_off_accorder(lane, XP);
+    const int offX = (lane & 31) * XP + 8 * (lane >> 5);
     const float Dh = D[h];
 #pragma unroll
     for (int side = 0; side < 2; ++side) {
@@ -461,12 +503,9 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
                 const bf16x8 mf = *reinterpret_cast<const bf16x8 *>(mrow + sub * 64 * 8);
-                const bf16 *xt = Xd + offX + (J * 32 + 16 * sub) * XP;
+                const bf16 *xt = Xd + offX + J * 32 + 16 * sub;
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    const bf16x8 af = cat8(tr_read4(xt + pp * 32), tr_read4(xt + pp * 32 + 8 * XP));
-                    mma(ya[side][pp], af, mf);
-                }
+                for (int pp = 0; pp < 2; ++pp) mma(ya[side][pp], ld16(xt + pp * 32 * XP), mf);
             }
         }
         if (full || t0 + i_loc < L) {
@@ -493,26 +532,26 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
 // ===========================================================================
 template <int Q, int NT, int KS>
 static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
-                            const float *dtT, const float *h0, void *S, float *hT, hipStream_t st)
+                            const float *wT, const float *h0, void *S, float *hT, hipStream_t st)
 {
     const int ntiles = (int)(s.N / NT);
     const int bH = (int)(s.b * s.H);
     const int xcd = (bH % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NT, KS>), dim3((unsigned)(bH * ntiles)),
                        dim3(64 * 2 * (NT / 32) * KS), 0, st, (const bf16 *)x, (const bf16 *)B, G2,
-                       dtT, h0, (bf16 *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
+                       wT, h0, (bf16 *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
                        (int)s.Lp, ntiles, xcd);
     return hipGetLastError();
 }
 
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
-                                  const float *dtT, const float *h0, void *S, float *hT,
+                                  const float *wT, const float *h0, void *S, float *hT,
                                   hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return sp_launch<64, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
-    case 128: return sp_launch<128, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
-    default: return sp_launch<256, 32, 2>(s, x, B, G2, dtT, h0, S, hT, st);
+    case 64: return sp_launch<64, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
+    case 128: return sp_launch<128, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
+    default: return sp_launch<256, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
     }
 }
 

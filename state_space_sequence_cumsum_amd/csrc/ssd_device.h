@@ -13,6 +13,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -150,6 +153,27 @@ constexpr int frag_pitch(int cols)
 {
     int b = (cols * 2 + 127) / 128 * 128 + 16;
     return b / 2;
+}
+
+// ---------------------------------------------------------------------------
+// Register transposes for staging token-major global tiles into k-packed LDS
+// rows (8 consecutive tokens of one column = one 16-byte MFMA fragment).
+// ---------------------------------------------------------------------------
+// Halves h of two dwords packed as (lo = a.h, hi = b.h).
+__device__ __forceinline__ uint32_t pack_halves(uint32_t a, uint32_t b, int h)
+{
+    return __builtin_amdgcn_perm(b, a, h ? 0x07060302u : 0x05040100u);
+}
+
+// bf16 <-> fp32 on raw bits (bf16 is the upper half of an fp32)
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    bf16x2_t r;
+    r[0] = (bf16)lo;
+    r[1] = (bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 }  // namespace ssd

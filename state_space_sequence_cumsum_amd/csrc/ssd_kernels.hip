@@ -20,13 +20,16 @@ namespace ssd {
 // scans its head's Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane
 // shuffle scan adds the lane prefixes, and the results are written
 // token-contiguous.  Padded tokens (last chunk) get dt = 0 and repeat the last
-// valid cumsum value exactly.
+// valid cumsum value exactly.  The same pass emits each token's state-pass
+// weight w_t = dt_t exp2(G_last - G_t) (its decay to the end of its chunk), so
+// the serial state pass reads it instead of recomputing it per state tile.
 // ===========================================================================
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__ dt,
                                                            const float *__restrict__ A,
                                                            float *__restrict__ G2,
-                                                           float *__restrict__ dtT, int L, int H,
+                                                           float *__restrict__ dtT,
+                                                           float *__restrict__ wT, int L, int H,
                                                            int Lp)
 {
     constexpr int HB = 4, PER = Q / 64;
@@ -67,12 +70,18 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
     for (int j = 0; j < PER; ++j)
         if (j == last % PER) tail = (excl + part[j]) * kLog2e;
     tail = __shfl(tail, last / PER, 64);
+    // value at the chunk's last position (the last valid token's on a ragged chunk)
+    float glast = __shfl((excl + part[PER - 1]) * kLog2e, 63, 64);
+    if (last < Q - 1) glast = tail;
     const int64_t base = ((int64_t)b * H + hb + hh) * Lp + t0 + lane * PER;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int t = lane * PER + j;
-        G2[base + j] = (t <= last) ? (excl + part[j]) * kLog2e : tail;
-        dtT[base + j] = tile[t][hh];
+        const float gt = (t <= last) ? (excl + part[j]) * kLog2e : tail;
+        const float d = tile[t][hh];
+        G2[base + j] = gt;
+        dtT[base + j] = d;
+        wT[base + j] = d * fast_exp2(glast - gt);
     }
 }
 
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const T *__restrict__ x, const T *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ dtT, const float *__restrict__ h0, T *__restrict__ S,
+    const float *__restrict__ wT, const float *__restrict__ h0, T *__restrict__ S,
     float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp)
 {
     constexpr int P = 64, NT = 64;
@@ -109,14 +118,14 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     }
 
     const float *Gh = G2 + (int64_t)bh * Lp;
-    const float *dh = dtT + (int64_t)bh * Lp;
+    const float *wh = wT + (int64_t)bh * Lp;
     const int64_t xrow = (int64_t)H * P;   // x token stride
     const int64_t brow = (int64_t)G * N;   // B token stride
 
     for (int c = 0; c < nc; ++c) {
         const int t0 = c * Q;
         const float glast = Gh[t0 + Q - 1];
-        for (int t = tid; t < Q; t += 256) wsh[t] = dh[t0 + t] * fast_exp2(glast - Gh[t0 + t]);
+        for (int t = tid; t < Q; t += 256) wsh[t] = wh[t0 + t];
         __syncthreads();
 
         // X_c [Q x 64] -> XT[p][t]
@@ -298,60 +307,61 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
 // ===========================================================================
 template <typename T, int Q>
 static hipError_t cumsum_tq(const Shape &s, const void *dt, const float *A, float *G2, float *dtT,
-                            hipStream_t st)
+                            float *wT, hipStream_t st)
 {
     dim3 grid((unsigned)s.nc, (unsigned)((s.H + 3) / 4), (unsigned)s.b);
     hipLaunchKernelGGL((chunk_cumsum_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)dt, A, G2,
-                       dtT, (int)s.L, (int)s.H, (int)s.Lp);
+                       dtT, wT, (int)s.L, (int)s.H, (int)s.Lp);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t cumsum_t(const Shape &s, const void *dt, const float *A, float *G2, float *dtT,
-                           hipStream_t st)
+                           float *wT, hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return cumsum_tq<T, 64>(s, dt, A, G2, dtT, st);
-    case 128: return cumsum_tq<T, 128>(s, dt, A, G2, dtT, st);
-    default: return cumsum_tq<T, 256>(s, dt, A, G2, dtT, st);
+    case 64: return cumsum_tq<T, 64>(s, dt, A, G2, dtT, wT, st);
+    case 128: return cumsum_tq<T, 128>(s, dt, A, G2, dtT, wT, st);
+    default: return cumsum_tq<T, 256>(s, dt, A, G2, dtT, wT, st);
     }
 }
 
 hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, float *G2,
-                               float *dtT, hipStream_t st)
+                               float *dtT, float *wT, hipStream_t st)
 {
-    return s.bf16 ? cumsum_t<bf16>(s, dt, A, G2, dtT, st) : cumsum_t<float>(s, dt, A, G2, dtT, st);
+    return s.bf16 ? cumsum_t<bf16>(s, dt, A, G2, dtT, wT, st)
+                  : cumsum_t<float>(s, dt, A, G2, dtT, wT, st);
 }
 
 template <typename T, int Q>
 static hipError_t state_pass_tq(const Shape &s, const void *x, const void *B, const float *G2,
-                                const float *dtT, const float *h0, void *S, float *hT,
+                                const float *wT, const float *h0, void *S, float *hT,
                                 hipStream_t st)
 {
     dim3 grid((unsigned)(s.N / 64), (unsigned)(s.b * s.H));
     hipLaunchKernelGGL((state_pass_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)x, (const T *)B,
-                       G2, dtT, h0, (T *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
+                       G2, wT, h0, (T *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
                        (int)s.Lp);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t state_pass_t(const Shape &s, const void *x, const void *B, const float *G2,
-                               const float *dtT, const float *h0, void *S, float *hT, hipStream_t st)
+                               const float *wT, const float *h0, void *S, float *hT, hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return state_pass_tq<T, 64>(s, x, B, G2, dtT, h0, S, hT, st);
-    case 128: return state_pass_tq<T, 128>(s, x, B, G2, dtT, h0, S, hT, st);
-    default: return state_pass_tq<T, 256>(s, x, B, G2, dtT, h0, S, hT, st);
+    case 64: return state_pass_tq<T, 64>(s, x, B, G2, wT, h0, S, hT, st);
+    case 128: return state_pass_tq<T, 128>(s, x, B, G2, wT, h0, S, hT, st);
+    default: return state_pass_tq<T, 256>(s, x, B, G2, wT, h0, S, hT, st);
     }
 }
 
 hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const float *G2,
-                             const float *dtT, const float *h0, void *S, float *hT,
+                             const float *wT, const float *h0, void *S, float *hT,
                              hipStream_t st)
 {
-    return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, dtT, h0, S, hT, st)
-                  : state_pass_t<float>(s, x, B, G2, dtT, h0, S, hT, st);
+    return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, wT, h0, S, hT, st)
+                  : state_pass_t<float>(s, x, B, G2, wT, h0, S, hT, st);
 }
 
 template <typename T, int Q>

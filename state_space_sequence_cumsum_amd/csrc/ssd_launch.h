@@ -13,10 +13,10 @@ struct Shape {
 };
 
 hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, float *G2,
-                               float *dtT, hipStream_t st);
+                               float *dtT, float *wT, hipStream_t st);
 
 hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const float *G2,
-                             const float *dtT, const float *h0, void *S, float *hT,
+                             const float *wT, const float *h0, void *S, float *hT,
                              hipStream_t st);
 
 hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const void *C,
@@ -25,7 +25,7 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
 
 // bf16 kernels (ssd_bf16.hip)
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
-                                  const float *dtT, const float *h0, void *S, float *hT,
+                                  const float *wT, const float *h0, void *S, float *hT,
                                   hipStream_t st);
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,

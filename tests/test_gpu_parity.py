@@ -40,15 +40,8 @@ def _gpu_forward(inp, w, dev, poison=True):
 
 
 def _workspace_views(ws, prob, w):
-    g2_off, dtt_off, s_off = ssd.ssd_workspace_layout(prob)
-    b, H, nc, Q, P, N = w.batch, w.nheads, w.nchunks, w.chunk, w.headdim, w.dstate
-    cnt = b * H * nc * Q
-    G2 = ws[g2_off:g2_off + 4 * cnt].view(torch.float32).view(b, H, nc * Q)
-    dtT = ws[dtt_off:dtt_off + 4 * cnt].view(torch.float32).view(b, H, nc * Q)
-    es = 2 if w.dtype == "bf16" else 4
-    S = ws[s_off:s_off + es * b * H * nc * P * N]
-    S = S.view(torch.bfloat16 if es == 2 else torch.float32).view(b, H, nc, P, N)
-    return G2, dtT, S
+    v = ssd.workspace_views(prob, ws)
+    return v["G2"], v["dtT"], v["S"]
 
 
 def _check_forward(w, seed=0, inp=None, dev=None):
@@ -76,19 +69,27 @@ def test_chunk_cumsum_parity(dtype, L, H, Q):
     w = _wl(dtype=dtype, b=2, L=L, H=H, Q=Q)
     inp = make_inputs(w, 3)
     prob = ssd.problem_of(inp["x"], inp["B"], Q)
-    G2, dtT = ssd.ssd_chunk_cumsum(prob, inp["dt"].to(dev), inp["A"].to(dev))
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, inp["dt"].to(dev), inp["A"].to(dev))
     torch.cuda.synchronize()
     G2_ref, dt_ref = oracle.chunk_cumsum(inp["dt"], inp["A"], Q)
-    G2g, dtg = f64(G2), f64(dtT)
+    G2g, dtg, wg = f64(G2), f64(dtT), f64(wT)
     # valid tokens: G2 within the fp32 summation bound, dtT exactly fp32(dt)
     bound = (Q + 2) * 2.0 ** -24 * max(1.0, np.abs(G2_ref).max())
     err = np.abs(G2g[:, :, :L] - G2_ref).max()
     print(f"  G2 max|err| = {err:.3e} (bound {bound:.3e})")
     assert err <= bound
     np.testing.assert_array_equal(dtg[:, :, :L], dt_ref)
-    # padded tail: dt = 0 and the cumsum frozen at the last valid token
+    # state-pass weights: dt times the decay from t to the chunk's last valid token,
+    # in fp64 from the oracle's cumsum; the fp32 exponent error above scales it by
+    # at most 2^(bound) on top of fp32 rounding
+    last = np.minimum((np.arange(L) // Q) * Q + Q - 1, L - 1)
+    w_ref = dt_ref * np.exp2(G2_ref[:, :, last] - G2_ref)
+    werr = np.abs(wg[:, :, :L] - w_ref).max() / np.abs(w_ref).max()
+    print(f"  wT max rel err = {werr:.3e}")
+    assert werr <= 2 * bound * np.log(2) + 1e-6
+    # padded tail: dt = w = 0 and the cumsum frozen at the last valid token
     if G2g.shape[2] > L:
-        assert (dtg[:, :, L:] == 0).all()
+        assert (dtg[:, :, L:] == 0).all() and (wg[:, :, L:] == 0).all()
         np.testing.assert_array_equal(G2g[:, :, L:], np.repeat(G2g[:, :, L - 1:L], G2g.shape[2] - L, 2))
 
 
@@ -199,8 +200,8 @@ def test_stages_compose_to_forward():
     inp = make_inputs(w, 10)
     d = to_dev(inp, dev)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
-    G2, dtT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
-    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"])
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"])
     y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
     yf, hTf, _, _ = _gpu_forward(inp, w, dev)
     assert torch.equal(y, yf) and torch.equal(hT, hTf)
