@@ -4,8 +4,9 @@
 One step = one whole forward (chunk cumsum, state pass, chunk output) over the
 16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints one
 JSON line:  tokens/s of ``ssd_forward``; per-stage durations from HIP events
-recorded on the launch stream; the roofline of the dominant kernel from its
-algorithmic bytes and flops; and the fp64 CPU oracle timed on this host.
+that the library records on the launch stream between its stages during the
+timed steps; the roofline of the dominant stage from its algorithmic bytes and
+flops; and the fp64 CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -103,39 +104,30 @@ def main():
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev, dtype=torch.float32)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
     ws = ssd.workspace_for(prob, dev)
-    views = ssd.workspace_views(prob, ws)
-    G2, dtT, wT, S = views["G2"], views["dtT"], views["wT"], views["S"]
     stream = torch.cuda.current_stream(dev)
+    names = ["chunk_cumsum", "state_pass", "chunk_out"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:          # create the HIP events before they are handed to the library
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
 
-    def forward():
+    def forward(events=None):
         ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
-                        y=y, hT=hT, workspace=ws, stream=stream)
+                        y=y, hT=hT, workspace=ws, stream=stream, events=events)
 
     for _ in range(args.warmup):
         forward()
     torch.cuda.synchronize()
 
-    # --- timed region: K whole forwards through the C ABI ---
+    # --- timed region: K whole forwards through the C ABI (ssd_forward_timed), with HIP
+    # events recorded on the launch stream between the three stages ---
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        forward()
+    for k in range(args.steps):
+        forward(evs[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # --- the same K steps, stage by stage, HIP events on the launch stream ---
-    names = ["chunk_cumsum", "state_pass", "chunk_out"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        e = evs[k]
-        e[0].record(stream)
-        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, wT, stream=stream)
-        e[1].record(stream)
-        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"], S, hT, stream=stream)
-        e[2].record(stream)
-        ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"], y, stream=stream)
-        e[3].record(stream)
-    torch.cuda.synchronize()
     per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)]
            for i, n in enumerate(names)}   # microseconds
     kern = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),

@@ -73,8 +73,8 @@ typedef struct {
 /* Host-only checks of `problem` (dimensions, divisibility, supported set).  No GPU. */
 ssd_status ssd_validate(const ssd_problem *problem);
 
-/* Bytes of device workspace ssd_forward needs (G2, dtT, wT and S, each 256-byte aligned);
- * 0 if `problem` is not valid.  Host-only. */
+/* Bytes of device workspace ssd_forward needs (G2, dtT, wT, S and the state pass's group
+ * state, each 256-byte aligned); 0 if `problem` is not valid.  Host-only. */
 size_t ssd_workspace_bytes(const ssd_problem *problem);
 
 /* Stage 1 (section "Kernel 1：计算累积和"): for each (b, h) and token t of chunk c,
@@ -109,13 +109,27 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
                          const float *D, void *y, void *stream);
 
 /* The whole forward pass: stage 1, 2 and 3 on `stream`, no host synchronisation.
- * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds G2, dtT, wT and S;
- * its contents on return are those intermediates.  h0 may be NULL; hT may be NULL
- * (final state not wanted).  Writes y and hT. */
+ * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds the intermediates.
+ * On return G2, dtT and wT hold the stage-1 outputs.  For bf16 problems the state pass
+ * may split each (batch, head) chain of chunks into groups that run in parallel from a
+ * zero state (the jump is linear), combine the group-final states with a short scan and
+ * let stage 3 add the carried-in state; S then holds chunk-start states relative to
+ * their group, and its contents are otherwise unspecified.  h0 may be NULL; hT may be
+ * NULL (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
                        const float *A, const void *B, const void *C, const float *D,
                        const float *h0, void *y, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* ssd_forward with stage timing marks, for profiling the forward pass as it runs.
+ * `events` holds 4 hipEvent_t handles created by the caller; they are recorded on
+ * `stream` before stage 1, after stage 1, after stage 2 (including the group scan
+ * when the state pass is split) and after stage 3.  events == NULL behaves exactly
+ * like ssd_forward. */
+ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *h0, void *y, float *hT, void *workspace,
+                             size_t workspace_bytes, void *stream, void *const *events);
 
 /* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,

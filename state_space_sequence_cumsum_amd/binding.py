@@ -64,6 +64,8 @@ def lib():
         L.ssd_chunk_out.argtypes, L.ssd_chunk_out.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ssd_forward.restype = st
+        L.ssd_forward_timed.argtypes = L.ssd_forward.argtypes + [ctypes.POINTER(vp)]
+        L.ssd_forward_timed.restype = st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
         L.ssd_last_hip_error.argtypes, L.ssd_last_hip_error.restype = [], ctypes.c_int
         _lib = L
@@ -226,8 +228,12 @@ def workspace_for(problem: SsdProblem, device) -> torch.Tensor:
 
 
 def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want_final=True,
-                workspace=None, stream=None):
-    """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None)."""
+                workspace=None, stream=None, events=None):
+    """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None).
+
+    ``events``: optional 4 recorded-once ``torch.cuda.Event`` objects; they are
+    re-recorded on the launch stream around the three stages (ssd_forward_timed).
+    """
     problem = problem_of(x, B, chunk)
     b, L, H, G, P, N, Q, nc = _dims(problem)
     io = _io_dtype(problem)
@@ -250,11 +256,16 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
     if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     nbytes = workspace.numel() * workspace.element_size()
-    _raise(lib().ssd_forward(ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                             _ptr(D), _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace), nbytes,
-                             _stream(stream, dev)), "ssd_forward")
+    args = (ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace), nbytes, _stream(stream, dev))
+    if events is None:
+        _raise(lib().ssd_forward(*args), "ssd_forward")
+    else:
+        if len(events) != 4 or not all(getattr(e, "cuda_event", 0) for e in events):
+            raise ValueError("events must be 4 torch.cuda.Event objects recorded at least once")
+        arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
     return y, hT
-
 
 def workspace_views(problem: SsdProblem, workspace: torch.Tensor) -> dict:
     """Typed views (G2, dtT, wT, S) of an ssd_forward workspace tensor."""

@@ -47,19 +47,29 @@ ssd::Shape make_shape(const ssd_problem *p)
 }
 
 struct Layout {
-    size_t g2, dtt, wt, S, total;
+    size_t g2, dtt, wt, S, ug, gam, beta, total;
+    ssd::Grouping gp;
 };
 
+// Workspace of ssd_forward: the stage-1 outputs, the chunk-start states and,
+// when the state pass is split into groups, the group states, group decays and
+// per-chunk decays since the group start.
 Layout layout_of(const ssd::Shape &s)
 {
-    const size_t cum = size_t(s.b) * s.H * s.Lp * sizeof(float);
-    const size_t snap = size_t(s.b) * s.H * s.nc * s.P * s.N * (s.bf16 ? 2 : 4);
+    const size_t bh = size_t(s.b) * s.H;
+    const size_t cum = bh * s.Lp * sizeof(float);
+    const size_t snap = bh * s.nc * s.P * s.N * (s.bf16 ? 2 : 4);
     Layout l;
+    l.gp = ssd::state_pass_groups(s);
+    const bool grouped = l.gp.ng > 1;
     l.g2 = 0;
     l.dtt = align_up(cum);
     l.wt = l.dtt + align_up(cum);
     l.S = l.wt + align_up(cum);
-    l.total = l.S + align_up(snap);
+    l.ug = l.S + align_up(snap);
+    l.gam = l.ug + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * sizeof(float)) : 0);
+    l.beta = l.gam + (grouped ? align_up(bh * l.gp.ng * sizeof(float)) : 0);
+    l.total = l.beta + (grouped ? align_up(bh * s.nc * sizeof(float)) : 0);
     return l;
 }
 
@@ -128,13 +138,16 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
                                             (hipStream_t)stream));
 }
 
-ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt, const float *A,
-                       const void *B, const void *C, const float *D, const float *h0, void *y,
-                       float *hT, void *workspace, size_t workspace_bytes, void *stream)
+ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *h0, void *y, float *hT, void *workspace,
+                             size_t workspace_bytes, void *stream, void *const *events)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
+    if (events != nullptr && (!events[0] || !events[1] || !events[2] || !events[3]))
+        return SSD_ERR_NULL_ARG;
     const ssd::Shape s = make_shape(problem);
     const Layout l = layout_of(s);
     if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
@@ -143,13 +156,34 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
     float *dtT = reinterpret_cast<float *>(ws + l.dtt);
     float *wT = reinterpret_cast<float *>(ws + l.wt);
     void *S = ws + l.S;
+    float *Ug = reinterpret_cast<float *>(ws + l.ug);
+    float *gam = reinterpret_cast<float *>(ws + l.gam);
+    float *beta = reinterpret_cast<float *>(ws + l.beta);
     hipStream_t hs = (hipStream_t)stream;
+    auto mark = [&](int i) -> ssd_status {
+        return events ? hip_status(hipEventRecord((hipEvent_t)events[i], hs)) : SSD_OK;
+    };
 
-    ssd_status r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
-    if (r != SSD_OK) return r;
-    r = hip_status(ssd::launch_state_pass(s, x, B, G2, wT, h0, S, hT, hs));
-    if (r != SSD_OK) return r;
-    return hip_status(ssd::launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, hs));
+    ssd_status r = mark(0);
+    if (r == SSD_OK) r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
+    if (r == SSD_OK) r = mark(1);
+    if (r == SSD_OK)
+        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam,
+                                                      beta, hs));
+    if (r == SSD_OK) r = mark(2);
+    if (r == SSD_OK)
+        r = hip_status(
+            ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, beta, hs));
+    if (r == SSD_OK) r = mark(3);
+    return r;
+}
+
+ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *h0, void *y,
+                       float *hT, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return ssd_forward_timed(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
+                             stream, nullptr);
 }
 
 const char *ssd_status_string(ssd_status status)

@@ -10,6 +10,8 @@
 // with 16-byte writes and the token-packed MFMA operands are read back with
 // the gfx950 LDS transpose read (ds_read_b64_tr_b16), so no element-wise
 // transposition happens on the way in.
+#include <algorithm>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -40,32 +42,42 @@ __device__ __forceinline__ void xcd_split(int id, int n_minor, bool xcd, int &ma
 }
 
 // ===========================================================================
-// State pass.  Workgroup = one (batch*head, N tile of NT columns).  It keeps
-// h^T [NT x 64] in fp32 accumulators: wave (ph, nh, kh) owns rows
-// n in [32 nh, 32 nh + 32) and columns p in [32 ph, 32 ph + 32) for the tokens
-// of K-half kh (KS = 2 splits each chunk's tokens over two wave sets whose
-// partial states are summed through LDS at every chunk boundary).
+// State pass.  Workgroup = one (batch*head, N tile of NT columns, group of up
+// to K consecutive chunks).  It keeps h^T [NT x 64] in fp32 accumulators: wave
+// (ph, nh, kh) owns rows n in [32 nh, 32 nh + 32) and columns p in
+// [32 ph, 32 ph + 32) for the tokens of K-half kh (KS = 2 splits each chunk's
+// tokens over two wave sets whose partial states are summed through LDS at
+// every chunk boundary).
+//
+// Groups.  The chunk jump h <- a_c h + U_c is linear, so a run of chunks can
+// start from a zero state and be corrected afterwards: group g (chunks
+// [gK, gK+K)) starts from h0 if g == 0 and from 0 otherwise, stores its local
+// chunk-start states, its final local state U_g, the decay products
+// beta_c = prod_{gK <= c' < c} a_c' and gamma_g = prod_{c' in g} a_c'.  A scan
+// over groups (group_scan_kernel) then gives the true state at each group
+// start, H_g, and the true chunk-start state is S_local[c] + beta_c H_g.  With
+// one group (K >= nc) the kernel is the plain serial state pass and writes
+// true states and hT directly.
 //
 // Operands, both k-packed by token:
-//   * X (B operand): the x tile is copied into LDS as is, token-major
-//     [t][p], with 16-byte writes of whole token rows, and read back with the
-//     LDS transpose read;
+//   * X (B operand): the x tile is copied into LDS as is, token-major [t][p],
+//     with 16-byte writes of whole token rows, and read back with the LDS
+//     transpose read;
 //   * W (A operand): each thread loads an 8-token x WC-column block of B,
 //     scales token t by its weight w_t (from stage 1) and bf16-packs the pairs
 //     (t, t+1) of each column, which is already the k-packed layout WT[n][t];
 //     read back as one 16-byte fragment per MFMA.
-//
-// Per chunk c, in order:
-//   * issue the global loads of chunk c+2 (x, B, w, G_last) into registers;
-//   * store S[c] = h (bf16, [P][N] so every lane writes 4 consecutive n);
-//   * h <- exp2(G_last) h + W_c^T X_c on MFMA;
-//   * write chunk c+1 (loaded one chunk earlier) into the other LDS buffer.
+// The LDS tile is single-buffered (about 65 KB at Q = 256) so that two
+// workgroups share a CU and overlap each other's loads, barriers and MFMAs;
+// global loads still run two chunks ahead in registers.
 // ===========================================================================
 template <int Q, int NT, int KS>
 __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
     const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
-    float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp, int ntiles, int xcd)
+    float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
+    float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int ntiles, int K,
+    int ng, int xcd)
 {
     constexpr int P = 64;
     constexpr int NWN = NT / 32, NWAVES = 2 * NWN * KS, NTHR = 64 * NWAVES;
@@ -79,15 +91,17 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
     static_assert(WC == 1 || WC == 2 || WC == 4 || WC == 8, "B staging block width");
     static_assert((Q / 8) * (NT / WC) == NTHR, "B staging cover");
 
-    __shared__ __attribute__((aligned(16))) bf16 Xs[2][Q * XP];
-    __shared__ __attribute__((aligned(16))) bf16 WT[2][NT * PT];
+    __shared__ __attribute__((aligned(16))) bf16 Xs[Q * XP];
+    __shared__ __attribute__((aligned(16))) bf16 WT[NT * PT];
     __shared__ float red[KS > 1 ? (NWAVES / 2) * 16 * 64 : 1];
-    __shared__ float alph[2];
+    __shared__ float alph;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ph = wave & 1, nh = (wave >> 1) % NWN, kh = wave / (2 * NWN);
-    int bh, nt;
-    xcd_split(blockIdx.x, ntiles, xcd != 0, bh, nt);
+    int bh, minor;
+    xcd_split(blockIdx.x, ntiles * ng, xcd != 0, bh, minor);
+    const int grp = minor / ntiles, nt = minor % ntiles;
+    const int c0 = grp * K, c1 = min(c0 + K, nc);
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int n_wave = nt * NT + nh * 32;            // first state column of this wave's rows
     const int p_col = ph * 32 + (lane & 31);          // this lane's p
@@ -98,9 +112,10 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
     const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + nt * NT;
+    const bool keeper = nt == 0 && tid == 0;          // writes beta / gamma of this group
 
     f32x16 acc = zero_acc();
-    if (h0 != nullptr && kh == 0) {
+    if (h0 != nullptr && kh == 0 && grp == 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f32x4 v = *reinterpret_cast<const f32x4 *>(h0 + st_off + (int64_t)p_col * N + n_lane + 8 * q);
@@ -126,34 +141,42 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
         f32x4 w[2];
         float glast;
     };
+    auto load_b_row = [&](uint32_t *dst, const bf16 *src) {
+        if constexpr (WC == 8) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+            dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+        } else if constexpr (WC == 4) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
+            dst[0] = v[0]; dst[1] = v[1];
+        } else if constexpr (WC == 2) {
+            dst[0] = *reinterpret_cast<const uint32_t *>(src);
+        } else {
+            dst[0] = *reinterpret_cast<const uint16_t *>(src);
+        }
+    };
     auto issue = [&](Stage &st, int c) {
         const int t0 = c * Q;
         const bf16 *xc = xb + (int64_t)t0 * xstride;
         const bf16 *bc = Bb + (int64_t)t0 * bstride + bo;
-        const bool full = t0 + Q <= L;
+        if (t0 + Q <= L) {   // full chunk (uniform): no per-lane predication
 #pragma unroll
-        for (int r = 0; r < XPC; ++r) {
-            const int t = (tid + NTHR * r) >> 3;
-            st.xr[r] = (full || t0 + t < L) ? ld16(xc + xo[r]) : zero8();
-        }
+            for (int r = 0; r < XPC; ++r) st.xr[r] = ld16(xc + xo[r]);
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const bf16 *src = bc + r * (int)bstride;
-            if (full || t0 + wtg * 8 + r < L) {
-                if constexpr (WC == 8) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-                    st.br[r][0] = v[0]; st.br[r][1] = v[1]; st.br[r][2] = v[2]; st.br[r][3] = v[3];
-                } else if constexpr (WC == 4) {
-                    const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
-                    st.br[r][0] = v[0]; st.br[r][1] = v[1];
-                } else if constexpr (WC == 2) {
-                    st.br[r][0] = *reinterpret_cast<const uint32_t *>(src);
+            for (int r = 0; r < 8; ++r) load_b_row(st.br[r], bc + r * (int)bstride);
+        } else {             // ragged last chunk: rows past L read as zero
+#pragma unroll
+            for (int r = 0; r < XPC; ++r) {
+                const int t = (tid + NTHR * r) >> 3;
+                st.xr[r] = (t0 + t < L) ? ld16(xc + xo[r]) : zero8();
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (t0 + wtg * 8 + r < L) {
+                    load_b_row(st.br[r], bc + r * (int)bstride);
                 } else {
-                    st.br[r][0] = *reinterpret_cast<const uint16_t *>(src);
-                }
-            } else {
 #pragma unroll
-                for (int k = 0; k < WD; ++k) st.br[r][k] = 0u;
+                    for (int k = 0; k < WD; ++k) st.br[r][k] = 0u;
+                }
             }
         }
         const f32x4 *wp = reinterpret_cast<const f32x4 *>(wh + t0 + wtg * 8);
@@ -161,11 +184,11 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
         st.w[1] = wp[1];
         st.glast = Gh[t0 + Q - 1];
     };
-    auto commit = [&](const Stage &st, int buf) {
+    auto commit = [&](const Stage &st) {
 #pragma unroll
         for (int r = 0; r < XPC; ++r) {
             const int id = tid + NTHR * r;
-            *reinterpret_cast<bf16x8 *>(&Xs[buf][(id >> 3) * XP + (id & 7) * 8]) = st.xr[r];
+            *reinterpret_cast<bf16x8 *>(&Xs[(id >> 3) * XP + (id & 7) * 8]) = st.xr[r];
         }
         // W: scale token row r by w_r, then pack the pair (2k, 2k+1) of column j
 #pragma unroll
@@ -179,35 +202,23 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
                 const float wa = st.w[k >> 1][2 * (k & 1)], wb = st.w[k >> 1][2 * (k & 1) + 1];
                 o[k] = pack_bf16(fa * wa, fb * wb);
             }
-            *reinterpret_cast<u32x4 *>(&WT[buf][(wcg * WC + j) * PT + wtg * 8]) = o;
+            *reinterpret_cast<u32x4 *>(&WT[(wcg * WC + j) * PT + wtg * 8]) = o;
         }
-        if (tid == 0) alph[buf] = fast_exp2(st.glast);
+        if (tid == 0) alph = fast_exp2(st.glast);
     };
 
     const int offW = (nh * 32 + (lane & 31)) * PT + 8 * (lane >> 5) + kh * (Q / KS);
     const int offX = tr_off_natural(lane, XP) + ph * 32 + kh * (Q / KS) * XP;
+    float run = 1.0f;   // decay product since the group start (keeper thread)
 
-    // One chunk: refill `refill` with chunk c+2, consume LDS buffer `cur` (chunk
-    // c), then move chunk c+1 from `next` into the other buffer.  Loads and
-    // commits are unconditional (indices clamped to the last chunk; the extra
-    // copies near the end are never read) so the body has no branches and the
-    // compiler's wait counts let the c+2 loads stay in flight across the commit.
-    auto step = [&](int c, int cur, const Stage &next, Stage &refill) {
-        issue(refill, min(c + 2, nc - 1));
-
-        if constexpr (KS > 1) {
-            if (kh == 1) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
-            }
-            __syncthreads();
-            if (kh == 0) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
-            } else {
-                acc = zero_acc();
-            }
-        }
+    // One chunk: refill `refill` with chunk c+2, store the chunk-start state,
+    // decay and accumulate chunk c from LDS, then (after everyone has read the
+    // tile) write chunk c+1 from `next` into LDS and fold the K-halves.  Loads
+    // and commits are unconditional (indices clamped to the group's last chunk;
+    // the extra copies are never used) so the wait counts let the c+2 loads stay
+    // in flight across the commit.
+    auto step = [&](int c, const Stage &next, Stage &refill) {
+        issue(refill, min(c + 2, c1 - 1));
         if (kh == 0) {
             bf16 *Sc = S + ((int64_t)bh * nc + c) * P * N + (int64_t)p_col * N + n_lane;
 #pragma unroll
@@ -218,53 +229,89 @@ __global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kerne
                 *reinterpret_cast<bf16x4 *>(Sc + 8 * q) = o;
             }
         }
-        const float a = alph[cur];
+        const float a = alph;
+        if (keeper && beta != nullptr) {
+            beta[(int64_t)bh * nc + c] = run;
+            run *= a;
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] *= a;
 
-        const bf16 *wt = WT[cur] + offW;
-        const bf16 *xt = Xs[cur] + offX;
+        const bf16 *wt = WT + offW;
+        const bf16 *xt = Xs + offX;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             const bf16x8 bf = cat8(tr_read4(xt + ks * 16 * XP), tr_read4(xt + (ks * 16 + 4) * XP));
             mma(acc, ld16(wt + ks * 16), bf);
         }
-        commit(next, cur ^ 1);
-        __syncthreads();
+        __syncthreads();   // tile of chunk c consumed
+        if constexpr (KS > 1) {
+            if (kh == 1) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
+            }
+        }
+        commit(next);
+        __syncthreads();   // tile of chunk c+1 and the partial states visible
+        if constexpr (KS > 1) {
+            if (kh == 0) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
+            } else {
+                acc = zero_acc();
+            }
+        }
     };
 
     Stage sa, sb;
-    issue(sa, 0);
-    issue(sb, min(1, nc - 1));
-    commit(sa, 0);
+    issue(sa, c0);
+    issue(sb, min(c0 + 1, c1 - 1));
+    commit(sa);
     __syncthreads();
-    int c = 0;
-    for (; c + 1 < nc; c += 2) {
-        step(c, 0, sb, sa);
-        step(c + 1, 1, sa, sb);
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
+        step(c, sb, sa);
+        step(c + 1, sa, sb);
     }
-    if (c < nc) step(c, 0, sb, sa);
+    if (c < c1) step(c, sb, sa);
 
-    if constexpr (KS > 1) {
-        if (kh == 1) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
-        }
-        __syncthreads();
-        if (kh == 0) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
-        }
-    }
-    if (hT != nullptr && kh == 0) {
+    // acc (kh = 0 waves) now holds the state after the group's last chunk
+    float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : hT;
+    if (dst != nullptr && (Ug != nullptr || hT != nullptr) && kh == 0) {
+        const int64_t off = (Ug != nullptr) ? 0 : st_off;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             f32x4 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] = acc[4 * q + r];
-            *reinterpret_cast<f32x4 *>(hT + st_off + (int64_t)p_col * N + n_lane + 8 * q) = o;
+            *reinterpret_cast<f32x4 *>(dst + off + (int64_t)p_col * N + n_lane + 8 * q) = o;
         }
     }
+    if (keeper && gam != nullptr) gam[(int64_t)bh * ng + grp] = run;
+}
+
+// ===========================================================================
+// Group scan.  For each (batch*head, state element): walk the groups in order,
+// H_1 = U_0 and H_{g+1} = gamma_g H_g + U_g; H_g (the true state at group g's
+// start) replaces U_g in place, and the state after the last group is hT.
+// ===========================================================================
+__global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
+                                                         const float *__restrict__ gam,
+                                                         float *__restrict__ hT, int PN, int ng)
+{
+    const int bh = blockIdx.y;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= PN) return;
+    f32x4 hcar = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < ng; ++g) {
+        f32x4 *u = reinterpret_cast<f32x4 *>(Ug + ((int64_t)bh * ng + g) * PN + e);
+        const f32x4 v = *u;
+        if (g > 0) *u = hcar;
+        const float gm = gam[(int64_t)bh * ng + g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hcar[r] = gm * hcar[r] + v[r];
+    }
+    if (hT != nullptr) *reinterpret_cast<f32x4 *>(hT + (int64_t)bh * PN + e) = hcar;
 }
 
 // ===========================================================================
@@ -292,7 +339,8 @@ template <int Q>
 __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
-    const float *__restrict__ D, bf16 *__restrict__ y, int L, int H, int G, int N, int nc, int Lp,
+    const float *__restrict__ D, bf16 *__restrict__ y, const float *__restrict__ Hg,
+    const float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng,
     int xcd)
 {
     constexpr int P = 64, NI = Q / 32, NTHR = Q, NW = Q / 64, NSLOT = NI + 1, NS = 64;
@@ -310,9 +358,20 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     bf16 *Bs = U, *Ss = U + BS_EL, *Mb = U;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // Workgroup -> (chunk, batch*head), heads innermost.  With `xcd` set (nc a
+    // multiple of 8) XCD x gets the contiguous chunk range [x nc/8, (x+1) nc/8):
+    // a chunk's B and C rows are shared by all its heads and a state-pass group's
+    // carried state by its consecutive chunks, and both then stay in one L2.
     const int bH = gridDim.x / nc;
     int c, bh;
-    xcd_split(blockIdx.x, bH, xcd != 0, c, bh);
+    if (xcd) {
+        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        c = x * (nc / 8) + slot / bH;
+        bh = slot % bH;
+    } else {
+        c = blockIdx.x / bH;
+        bh = blockIdx.x % bH;
+    }
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int t0 = c * Q;
     const bool full = t0 + Q <= L;
@@ -325,6 +384,12 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     const float *dh = dtT + (int64_t)bh * Lp + t0;
     const int kq = 8 * (lane >> 5);
     const int I0 = w, I1 = NI - 1 - w;
+    // Chunk-start state handed over by a grouped state pass: S holds the state
+    // relative to the start of the chunk's group, to which beta_c H_g is added
+    // (group 0 already started from the true initial state).
+    const int cgrp = (Hg != nullptr) ? c / K : 0;
+    const float *Hc = (cgrp > 0) ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr;
+    const float bc = (cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
 
     const bool v0 = full || t0 + I0 * 32 + (lane & 31) < L;
     const bool v1 = full || t0 + I1 * 32 + (lane & 31) < L;
@@ -335,21 +400,39 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     // 8 B pieces and P*8/Q S pieces per thread (16 bytes each), 4+4 C fragments.
     constexpr int SPC = P * 8 / NTHR;
     bf16x8 bq[8], sq[SPC], c0n[NS / 16], c1n[NS / 16];
+    f32x4 hq[SPC][2];
     auto load_slice = [&](int n0) {
+        if (full) {   // uniform: no per-lane predication
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-            bq[r] = (full || t0 + t < L) ? ld16(Bb + t * (int)cstride + n0 + oct * 8) : zero8();
+            for (int r = 0; r < 8; ++r) {
+                const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+                bq[r] = ld16(Bb + t * (int)cstride + n0 + oct * 8);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NS / 16; ++ks) {
+                c0n[ks] = ld16(crow0 + n0 + ks * 16);
+                c1n[ks] = ld16(crow1 + n0 + ks * 16);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+                bq[r] = (t0 + t < L) ? ld16(Bb + t * (int)cstride + n0 + oct * 8) : zero8();
+            }
+#pragma unroll
+            for (int ks = 0; ks < NS / 16; ++ks) {
+                c0n[ks] = v0 ? ld16(crow0 + n0 + ks * 16) : zero8();
+                c1n[ks] = v1 ? ld16(crow1 + n0 + ks * 16) : zero8();
+            }
         }
 #pragma unroll
         for (int r = 0; r < SPC; ++r) {
             const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
             sq[r] = ld16(Sb + p * N + n0 + oct * 8);
-        }
-#pragma unroll
-        for (int ks = 0; ks < NS / 16; ++ks) {
-            c0n[ks] = v0 ? ld16(crow0 + n0 + ks * 16) : zero8();
-            c1n[ks] = v1 ? ld16(crow1 + n0 + ks * 16) : zero8();
+            if (Hc != nullptr) {
+                hq[r][0] = *reinterpret_cast<const f32x4 *>(Hc + p * N + n0 + oct * 8);
+                hq[r][1] = *reinterpret_cast<const f32x4 *>(Hc + p * N + n0 + oct * 8 + 4);
+            }
         }
     };
 
@@ -361,11 +444,17 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     {
         const int tg = w * 8 + (lane & 7), cg = lane >> 3;
         u32x4 xv[8];
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            xv[r] = (full || t0 + tg * 8 + r < L)
-                        ? *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
+            for (int r = 0; r < 8; ++r)
+                xv[r] = *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                xv[r] = (t0 + tg * 8 + r < L)
+                            ? *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8)
+                            : u32x4{0u, 0u, 0u, 0u};
+        }
         const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dh + tg * 8);
         const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dh + tg * 8 + 4);
         const float gt = Gh[tid];
@@ -413,7 +502,12 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < SPC; ++r) {
             const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
-            *reinterpret_cast<bf16x8 *>(&Ss[p * SP + oct * 8]) = sq[r];
+            bf16x8 sv = sq[r];
+            if (Hc != nullptr) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sv[e] = (bf16)((float)sv[e] + bc * hq[r][e >> 2][e & 3]);
+            }
+            *reinterpret_cast<bf16x8 *>(&Ss[p * SP + oct * 8]) = sv;
         }
         bf16x8 cf0[NS / 16], cf1[NS / 16];
 #pragma unroll
@@ -530,52 +624,96 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int Q, int NT, int KS>
+template <int Q>
 static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
-                            const float *wT, const float *h0, void *S, float *hT, hipStream_t st)
+                            const float *wT, const float *h0, void *S, float *hT, float *Ug,
+                            float *gam, float *beta, int K, int ng, hipStream_t st)
 {
+    constexpr int NT = 32, KS = 2;
     const int ntiles = (int)(s.N / NT);
     const int bH = (int)(s.b * s.H);
     const int xcd = (bH % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NT, KS>), dim3((unsigned)(bH * ntiles)),
+    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NT, KS>), dim3((unsigned)(bH * ntiles * ng)),
                        dim3(64 * 2 * (NT / 32) * KS), 0, st, (const bf16 *)x, (const bf16 *)B, G2,
-                       wT, h0, (bf16 *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
-                       (int)s.Lp, ntiles, xcd);
+                       wT, h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G,
+                       (int)s.N, (int)s.nc, (int)s.Lp, ntiles, K, ng, xcd);
     return hipGetLastError();
+}
+
+static hipError_t sp_dispatch(const Shape &s, const void *x, const void *B, const float *G2,
+                              const float *wT, const float *h0, void *S, float *hT, float *Ug,
+                              float *gam, float *beta, int K, int ng, hipStream_t st)
+{
+    switch (s.Q) {
+    case 64: return sp_launch<64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_launch<128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_launch<256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    }
 }
 
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
                                   const float *wT, const float *h0, void *S, float *hT,
                                   hipStream_t st)
 {
-    switch (s.Q) {
-    case 64: return sp_launch<64, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
-    case 128: return sp_launch<128, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
-    default: return sp_launch<256, 32, 2>(s, x, B, G2, wT, h0, S, hT, st);
+    return sp_dispatch(s, x, B, G2, wT, h0, S, hT, nullptr, nullptr, nullptr, (int)s.nc, 1, st);
+}
+
+Grouping state_pass_groups(const Shape &s)
+{
+    Grouping gp;
+    if (!s.bf16) {
+        gp.K = (int)s.nc;
+        gp.ng = 1;
+        return gp;
     }
+    // aim for about four state-pass workgroups per CU (two are resident at a
+    // time) while keeping at least two chunks per group
+    const int64_t units = s.b * s.H * (s.N / 32);
+    int64_t ng = (1024 + units - 1) / units;
+    ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc / 2));
+    const int64_t K = (s.nc + ng - 1) / ng;
+    gp.K = (int)K;
+    gp.ng = (int)((s.nc + K - 1) / K);
+    return gp;
+}
+
+hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
+                                     const void *B, const float *G2, const float *wT,
+                                     const float *h0, void *S, float *hT, float *Ug, float *gam,
+                                     float *beta, hipStream_t st)
+{
+    if (!s.bf16 || gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
+    hipError_t e = sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st);
+    if (e != hipSuccess) return e;
+    const int PN = (int)(s.P * s.N);
+    dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
+    hipLaunchKernelGGL(group_scan_kernel, grid, dim3(256), 0, st, Ug, gam, hT, PN, gp.ng);
+    return hipGetLastError();
 }
 
 template <int Q>
 static hipError_t co_launch(const Shape &s, const void *x, const void *B, const void *C,
                             const float *G2, const float *dtT, const void *S, const float *D,
-                            void *y, hipStream_t st)
+                            void *y, const float *Hg, const float *beta, int K, int ng,
+                            hipStream_t st)
 {
     const int xcd = (s.nc % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((chunk_out_bf16_kernel<Q>), dim3((unsigned)(s.nc * s.b * s.H)), dim3(Q), 0,
                        st, (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
-                       (const bf16 *)S, D, (bf16 *)y, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
-                       (int)s.nc, (int)s.Lp, xcd);
+                       (const bf16 *)S, D, (bf16 *)y, Hg, beta, (int)s.L, (int)s.H, (int)s.G,
+                       (int)s.N, (int)s.nc, (int)s.Lp, K, ng, xcd);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
-                                 void *y, hipStream_t st)
+                                 void *y, const float *Hg, const float *beta, int K, int ng,
+                                 hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return co_launch<64>(s, x, B, C, G2, dtT, S, D, y, st);
-    case 128: return co_launch<128>(s, x, B, C, G2, dtT, S, D, y, st);
-    default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, st);
+    case 64: return co_launch<64>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    case 128: return co_launch<128>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
     }
 }
 

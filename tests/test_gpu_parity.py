@@ -39,9 +39,17 @@ def _gpu_forward(inp, w, dev, poison=True):
     return y, hT, ws, prob
 
 
-def _workspace_views(ws, prob, w):
-    v = ssd.workspace_views(prob, ws)
-    return v["G2"], v["dtT"], v["S"]
+def _stage_states(inp, w, dev):
+    """True chunk-start states and final state from the public stage-1 and stage-2
+    entry points (one serial chain per (batch, head) and N tile)."""
+    d = to_dev(inp, dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S = torch.full((w.batch, w.nheads, w.nchunks, w.headdim, w.dstate), float("nan"),
+                   device=dev, dtype=d["x"].dtype)
+    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"], S=S)
+    torch.cuda.synchronize()
+    return S, hT
 
 
 def _check_forward(w, seed=0, inp=None, dev=None):
@@ -54,8 +62,9 @@ def _check_forward(w, seed=0, inp=None, dev=None):
     tol = TOL[w.dtype]
     check(f64(y), ref["y"], tol, "y")
     check(f64(hT), ref["hT"], tol, "hT")
-    G2, dtT, S = _workspace_views(ws, prob, w)
-    check(f64(S), ref["snaps"], tol, "chunk-start states")
+    S, hT2 = _stage_states(inp, w, dev)
+    check(f64(S), ref["snaps"], tol, "chunk-start states (stage 2)")
+    check(f64(hT2), ref["hT"], tol, "hT (stage 2)")
     return y, hT, ref
 
 
@@ -108,6 +117,11 @@ SMALL_CASES = [
     _wl("bf16_tail_q256", "bf16", 2, 700, 2, 64, 192, 1, 256),
     _wl("bf16_short", "bf16", 1, 37, 2, 64, 64, 1, 128),
     _wl("bf16_one_token", "bf16", 1, 1, 2, 64, 64, 1, 64),
+    # many state-pass groups, ragged last chunk, groups of uneven length
+    _wl("bf16_groups_q128", "bf16", 1, 3000, 2, 64, 128, 1, 128),
+    _wl("bf16_groups_q256", "bf16", 2, 2900, 3, 64, 256, 3, 256),
+    _wl("bf16_groups_q64", "bf16", 1, 1100, 1, 64, 64, 1, 64, h0=False),
+    _wl("bf16_groups_odd", "bf16", 1, 1100, 43, 64, 256, 1, 128),   # 3 chunks per group
 ]
 
 
@@ -194,9 +208,11 @@ def test_deterministic_bitwise():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
-def test_stages_compose_to_forward():
+def test_stages_match_forward():
+    """The public stages (one serial chain) and ssd_forward (grouped state pass with the
+    carried state added in stage 3) agree with each other and with the oracle."""
     dev = require_gpu()
-    w = _wl("stages", "bf16", 2, 320, 4, 64, 128, 2, 64)
+    w = _wl("stages", "bf16", 2, 1280, 4, 64, 128, 2, 64)
     inp = make_inputs(w, 10)
     d = to_dev(inp, dev)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
@@ -204,7 +220,27 @@ def test_stages_compose_to_forward():
     S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"])
     y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
     yf, hTf, _, _ = _gpu_forward(inp, w, dev)
-    assert torch.equal(y, yf) and torch.equal(hT, hTf)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    check(f64(y), ref["y"], TOL["bf16"], "y (stages)")
+    check(f64(yf), ref["y"], TOL["bf16"], "y (forward)")
+    check(f64(hTf), f64(hT), 1e-5, "hT forward vs stages (both fp32 states)")
+
+
+def test_forward_timed_events():
+    dev = require_gpu()
+    w = _wl("timed", "bf16", 1, 1024, 2, 64, 128, 1, 128)
+    inp = make_inputs(w, 12)
+    d = to_dev(inp, dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    y1, h1 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                             events=evs)
+    y2, h2 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    assert all(t >= 0 for t in times), times
 
 
 def test_errors_before_launch():
@@ -244,7 +280,6 @@ def test_full_workload_sampled(name, units):
     inp = make_inputs(w, 0)
     print(f"case {name}: units {units}", flush=True)
     y, hT, ws, prob = _gpu_forward(inp, w, dev)
-    _, _, S = _workspace_views(ws, prob, w)
     ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
                          units=units, chunk=w.chunk)
     u = ref["units"]
@@ -253,7 +288,9 @@ def test_full_workload_sampled(name, units):
     tol = TOL[w.dtype]
     check(y_s, ref["y"], tol, "y (sampled units)")
     check(np.stack([f64(hT[b, h]) for b, h in zip(b_idx, h_idx)]), ref["hT"], tol, "hT (sampled units)")
+    S, _ = _stage_states(inp, w, dev)
     check(np.stack([f64(S[b, h]) for b, h in zip(b_idx, h_idx)]), ref["snaps"], tol,
-          "chunk-start states (sampled units)")
+          "chunk-start states (stage 2, sampled units)")
+    del S
     # every output element was written and is finite
     assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
