@@ -315,49 +315,57 @@ __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
 }
 
 // ===========================================================================
-// Chunk output.  Workgroup = one (chunk, batch*head), Q/64 waves; wave w owns
-// row tiles I0 = w and I1 = Q/32-1-w (32 tokens each), so every wave handles
-// the same number (Q/32 + 1) of causal tile pairs (J, I), J <= I.  The output
-// is built transposed, Y^T [64 p x 32 tokens] per row tile.
+// Chunk output.  Workgroup = one (chunk, batch*head) with Q/32 waves; wave w
+// owns one 32-token row tile I = rowtile(w).  Waves w and w + Q/64 (which the
+// hardware places on the same SIMD) get tiles that add up to Q/32 - 1, so every
+// SIMD does the same number, Q/32 + 1, of causal tile pairs (J, I), J <= I.
+// Two waves per SIMD let one wave's loads, barriers and exponentials overlap
+// the other's matrix products.  The output is built transposed, Y^T [64 p x 32
+// tokens] per row tile.
 //
 // Phase 1 streams N in slices of 64: the slice of B (all chunk rows) and of S
-// (all p) is staged in LDS; each wave reads its C rows from global and
-//   * accumulates (B C^T)[j, i] for its tile pairs (accumulators live across
-//     all slices; slot s <= w is (J = s, I0), slot s > w is (J = s - w - 1, I1));
-//   * accumulates Y^T += S C^T (the inter-chunk term).
-// Phase 2 turns every C B^T tile into the decay matrix
+// (all p) is staged in LDS, the wave's C rows come from global memory, and the
+// next slice is loaded into registers while the current one is multiplied:
+//   * CB_J = (B C^T)[tile J, tile I] for J <= I (accumulators indexed by J);
+//   * Y^T += S C^T (the inter-chunk term).
+// Phase 2, per J <= I: the C B^T tile becomes the decay matrix
 //   M[j, i] = (i >= j) ? CB[j, i] * exp2(G_i - G_j) : 0      (selection, never a product with a mask)
-// rounded to bf16 and parked in LDS (it reuses the B/S staging space).  Off the
-// diagonal (J < I) the decay factors exactly into exp2(G_i - G_e) * exp2(G_e - G_j)
-// with e the last token of tile J; both factors are <= 1, the second is a
-// per-token table, so such a tile costs one exp2 per lane instead of sixteen.
-// Phase 3, per row tile: scale Y^T column i by exp2(G_i), add M(J, I) (dt x)_J
-// for J <= I with M read back as the B operand and (dt x)^T read from LDS as
-// 16-byte fragments in the accumulator's token order, then add D x and store.
+// rounded to bf16 and fed to MFMA straight from registers against (dt x)^T.
+// Off the diagonal (J < I) the decay factors exactly into
+// exp2(G_i - G_e) * exp2(G_e - G_j), e the last token of tile J; both factors are
+// <= 1, the second a per-token table, so such a tile costs one exp2 per lane.
+// The Y^T accumulator is scaled by exp2(G_i) between the two phases.
+//
+// Chunk-start state handed over by a grouped state pass (Hg != NULL): S holds
+// the state relative to the start of the chunk's group, to which beta_c H_g is
+// added while staging (group 0 already started from the true initial state).
 // ===========================================================================
 template <int Q>
-__global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
+__global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
     const float *__restrict__ D, bf16 *__restrict__ y, const float *__restrict__ Hg,
     const float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng,
     int xcd)
 {
-    constexpr int P = 64, NI = Q / 32, NTHR = Q, NW = Q / 64, NSLOT = NI + 1, NS = 64;
+    constexpr int P = 64, NI = Q / 32, NW = Q / 32, NTHR = 2 * Q, NS = 64;
     constexpr int XP = Q + 8, BP = frag_pitch(NS), SP = frag_pitch(NS);
-    constexpr int BS_EL = Q * BP, SS_EL = P * SP, MB_EL = NW * NSLOT * 2 * 64 * 8;
-    constexpr int U_EL = (BS_EL + SS_EL > MB_EL) ? BS_EL + SS_EL : MB_EL;
+    constexpr int BPC = Q * (NS / 8) / NTHR;   // 16-byte B pieces per thread per slice
+    constexpr int SPC = P * (NS / 8) / NTHR;   // 16-byte S pieces per thread per slice
+    static_assert(BPC >= 1 && SPC >= 1, "slice staging cover");
     // (dt x)^T [p][position]: within each 16-token group the token at offset o is
-    // kept at position o ^ ((o >> 2 & 1) ^ (o >> 3 & 1)) * 12, i.e. the middle two
-    // 4-token blocks are swapped, so the accumulator token order 4(l/32)+{0..3},
-    // 8+4(l/32)+{0..3} of lane l becomes 8 consecutive positions.
+    // kept at position o with its middle two 4-token blocks swapped, so the
+    // accumulator token order 4(l/32)+{0..3}, 8+4(l/32)+{0..3} of lane l becomes 8
+    // consecutive positions.
     __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
-    __shared__ __attribute__((aligned(16))) bf16 U[U_EL];
+    __shared__ __attribute__((aligned(16))) bf16 Bs[Q * BP];
+    __shared__ __attribute__((aligned(16))) bf16 Ss[P * SP];
     __shared__ __attribute__((aligned(16))) float Gs[Q];
     __shared__ __attribute__((aligned(16))) float We[Q];   // exp2(G_e - G_j), e = end of j's tile
-    bf16 *Bs = U, *Ss = U + BS_EL, *Mb = U;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int I = (w < NW / 2) ? w : NW - 1 - (w - NW / 2);
+
     // Workgroup -> (chunk, batch*head), heads innermost.  With `xcd` set (nc a
     // multiple of 8) XCD x gets the contiguous chunk range [x nc/8, (x+1) nc/8):
     // a chunk's B and C rows are shared by all its heads and a state-pass group's
@@ -365,8 +373,8 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     const int bH = gridDim.x / nc;
     int c, bh;
     if (xcd) {
-        const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        c = x * (nc / 8) + slot / bH;
+        const int xx = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        c = xx * (nc / 8) + slot / bH;
         bh = slot % bH;
     } else {
         c = blockIdx.x / bH;
@@ -383,47 +391,34 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     const float *Gh = G2 + (int64_t)bh * Lp + t0;
     const float *dh = dtT + (int64_t)bh * Lp + t0;
     const int kq = 8 * (lane >> 5);
-    const int I0 = w, I1 = NI - 1 - w;
-    // Chunk-start state handed over by a grouped state pass: S holds the state
-    // relative to the start of the chunk's group, to which beta_c H_g is added
-    // (group 0 already started from the true initial state).
     const int cgrp = (Hg != nullptr) ? c / K : 0;
     const float *Hc = (cgrp > 0) ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr;
     const float bc = (cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
 
-    const bool v0 = full || t0 + I0 * 32 + (lane & 31) < L;
-    const bool v1 = full || t0 + I1 * 32 + (lane & 31) < L;
-    const bf16 *crow0 = Cb + (I0 * 32 + (lane & 31)) * (int)cstride + kq;
-    const bf16 *crow1 = Cb + (I1 * 32 + (lane & 31)) * (int)cstride + kq;
+    const int i_loc = I * 32 + (lane & 31);
+    const bool iv = full || t0 + i_loc < L;
+    const bf16 *crow = Cb + i_loc * (int)cstride + kq;
 
-    // Registers holding the next N slice while the current one is multiplied:
-    // 8 B pieces and P*8/Q S pieces per thread (16 bytes each), 4+4 C fragments.
-    constexpr int SPC = P * 8 / NTHR;
-    bf16x8 bq[8], sq[SPC], c0n[NS / 16], c1n[NS / 16];
+    // registers holding the next N slice while the current one is multiplied
+    bf16x8 bq[BPC], sq[SPC], cn[NS / 16];
     f32x4 hq[SPC][2];
     auto load_slice = [&](int n0) {
         if (full) {   // uniform: no per-lane predication
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
+            for (int r = 0; r < BPC; ++r) {
                 const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
                 bq[r] = ld16(Bb + t * (int)cstride + n0 + oct * 8);
             }
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) {
-                c0n[ks] = ld16(crow0 + n0 + ks * 16);
-                c1n[ks] = ld16(crow1 + n0 + ks * 16);
-            }
+            for (int ks = 0; ks < NS / 16; ++ks) cn[ks] = ld16(crow + n0 + ks * 16);
         } else {
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
+            for (int r = 0; r < BPC; ++r) {
                 const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
                 bq[r] = (t0 + t < L) ? ld16(Bb + t * (int)cstride + n0 + oct * 8) : zero8();
             }
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) {
-                c0n[ks] = v0 ? ld16(crow0 + n0 + ks * 16) : zero8();
-                c1n[ks] = v1 ? ld16(crow1 + n0 + ks * 16) : zero8();
-            }
+            for (int ks = 0; ks < NS / 16; ++ks) cn[ks] = iv ? ld16(crow + n0 + ks * 16) : zero8();
         }
 #pragma unroll
         for (int r = 0; r < SPC; ++r) {
@@ -437,35 +432,37 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
     };
 
     // (dt x)^T tile and the chunk's decays; the first N slice is requested right
-    // behind the x tile so both latencies overlap.  Thread = one 8-token x 8-p
+    // behind the x tile so both latencies overlap.  Thread = one 8-token x 4-p
     // block: rows loaded token-major, scaled by dt, packed per p column.  A wave
-    // covers 8 token groups (lane % 8) x 8 column groups (lane / 8): whole token
-    // rows per load, distinct banks per 16-lane group of LDS writes.
+    // covers 8 token groups (lane % 8) x 8 column groups (lane / 8).
     {
-        const int tg = w * 8 + (lane & 7), cg = lane >> 3;
-        u32x4 xv[8];
+        const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + (lane >> 3);
+        u32x2 xv[8];
         if (full) {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                xv[r] = *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8);
+                xv[r] = *reinterpret_cast<const u32x2 *>(xb + (tg * 8 + r) * (int)xstride + cg * 4);
         } else {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 xv[r] = (t0 + tg * 8 + r < L)
-                            ? *reinterpret_cast<const u32x4 *>(xb + (tg * 8 + r) * (int)xstride + cg * 8)
-                            : u32x4{0u, 0u, 0u, 0u};
+                            ? *reinterpret_cast<const u32x2 *>(xb + (tg * 8 + r) * (int)xstride + cg * 4)
+                            : u32x2{0u, 0u};
         }
         const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dh + tg * 8);
         const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dh + tg * 8 + 4);
-        const float gt = Gh[tid];
-        const float ge = Gh[tid | 31];
+        float gt = 0.0f, ge = 0.0f;
+        if (tid < Q) {
+            gt = Gh[tid];
+            ge = Gh[tid | 31];
+        }
         load_slice(0);
         const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
         // positions of this block's tokens: 8 tokens at offset 0 or 8 of a 16-group
         // -> two runs of 4 positions, 8 apart
         const int pos0 = (tg >> 1) * 16 + ((tg & 1) ? 4 : 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             u32x2 lo, hi;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
@@ -476,26 +473,26 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
                 hi[k] = pack_bf16(((j & 1) ? bf_hi(b0) : bf_lo(b0)) * d[4 + 2 * k],
                                   ((j & 1) ? bf_hi(b1) : bf_lo(b1)) * d[5 + 2 * k]);
             }
-            bf16 *row = Xd + (cg * 8 + j) * XP + pos0;
+            bf16 *row = Xd + (cg * 4 + j) * XP + pos0;
             *reinterpret_cast<u32x2 *>(row) = lo;
             *reinterpret_cast<u32x2 *>(row + 8) = hi;
         }
-        Gs[tid] = gt;
-        We[tid] = fast_exp2(ge - gt);
+        if (tid < Q) {
+            Gs[tid] = gt;
+            We[tid] = fast_exp2(ge - gt);
+        }
     }
 
-    f32x16 cb[NSLOT];
+    f32x16 cb[NI];
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) cb[s] = zero_acc();
-    f32x16 ya[2][2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) { ya[s][0] = zero_acc(); ya[s][1] = zero_acc(); }
+    for (int J = 0; J < NI; ++J) cb[J] = zero_acc();
+    f32x16 ya[2] = {zero_acc(), zero_acc()};
 
     // ---------------- phase 1: C B^T tiles and S C^T over N slices ----------------
     for (int n0 = 0; n0 < N; n0 += NS) {
         __syncthreads();   // previous slice consumed; first time: Xd, Gs, We written
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
+        for (int r = 0; r < BPC; ++r) {
             const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
             *reinterpret_cast<bf16x8 *>(&Bs[t * BP + oct * 8]) = bq[r];
         }
@@ -509,49 +506,40 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
             }
             *reinterpret_cast<bf16x8 *>(&Ss[p * SP + oct * 8]) = sv;
         }
-        bf16x8 cf0[NS / 16], cf1[NS / 16];
+        bf16x8 cf[NS / 16];
 #pragma unroll
-        for (int ks = 0; ks < NS / 16; ++ks) { cf0[ks] = c0n[ks]; cf1[ks] = c1n[ks]; }
+        for (int ks = 0; ks < NS / 16; ++ks) cf[ks] = cn[ks];
         // next slice (the last iteration re-requests the last slice; never used)
         load_slice(min(n0 + NS, N - NS));
         __syncthreads();
 
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            const bool side0 = s <= w;
-            const int J = side0 ? s : s - w - 1;
-            const bf16 *brow = Bs + (J * 32 + (lane & 31)) * BP + kq;
-            if (side0) {
+        for (int J = 0; J < NI; ++J) {
+            if (J <= I) {
+                const bf16 *brow = Bs + (J * 32 + (lane & 31)) * BP + kq;
 #pragma unroll
                 for (int ks = 0; ks < NS / 16; ++ks)
-                    mma(cb[s], *reinterpret_cast<const bf16x8 *>(brow + ks * 16), cf0[ks]);
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < NS / 16; ++ks)
-                    mma(cb[s], *reinterpret_cast<const bf16x8 *>(brow + ks * 16), cf1[ks]);
+                    mma(cb[J], *reinterpret_cast<const bf16x8 *>(brow + ks * 16), cf[ks]);
             }
         }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
             const bf16 *srow = Ss + (pp * 32 + (lane & 31)) * SP + kq;
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) {
-                const bf16x8 sf = *reinterpret_cast<const bf16x8 *>(srow + ks * 16);
-                mma(ya[0][pp], sf, cf0[ks]);
-                mma(ya[1][pp], sf, cf1[ks]);
-            }
+            for (int ks = 0; ks < NS / 16; ++ks)
+                mma(ya[pp], *reinterpret_cast<const bf16x8 *>(srow + ks * 16), cf[ks]);
         }
     }
-    __syncthreads();   // B/S staging space becomes the M store
 
-    // ---------------- phase 2: decay, causal selection, bf16, into LDS ----------------
-    const float gi0 = Gs[I0 * 32 + (lane & 31)], gi1 = Gs[I1 * 32 + (lane & 31)];
+    // ---------------- phase 2: Y^T = exp2(G_i) Y^T + M (dt x) ----------------
+    const float gi = Gs[i_loc];
+    const float si = fast_exp2(gi);
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) {
-        const bool side0 = s <= w;
-        const int J = side0 ? s : s - w - 1;
-        const int I = side0 ? I0 : I1;
-        const float gi = side0 ? gi0 : gi1;
+    for (int v = 0; v < 16; ++v) { ya[0][v] *= si; ya[1][v] *= si; }
+    const int offX = (lane & 31) * XP + 8 * (lane >> 5);
+#pragma unroll
+    for (int J = 0; J < NI; ++J) {
+        if (J > I) continue;
         const int jrow = J * 32 + 4 * (lane >> 5);   // + 8q + r for element 4q + r
         bf16x8 m[2];
         if (J < I) {
@@ -560,62 +548,42 @@ __global__ __launch_bounds__(Q) void chunk_out_bf16_kernel(
             for (int q = 0; q < 4; ++q) {
                 const f32x4 we = *reinterpret_cast<const f32x4 *>(&We[jrow + 8 * q]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) m[q >> 1][4 * (q & 1) + r] = (bf16)(cb[s][4 * q + r] * we[r] * ci);
+                for (int r = 0; r < 4; ++r) m[q >> 1][4 * (q & 1) + r] = (bf16)(cb[J][4 * q + r] * we[r] * ci);
             }
         } else {
-            const int i_loc = I * 32 + (lane & 31);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gs[jrow + 8 * q]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float dec = fast_exp2(gi - gj[r]);
-                    const float val = cb[s][4 * q + r] * dec;
+                    const float val = cb[J][4 * q + r] * fast_exp2(gi - gj[r]);
                     m[q >> 1][4 * (q & 1) + r] = (bf16)((i_loc >= jrow + 8 * q + r) ? val : 0.0f);
                 }
             }
         }
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-            *reinterpret_cast<bf16x8 *>(&Mb[(((w * NSLOT + s) * 2 + sub) * 64 + lane) * 8]) = m[sub];
-    }
-    // each lane reads back only what it wrote: no barrier needed
-
-    // ---------------- phase 3: Y^T += M (dt x), then D x and store ----------------
-    const int offX = (lane & 31) * XP + 8 * (lane >> 5);
-    const float Dh = D[h];
+        for (int sub = 0; sub < 2; ++sub) {
+            const bf16 *xt = Xd + offX + J * 32 + 16 * sub;
 #pragma unroll
-    for (int side = 0; side < 2; ++side) {
-        const int I = side == 0 ? I0 : I1;
-        const int i_loc = I * 32 + (lane & 31);
-        const float si = fast_exp2(side == 0 ? gi0 : gi1);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) { ya[side][0][v] *= si; ya[side][1][v] *= si; }
-        const int s0 = side == 0 ? 0 : w + 1;
-        for (int J = 0; J <= I; ++J) {
-            const bf16 *mrow = Mb + (((w * NSLOT + s0 + J) * 2) * 64 + lane) * 8;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const bf16x8 mf = *reinterpret_cast<const bf16x8 *>(mrow + sub * 64 * 8);
-                const bf16 *xt = Xd + offX + J * 32 + 16 * sub;
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) mma(ya[side][pp], ld16(xt + pp * 32 * XP), mf);
-            }
+            for (int pp = 0; pp < 2; ++pp) mma(ya[pp], ld16(xt + pp * 32 * XP), m[sub]);
         }
-        if (full || t0 + i_loc < L) {
-            const int yo = i_loc * (int)xstride;
-            bf16 *yb = y + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
+    }
+
+    // ---------------- y = Y + D x ----------------
+    if (iv) {
+        const float Dh = D[h];
+        const int yo = i_loc * (int)xstride;
+        bf16 *yb = y + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
 #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
+        for (int pp = 0; pp < 2; ++pp) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
-                    const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xb + yo + p);
-                    bf16x4 o;
+            for (int q = 0; q < 4; ++q) {
+                const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xb + yo + p);
+                bf16x4 o;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[side][pp][4 * q + r] + Dh * (float)xv[r]);
-                    *reinterpret_cast<bf16x4 *>(yb + yo + p) = o;
-                }
+                for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pp][4 * q + r] + Dh * (float)xv[r]);
+                *reinterpret_cast<bf16x4 *>(yb + yo + p) = o;
             }
         }
     }
@@ -698,7 +666,7 @@ static hipError_t co_launch(const Shape &s, const void *x, const void *B, const 
                             hipStream_t st)
 {
     const int xcd = (s.nc % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_out_bf16_kernel<Q>), dim3((unsigned)(s.nc * s.b * s.H)), dim3(Q), 0,
+    hipLaunchKernelGGL((chunk_out_bf16_kernel<Q>), dim3((unsigned)(s.nc * s.b * s.H)), dim3(2 * Q), 0,
                        st, (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
                        (const bf16 *)S, D, (bf16 *)y, Hg, beta, (int)s.L, (int)s.H, (int)s.G,
                        (int)s.N, (int)s.nc, (int)s.Lp, K, ng, xcd);
