@@ -9,10 +9,26 @@ timed steps; the roofline of the dominant stage from its algorithmic bytes and
 flops; and the fp64 CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--copy-mib M]
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of this
+script (FETCH_SIZE, then WRITE_SIZE), each with ``--copy-mib`` so that a plain
+device-to-device copy of known size calibrates the counter:
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d DIR_F -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -f csv -d DIR_W -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-mib 1024
+    python bench.py --summarize-pmc DIR_F DIR_W --copy-mib 1024
+
+The last command writes profiles/traffic_<workload>.json, which later runs report
+as ``roofline.traffic`` as long as the kernel sources hash to the same value (null
+otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import statistics
@@ -23,6 +39,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+KERNEL_SOURCES = ["state_space_sequence_cumsum_amd/csrc/ssd_bf16.hip",
+                  "state_space_sequence_cumsum_amd/csrc/ssd_kernels.hip",
+                  "state_space_sequence_cumsum_amd/csrc/ssd_device.h",
+                  "state_space_sequence_cumsum_amd/csrc/ssd_api.cpp",
+                  "state_space_sequence_cumsum_amd/build.py"]
+KERNEL_NAMES = {"chunk_cumsum": "chunk_cumsum_kernel", "state_pass": "state_pass",
+                "group_scan": "group_scan_kernel", "chunk_out": "chunk_out"}
+COPY_KERNEL = "copyBuffer"
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
@@ -76,6 +100,68 @@ def cpu_baseline(w, inp, budget_s=20.0):
                       f"fraction of heads / wall time {el:.2f} s"}
 
 
+def source_hash():
+    """sha256 over the kernel sources and build flags: counter figures taken from another
+    version of the kernels are not reported."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(w):
+    return os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+
+
+def read_counter_runs(d, counter):
+    """Mean counter value (KiB) per dispatch, per kernel kind, from a rocprofv3 --pmc csv run."""
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                kind = next((k for k, key in KERNEL_NAMES.items() if key in name), None)
+                if kind is None and COPY_KERNEL in name:
+                    kind = "copy"
+                if kind is not None:
+                    vals.setdefault(kind, []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_pmc(w, fetch_dir, write_dir, copy_mib):
+    """Per-launch HBM bytes of each kernel from the FETCH_SIZE and WRITE_SIZE runs, each
+    scaled by what the same counter reads for the copy of copy_mib MiB."""
+    f, wr = read_counter_runs(fetch_dir, "FETCH_SIZE"), read_counter_runs(write_dir, "WRITE_SIZE")
+    if "copy" not in f or "copy" not in wr:
+        raise SystemExit("no copy kernel in the counter runs: record them with --copy-mib")
+    known_kib = copy_mib * 1024.0
+    # the copy is the largest copyBuffer dispatch (inputs are also uploaded by copies)
+    f_scale = known_kib / max(f["copy"])
+    w_scale = known_kib / max(wr["copy"])
+    alg = algorithmic(w)
+    cmd = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 3 --warmup 1 "
+           f"--no-cpu-baseline --copy-mib {copy_mib} --workload {w.name}")
+    out = {"workload": w.name, "source_hash": source_hash(), "copy_mib": copy_mib,
+           "commands": [cmd.format(c="FETCH_SIZE", d=fetch_dir), cmd.format(c="WRITE_SIZE", d=write_dir),
+                        f"python bench.py --summarize-pmc {fetch_dir} {write_dir} --copy-mib {copy_mib}"
+                        f" --workload {w.name}"],
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in ("chunk_cumsum", "state_pass", "group_scan", "chunk_out"):
+        if k not in f or k not in wr:
+            continue
+        fk, wk = statistics.fmean(f[k]), statistics.fmean(wr[k])
+        tb = (fk * f_scale + wk * w_scale) * 1024.0
+        out["kernels"][k] = {"fetch_kib": fk, "write_kib": wk, "dispatches": len(f[k]),
+                             "traffic_bytes": tb,
+                             "algorithmic_bytes": alg[k]["bytes"] if k in alg else None}
+    with open(traffic_file(w), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,7 +170,15 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        from state_space_sequence_cumsum_amd.inputs import HEADLINE, WORKLOADS
+        summarize_pmc(WORKLOADS[args.workload or HEADLINE], *args.summarize_pmc, args.copy_mib)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -116,6 +210,14 @@ def main():
         ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
                         y=y, hT=hT, workspace=ws, stream=stream, events=events)
 
+    if args.copy_mib > 0:   # a plain copy of known size, outside the timed region
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         forward()
     torch.cuda.synchronize()
@@ -143,9 +245,17 @@ def main():
         if n != "chunk_cumsum":
             kern[n]["frac_mfma"] = kern[n]["TFLOP_s"] / peak
     dom = max(("state_pass", "chunk_out"), key=lambda n: kern[n]["mean_us"])
+    traffic = None
+    try:
+        with open(traffic_file(w)) as fh:
+            tf = json.load(fh)
+        if tf.get("source_hash") == source_hash() and dom in tf["kernels"]:
+            traffic = int(tf["kernels"][dom]["traffic_bytes"])
+    except (OSError, ValueError, KeyError):
+        traffic = None
     roof = {"bound": "hbm", "kernel": dom, "achieved": round(kern[dom]["GB_s"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(alg[dom]["bytes"]),
             "mean_launch_us": round(kern[dom]["mean_us"], 2)}
 
