@@ -89,8 +89,10 @@ ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const fl
 
 /* Stage 2 (section "Kernel 2: fwd_pass_state", the decayed chunk jump): serially over
  * chunks c, S[b,h,c] = h (the state at the chunk start, h = h0 or 0 for c = 0), then
- *     h <- exp2(G2_last) h + X_c^T W_c,   W_c[t,n] = round(wT_t B[t,n])
- * with G2_last = G2 at the chunk's last position and W rounded to the input type.
+ *     h <- exp2(G2_last) h + Xw_c^T B_c,   Xw_c[t,p] = round(wT_t x[t,p])
+ * with G2_last = G2 at the chunk's last position.  The weight wT_t multiplies the
+ * 64-wide x row (rounded to the input type) instead of the N-wide B row; the product
+ * is the same sum of wT_t x[t,p] B[t,n].
  * After the last chunk hT = h (skipped when hT is NULL).  h0 may be NULL (zero
  * initial state).  Reads x, B, G2, wT, h0; writes S, hT. */
 ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,

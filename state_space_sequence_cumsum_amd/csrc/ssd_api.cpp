@@ -29,9 +29,12 @@ ssd_status check_shape(const ssd_problem *p)
     if (p->batch * p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->seqlen > (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
     if (p->batch > 65535) return SSD_ERR_UNSUPPORTED;
-    // in-chunk element offsets are 32-bit
+    // in-chunk element offsets are 32-bit, and so are byte offsets within one batch
+    // of x and of B / C
     if (p->chunk * p->nheads * p->headdim >= (int64_t(1) << 31)) return SSD_ERR_UNSUPPORTED;
     if (p->chunk * p->ngroups * p->dstate >= (int64_t(1) << 31)) return SSD_ERR_UNSUPPORTED;
+    if (p->seqlen * p->nheads * p->headdim >= (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
+    if (p->seqlen * p->ngroups * p->dstate >= (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 

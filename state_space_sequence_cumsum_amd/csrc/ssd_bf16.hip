@@ -42,252 +42,363 @@ __device__ __forceinline__ void xcd_split(int id, int n_minor, bool xcd, int &ma
 }
 
 // ===========================================================================
-// State pass.  Workgroup = one (batch*head, N tile of NT columns, group of up
-// to K consecutive chunks).  It keeps h^T [NT x 64] in fp32 accumulators: wave
-// (ph, nh, kh) owns rows n in [32 nh, 32 nh + 32) and columns p in
-// [32 ph, 32 ph + 32) for the tokens of K-half kh (KS = 2 splits each chunk's
-// tokens over two wave sets whose partial states are summed through LDS at
-// every chunk boundary).
+// State pass.  Workgroup = one (batch*head, range of NR state columns, group
+// of up to K consecutive chunks), NR the largest of 256, 128, 64 dividing N; it
+// keeps h^T [NR x 64] in fp32 MFMA accumulators, wave w owning RTW 32-row tiles
+// of n and CTW 32-column tiles of p.
 //
-// Groups.  The chunk jump h <- a_c h + U_c is linear, so a run of chunks can
-// start from a zero state and be corrected afterwards: group g (chunks
-// [gK, gK+K)) starts from h0 if g == 0 and from 0 otherwise, stores its local
-// chunk-start states, its final local state U_g, the decay products
-// beta_c = prod_{gK <= c' < c} a_c' and gamma_g = prod_{c' in g} a_c'.  A scan
-// over groups (group_scan_kernel) then gives the true state at each group
-// start, H_g, and the true chunk-start state is S_local[c] + beta_c H_g.  With
-// one group (K >= nc) the kernel is the plain serial state pass and writes
-// true states and hT directly.
+// The chunk jump h <- a_c h + sum_t w_t x_t (outer) B_t (a_c = exp2(G2_last),
+// w_t = dt_t exp2(G2_last - G2_t) from stage 1) is evaluated with the weight on
+// the x side: the contraction operand is x~ = round_bf16(w_t x_t), 64 wide, so
+// the N-wide B tile is used exactly as loaded.
 //
-// Operands, both k-packed by token:
-//   * X (B operand): the x tile is copied into LDS as is, token-major [t][p],
-//     with 16-byte writes of whole token rows, and read back with the LDS
-//     transpose read;
-//   * W (A operand): each thread loads an 8-token x WC-column block of B,
-//     scales token t by its weight w_t (from stage 1) and bf16-packs the pairs
-//     (t, t+1) of each column, which is already the k-packed layout WT[n][t];
-//     read back as one 16-byte fragment per MFMA.
-// The LDS tile is single-buffered (about 65 KB at Q = 256) so that two
-// workgroups share a CU and overlap each other's loads, barriers and MFMAs;
-// global loads still run two chunks ahead in registers.
+// Each chunk is processed in sub-steps of TS tokens.  Step s of the loop:
+//   * copies B of sub-step s+1 into LDS token-major (16-byte rows) and x~ of
+//     sub-step s+2 (scaled on the way), both from registers loaded D sub-steps
+//     earlier, then reloads the freed registers;
+//   * k-packs x~ of s+1, Xk[p][t], by transpose-reading its token-major tile
+//     (4 consecutive tokens of one p per lane) and writing 8 bytes;
+//   * at a chunk start, writes the chunk-start state (bf16) into an LDS tile,
+//     which the next step stores to HBM as whole 16-byte-per-lane rows, and
+//     decays the state;
+//   * MFMA over sub-step s: A = B^T rows n, transpose-read from the token-major
+//     B tile (each B element is read once), B operand = Xk rows p (16-byte
+//     reads; every wave reads all of x~, the cheap operand);
+//   * one barrier.
+// Every LDS buffer is written one step before it is read and rewritten only
+// after the barrier that follows its last read, so two copies of each suffice.
+// Indices past the group's last sub-step are clamped (the extra copies are
+// never read) and rows past L are clamped to row L-1 (their weight is 0), so
+// the loop body has no branches around memory operations and the wait counts
+// leave later sub-steps in flight.
+//
+// Groups.  The jump is linear, so a run of chunks can start from a zero state
+// and be corrected afterwards: group g (chunks [gK, gK+K)) starts from h0 if
+// g == 0 and from 0 otherwise, stores its local chunk-start states, its final
+// local state U_g, the decay products beta_c = prod_{gK <= c' < c} a_c' and
+// gamma_g = prod_{c' in g} a_c'.  A scan over groups (group_scan_kernel) then
+// gives the true state at each group start, H_g, and the true chunk-start state
+// is S_local[c] + beta_c H_g.  With one group (K >= nc) the kernel is the plain
+// serial state pass and writes true states and hT directly.
 // ===========================================================================
-template <int Q, int NT, int KS>
-__global__ __launch_bounds__(64 * 2 * (NT / 32) * KS) void state_pass_bf16_kernel(
+constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
+constexpr int lcm3(int a, int b, int c)
+{
+    const int ab = a / gcd_(a, b) * b;
+    return ab / gcd_(ab, c) * c;
+}
+
+template <int Q, int N>   // N = NR, the columns of one workgroup
+struct SpCfg {
+    static constexpr int P = 64;
+    static constexpr int TS = 64;                                // tokens per sub-step
+    static constexpr int NSUB = Q / TS;                          // sub-steps per chunk
+    static constexpr int NWAVE = (N == 64) ? 4 : 8;
+    static constexpr int NTHR = 64 * NWAVE;
+    static constexpr int RTW = 1;                                // n tiles per wave
+    static constexpr int CTW = (N == 256) ? 2 : 1;               // p tiles per wave
+    static constexpr int BP = tr_pitch(N);                       // token-major B rows
+    static constexpr int XRP = tr_pitch(P);                      // token-major x rows
+    static constexpr int XKP = TS + 8;                           // k-packed x~ rows
+    static constexpr int SSP = N + 8;                            // chunk-start state staging rows
+    static constexpr int SPT = P * N / 8 / NTHR;                 // 16-byte state pieces per thread
+    static constexpr int BPT = TS * N / 8 / NTHR;                // 16-byte B pieces per thread
+    static constexpr int XPIECES = TS * P / 8;                   // 16-byte x pieces per sub-step
+    static constexpr int XPT = (XPIECES + NTHR - 1) / NTHR;      // per thread (last may idle)
+    static constexpr int TRG = TS * P / (4 * 16);                // 16-lane transpose reads per sub-step
+    static constexpr int TRL = TRG / (4 * NWAVE);                // ... per lane
+    static_assert(BPT >= 1 && TS * N / 8 % NTHR == 0, "B staging cover");
+    static_assert(TRL >= 1 && TRG % (4 * NWAVE) == 0, "x~ build cover");
+    static_assert((N / 32 / RTW) * (2 / CTW) == NWAVE, "wave tiling");
+    static_assert(Q % TS == 0, "sub-steps per chunk");
+};
+
+template <int Q, int NR, int D>
+__global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
     const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
     float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
-    float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int ntiles, int K,
-    int ng, int xcd)
+    float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng, int xcd)
 {
-    constexpr int P = 64;
-    constexpr int NWN = NT / 32, NWAVES = 2 * NWN * KS, NTHR = 64 * NWAVES;
-    constexpr int KSTEPS = Q / 16 / KS;
-    constexpr int XP = tr_pitch(P);                  // token-major x rows (elements)
-    constexpr int PT = Q + 8;                        // k-packed W rows (elements)
-    constexpr int XPC = Q * (P / 8) / NTHR;          // 16-byte x pieces per thread
-    constexpr int WC = Q * NT / (8 * NTHR);          // W block: 8 tokens x WC columns
-    constexpr int WD = (WC + 1) / 2;                 // dwords per loaded B row piece
-    static_assert(XPC >= 1 && (Q * (P / 8)) % NTHR == 0, "x staging cover");
-    static_assert(WC == 1 || WC == 2 || WC == 4 || WC == 8, "B staging block width");
-    static_assert((Q / 8) * (NT / WC) == NTHR, "B staging cover");
-
-    __shared__ __attribute__((aligned(16))) bf16 Xs[Q * XP];
-    __shared__ __attribute__((aligned(16))) bf16 WT[NT * PT];
-    __shared__ float red[KS > 1 ? (NWAVES / 2) * 16 * 64 : 1];
-    __shared__ float alph;
+    using C = SpCfg<Q, NR>;
+    constexpr int P = C::P, TS = C::TS, NSUB = C::NSUB, NTHR = C::NTHR, RTW = C::RTW,
+                  CTW = C::CTW, BP = C::BP, XRP = C::XRP, XKP = C::XKP, BPT = C::BPT,
+                  XPT = C::XPT, XPIECES = C::XPIECES, TRL = C::TRL;
+    constexpr int SSP = C::SSP, SPT = C::SPT;
+    __shared__ __attribute__((aligned(16))) bf16 Bs[2][TS * BP];
+    __shared__ __attribute__((aligned(16))) bf16 Xr[2][TS * XRP];
+    __shared__ __attribute__((aligned(16))) bf16 Xk[2][P * XKP];
+    __shared__ __attribute__((aligned(16))) bf16 Ss[P * SSP];
+    __shared__ float Al[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ph = wave & 1, nh = (wave >> 1) % NWN, kh = wave / (2 * NWN);
-    int bh, minor;
-    xcd_split(blockIdx.x, ntiles * ng, xcd != 0, bh, minor);
-    const int grp = minor / ntiles, nt = minor % ntiles;
+    // workgroup -> (group, batch*head, column range); with `xcd` all heads of one
+    // group share an XCD, so the group's B tiles are fetched into one L2
+    int grp, minor;
+    xcd_split(blockIdx.x, (int)(gridDim.x / ng), xcd != 0, grp, minor);
+    const int ntiles = N / NR, bh = minor / ntiles, n0 = (minor % ntiles) * NR;
     const int c0 = grp * K, c1 = min(c0 + K, nc);
+    const int U = (c1 - c0) * NSUB;                               // sub-steps of this group
     const int b = bh / H, h = bh % H, g = h / (H / G);
-    const int n_wave = nt * NT + nh * 32;            // first state column of this wave's rows
-    const int p_col = ph * 32 + (lane & 31);          // this lane's p
-    const int n_lane = n_wave + 4 * (lane >> 5);      // + 8q + r for accumulator element 4q + r
+    const int rt0 = (wave / (2 / CTW)) * RTW, ct0 = (wave % (2 / CTW)) * CTW;
     const int64_t st_off = (int64_t)bh * P * N;
     const float *Gh = G2 + (int64_t)bh * Lp;
     const float *wh = wT + (int64_t)bh * Lp;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
-    const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + nt * NT;
-    const bool keeper = nt == 0 && tid == 0;          // writes beta / gamma of this group
+    const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + n0;
+    const bool keeper = tid == 0 && n0 == 0;   // writes beta / gamma of this group
 
-    f32x16 acc = zero_acc();
-    if (h0 != nullptr && kh == 0 && grp == 0) {
+    // accumulator element v of tile (i, j): row n = 32 (rt0 + i) + acc_row(v, lane),
+    // column p = 32 (ct0 + j) + lane % 32
+    f32x16 acc[RTW][CTW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(h0 + st_off + (int64_t)p_col * N + n_lane + 8 * q);
+    for (int i = 0; i < RTW; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[4 * q + r] = v[r];
-        }
-    }
-
-    // staging assignments: x piece r of this thread is token (tid + NTHR r) / 8,
-    // p octet (tid + NTHR r) % 8; the B block is token group wtg, column group wcg
-    int xo[XPC];
+        for (int j = 0; j < CTW; ++j) acc[i][j] = zero_acc();
+    if (h0 != nullptr && grp == 0) {
 #pragma unroll
-    for (int r = 0; r < XPC; ++r) {
-        const int id = tid + NTHR * r;
-        xo[r] = (id >> 3) * (int)xstride + (id & 7) * 8;
-    }
-    const int wtg = tid / (NT / WC), wcg = tid % (NT / WC);
-    const int bo = wtg * 8 * (int)bstride + wcg * WC;
-
-    struct Stage {
-        bf16x8 xr[XPC];
-        uint32_t br[8][WD];
-        f32x4 w[2];
-        float glast;
-    };
-    auto load_b_row = [&](uint32_t *dst, const bf16 *src) {
-        if constexpr (WC == 8) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
-            dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
-        } else if constexpr (WC == 4) {
-            const u32x2 v = *reinterpret_cast<const u32x2 *>(src);
-            dst[0] = v[0]; dst[1] = v[1];
-        } else if constexpr (WC == 2) {
-            dst[0] = *reinterpret_cast<const uint32_t *>(src);
-        } else {
-            dst[0] = *reinterpret_cast<const uint16_t *>(src);
-        }
-    };
-    auto issue = [&](Stage &st, int c) {
-        const int t0 = c * Q;
-        const bf16 *xc = xb + (int64_t)t0 * xstride;
-        const bf16 *bc = Bb + (int64_t)t0 * bstride + bo;
-        if (t0 + Q <= L) {   // full chunk (uniform): no per-lane predication
+        for (int i = 0; i < RTW; ++i)
 #pragma unroll
-            for (int r = 0; r < XPC; ++r) st.xr[r] = ld16(xc + xo[r]);
+            for (int j = 0; j < CTW; ++j) {
+                const int p = 32 * (ct0 + j) + (lane & 31), n = n0 + 32 * (rt0 + i) + 4 * (lane >> 5);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) load_b_row(st.br[r], bc + r * (int)bstride);
-        } else {             // ragged last chunk: rows past L read as zero
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(h0 + st_off + (int64_t)p * N + n + 8 * q);
 #pragma unroll
-            for (int r = 0; r < XPC; ++r) {
-                const int t = (tid + NTHR * r) >> 3;
-                st.xr[r] = (t0 + t < L) ? ld16(xc + xo[r]) : zero8();
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                if (t0 + wtg * 8 + r < L) {
-                    load_b_row(st.br[r], bc + r * (int)bstride);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < WD; ++k) st.br[r][k] = 0u;
+                    for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = v[r];
                 }
             }
-        }
-        const f32x4 *wp = reinterpret_cast<const f32x4 *>(wh + t0 + wtg * 8);
-        st.w[0] = wp[0];
-        st.w[1] = wp[1];
-        st.glast = Gh[t0 + Q - 1];
+    }
+
+    // ---- staging: sub-step u covers tokens t0(u) .. t0(u) + TS of chunk c0 + u / NSUB.
+    // Rows past L are clamped to row L-1 instead of zeroed: their weight w is 0 (stage
+    // 1 writes zeros there), so their x~ rows are 0 and they add nothing.  Every
+    // load is issued unconditionally, which keeps the loop body free of branches
+    // around memory operations and lets the wait counts leave later sub-steps in
+    // flight.
+    // Global offsets are 32-bit byte offsets from the batch's base pointer (the
+    // host checks that one batch of x and of B spans less than 2^31 bytes), so
+    // the loads use a scalar base plus one vector register.
+    int bo[BPT], blo[BPT], bt_[BPT], xo[XPT], xlo[XPT], xt_[XPT];
+#pragma unroll
+    for (int r = 0; r < BPT; ++r) {
+        const int id = tid + NTHR * r, t = id / (NR / 8), c8 = id % (NR / 8);
+        bo[r] = c8 * 16;
+        bt_[r] = t;
+        blo[r] = t * BP + c8 * 8;
+    }
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) {
+        const int id = min(tid + NTHR * r, XPIECES - 1), t = id >> 3, c8 = id & 7;
+        xo[r] = c8 * 16;
+        xt_[r] = t;
+        xlo[r] = t * XRP + c8 * 8;
+    }
+    const char *Bbytes = reinterpret_cast<const char *>(Bb);
+    const char *xbytes = reinterpret_cast<const char *>(xb);
+    const int brow = (int)bstride * 2, xrow = (int)xstride * 2;
+    // x~ k-packing: 16-lane group j transpose-reads tokens 4 tb .. 4 tb + 3 of p
+    // block pb (16 p) of the scaled token-major tile; lane m of the group gets
+    // those 4 tokens of p = 16 pb + m and writes them k-packed.  The groups of one
+    // wave take consecutive token blocks so their 8-byte writes land in distinct
+    // banks.
+    const int m16 = lane & 15;
+    int tbv[TRL], pbv[TRL];
+#pragma unroll
+    for (int r = 0; r < TRL; ++r) {
+        const int gr = (lane >> 4) + 4 * wave + 4 * C::NWAVE * r;
+        tbv[r] = gr % (TS / 4);
+        pbv[r] = gr / (TS / 4);
+    }
+    struct Regs {
+        bf16x8 b[BPT];
+        bf16x8 x[XPT];
+        float w[XPT];   // weight of the token of x piece r
+        float gl;
     };
-    auto commit = [&](const Stage &st) {
+    const int last_row = L - 1;
+    auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
+    auto load = [&](Regs &R, int u) {
+        u = min(u, U - 1);
+        const int t0 = tok0(u);
 #pragma unroll
-        for (int r = 0; r < XPC; ++r) {
-            const int id = tid + NTHR * r;
-            *reinterpret_cast<bf16x8 *>(&Xs[(id >> 3) * XP + (id & 7) * 8]) = st.xr[r];
+        for (int r = 0; r < BPT; ++r) {
+            const uint32_t off = (uint32_t)(min(t0 + bt_[r], last_row) * brow + bo[r]);
+            R.b[r] = *reinterpret_cast<const bf16x8 *>(Bbytes + off);
         }
-        // W: scale token row r by w_r, then pack the pair (2k, 2k+1) of column j
 #pragma unroll
-        for (int j = 0; j < WC; ++j) {
+        for (int r = 0; r < XPT; ++r) {
+            const uint32_t off = (uint32_t)(min(t0 + xt_[r], last_row) * xrow + xo[r]);
+            R.x[r] = *reinterpret_cast<const bf16x8 *>(xbytes + off);
+        }
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) R.w[r] = wh[t0 + xt_[r]];
+        // the chunk's last cumsum value, as a per-lane load (a scalar load would
+        // share the LDS wait counter and stall every LDS wait behind it)
+        int gi = (c0 + u / NSUB) * Q + Q - 1;
+        asm volatile("" : "+v"(gi));
+        R.gl = Gh[gi];
+    };
+    // LDS buffer indices are passed in as compile-time constants
+    auto storeB = [&](const Regs &R, int kb) {
+#pragma unroll
+        for (int r = 0; r < BPT; ++r) *reinterpret_cast<bf16x8 *>(&Bs[kb][blo[r]]) = R.b[r];
+    };
+    auto storeX = [&](const Regs &R, int kx, int ka) {
+        // x~ = round(w_t x_t), token-major
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            const u32x4 xv = __builtin_bit_cast(u32x4, R.x[r]);
             u32x4 o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t a = st.br[2 * k][j >> 1], bb = st.br[2 * k + 1][j >> 1];
-                const float fa = (j & 1) ? bf_hi(a) : bf_lo(a);
-                const float fb = (j & 1) ? bf_hi(bb) : bf_lo(bb);
-                const float wa = st.w[k >> 1][2 * (k & 1)], wb = st.w[k >> 1][2 * (k & 1) + 1];
-                o[k] = pack_bf16(fa * wa, fb * wb);
-            }
-            *reinterpret_cast<u32x4 *>(&WT[(wcg * WC + j) * PT + wtg * 8]) = o;
+            for (int k2 = 0; k2 < 4; ++k2) o[k2] = pack_bf16(bf_lo(xv[k2]) * R.w[r], bf_hi(xv[k2]) * R.w[r]);
+            if (XPT * NTHR == XPIECES || tid + NTHR * r < XPIECES)
+                *reinterpret_cast<u32x4 *>(&Xr[kx][xlo[r]]) = o;
         }
-        if (tid == 0) alph = fast_exp2(st.glast);
+        Al[ka] = fast_exp2(R.gl);   // same value from every thread
     };
-
-    const int offW = (nh * 32 + (lane & 31)) * PT + 8 * (lane >> 5) + kh * (Q / KS);
-    const int offX = tr_off_natural(lane, XP) + ph * 32 + kh * (Q / KS) * XP;
-    float run = 1.0f;   // decay product since the group start (keeper thread)
-
-    // One chunk: refill `refill` with chunk c+2, store the chunk-start state,
-    // decay and accumulate chunk c from LDS, then (after everyone has read the
-    // tile) write chunk c+1 from `next` into LDS and fold the K-halves.  Loads
-    // and commits are unconditional (indices clamped to the group's last chunk;
-    // the extra copies are never used) so the wait counts let the c+2 loads stay
-    // in flight across the commit.
-    auto step = [&](int c, const Stage &next, Stage &refill) {
-        issue(refill, min(c + 2, c1 - 1));
-        if (kh == 0) {
-            bf16 *Sc = S + ((int64_t)bh * nc + c) * P * N + (int64_t)p_col * N + n_lane;
+    auto build = [&](int k, int kx) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bf16x4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[4 * q + r];
-                *reinterpret_cast<bf16x4 *>(Sc + 8 * q) = o;
-            }
-        }
-        const float a = alph;
-        if (keeper && beta != nullptr) {
-            beta[(int64_t)bh * nc + c] = run;
-            run *= a;
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] *= a;
-
-        const bf16 *wt = WT + offW;
-        const bf16 *xt = Xs + offX;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 bf = cat8(tr_read4(xt + ks * 16 * XP), tr_read4(xt + (ks * 16 + 4) * XP));
-            mma(acc, ld16(wt + ks * 16), bf);
-        }
-        __syncthreads();   // tile of chunk c consumed
-        if constexpr (KS > 1) {
-            if (kh == 1) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) red[((wave - 2 * NWN) * 16 + v) * 64 + lane] = acc[v];
-            }
-        }
-        commit(next);
-        __syncthreads();   // tile of chunk c+1 and the partial states visible
-        if constexpr (KS > 1) {
-            if (kh == 0) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] += red[(wave * 16 + v) * 64 + lane];
-            } else {
-                acc = zero_acc();
-            }
+        for (int r = 0; r < TRL; ++r) {
+            const int tb = tbv[r], pb = pbv[r];
+            const bf16x4 v = tr_read4(&Xr[k][(4 * tb + (m16 >> 2)) * XRP + 16 * pb + 4 * (m16 & 3)]);
+            *reinterpret_cast<bf16x4 *>(&Xk[kx][(16 * pb + m16) * XKP + 4 * tb]) = v;
         }
     };
 
-    Stage sa, sb;
-    issue(sa, c0);
-    issue(sb, min(c0 + 1, c1 - 1));
-    commit(sa);
+    const int offA = tr_off_natural(lane, BP);
+    const int offB = (lane & 31) * XKP + 8 * (lane >> 5);
+
+    // chunk start (sub-step u, u % NSUB == 0): store the chunk-start state, decay
+    // chunk start (sub-step u, u % NSUB == 0): the chunk-start state goes to the
+    // LDS staging tile as bf16 (row p, columns n), then the state decays
+    auto chunk_start = [&](int ka) {
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+#pragma unroll
+            for (int j = 0; j < CTW; ++j) {
+                const int p = 32 * (ct0 + j) + (lane & 31), n = 32 * (rt0 + i) + 4 * (lane >> 5);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[i][j][4 * q + r];
+                    *reinterpret_cast<bf16x4 *>(&Ss[p * SSP + n + 8 * q]) = o;
+                }
+            }
+        const float a = Al[ka];
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+#pragma unroll
+            for (int j = 0; j < CTW; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] *= a;
+    };
+    // the staged state of chunk c to HBM: thread piece r is row p, 8 columns;
+    // consecutive lanes cover consecutive 16 bytes of a row
+    auto state_out = [&](int c) {
+        char *Sc = reinterpret_cast<char *>(S + ((int64_t)bh * nc + c) * P * N + n0);
+#pragma unroll
+        for (int r = 0; r < SPT; ++r) {
+            const int id = tid + NTHR * r, p = id / (NR / 8), c8 = id % (NR / 8);
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&Ss[p * SSP + 8 * c8]);
+            *reinterpret_cast<bf16x8 *>(Sc + (uint32_t)((p * N + 8 * c8) * 2)) = v;
+        }
+    };
+    auto mma_sub = [&](int kb, int kx) {
+        const bf16 *bt = &Bs[kb][offA];
+        const bf16 *xt = &Xk[kx][offB];
+#pragma unroll
+        for (int ks = 0; ks < TS / 16; ++ks) {
+            bf16x8 bfr[CTW];
+#pragma unroll
+            for (int j = 0; j < CTW; ++j) bfr[j] = ld16(xt + 32 * (ct0 + j) * XKP + 16 * ks);
+#pragma unroll
+            for (int i = 0; i < RTW; ++i) {
+                const bf16 *a0 = bt + 16 * ks * BP + 32 * (rt0 + i);
+                const bf16x8 af = cat8(tr_read4(a0), tr_read4(a0 + 4 * BP));
+#pragma unroll
+                for (int j = 0; j < CTW; ++j) mma(acc[i][j], af, bfr[j]);
+            }
+        }
+    };
+
+    // Register ring of D sub-steps: sub-step u sits in R[u % D] from its load
+    // (step u - 1 - D) until its B tile is copied (step u - 1); its x~ is copied
+    // one step earlier (step u - 2).
+    static_assert(D >= 2, "a ring slot holds one sub-step from x~ copy to B copy");
+    Regs R[D];
+    // step s, with j = s mod UNR a compile-time constant
+    // The products of sub-step s come first so that the copies for later
+    // sub-steps (independent buffers) can issue while the MFMAs run.
+    auto step = [&](int s, int j) {
+        if (j % NSUB == 0) {
+            if constexpr (NSUB == 1) {   // the previous chunk's staged state leaves first
+                if (s > 0) state_out(c0 + s - 1);
+                __syncthreads();
+            }
+            chunk_start(j & 3);
+        }
+        mma_sub(j & 1, j & 1);
+        storeB(R[(j + 1) % D], (j + 1) & 1);
+        storeX(R[(j + 2) % D], (j + 2) & 1, (j + 2) & 3);
+        load(R[(j + 1) % D], s + 1 + D);
+        if (NSUB > 1 && j % NSUB == 1) state_out(c0 + s / NSUB);
+        build((j + 1) & 1, (j + 1) & 1);
+        __syncthreads();
+    };
+
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(R[u], u);
+    storeX(R[0], 0, 0);
+    storeB(R[0], 0);
+    load(R[0], D);
+    storeX(R[1 % D], 1, 1);
     __syncthreads();
-    int c = c0;
-    for (; c + 1 < c1; c += 2) {
-        step(c, sb, sa);
-        step(c + 1, sa, sb);
+    build(0, 0);
+    __syncthreads();
+    // The body covers UNR = lcm(NSUB, D, 4) sub-steps so that ring slots, LDS
+    // buffers and chunk-start positions are compile-time constants.
+    constexpr int UNR = lcm3(NSUB, D, 4);
+    int s = 0;
+    for (; s + UNR <= U; s += UNR) {
+#pragma unroll
+        for (int j = 0; j < UNR; ++j) step(s + j, j);
     }
-    if (c < c1) step(c, sb, sa);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+        if (s + j < U) step(s + j, j);
+    // with one sub-step per chunk the last chunk's staged state is still in LDS
+    if constexpr (NSUB == 1) state_out(c1 - 1);
 
-    // acc (kh = 0 waves) now holds the state after the group's last chunk
-    float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : hT;
-    if (dst != nullptr && (Ug != nullptr || hT != nullptr) && kh == 0) {
-        const int64_t off = (Ug != nullptr) ? 0 : st_off;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f32x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = acc[4 * q + r];
-            *reinterpret_cast<f32x4 *>(dst + off + (int64_t)p_col * N + n_lane + 8 * q) = o;
+    // decay products of the group (beta_c before each chunk, gamma for the group)
+    if (keeper) {
+        float run = 1.0f;
+        for (int c = c0; c < c1; ++c) {
+            if (beta != nullptr) beta[(int64_t)bh * nc + c] = run;
+            run *= fast_exp2(Gh[c * Q + Q - 1]);
         }
+        if (gam != nullptr) gam[(int64_t)bh * ng + grp] = run;
     }
-    if (keeper && gam != nullptr) gam[(int64_t)bh * ng + grp] = run;
+
+    // the state after the group's last chunk
+    float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : (hT ? hT + st_off : nullptr);
+    if (dst != nullptr) {
+#pragma unroll
+        for (int i = 0; i < RTW; ++i)
+#pragma unroll
+            for (int j = 0; j < CTW; ++j) {
+                const int p = 32 * (ct0 + j) + (lane & 31), n = n0 + 32 * (rt0 + i) + 4 * (lane >> 5);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = acc[i][j][4 * q + r];
+                    *reinterpret_cast<f32x4 *>(dst + (int64_t)p * N + n + 8 * q) = o;
+                }
+            }
+    }
 }
 
 // ===========================================================================
@@ -592,20 +703,36 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
 // ===========================================================================
 // Launchers
 // ===========================================================================
-template <int Q>
+// register ring depth of the state pass (sub-steps in flight)
+constexpr int kSpDepth = 2;
+
+template <int Q, int NR>
 static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
                             const float *wT, const float *h0, void *S, float *hT, float *Ug,
                             float *gam, float *beta, int K, int ng, hipStream_t st)
 {
-    constexpr int NT = 32, KS = 2;
-    const int ntiles = (int)(s.N / NT);
-    const int bH = (int)(s.b * s.H);
-    const int xcd = (bH % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NT, KS>), dim3((unsigned)(bH * ntiles * ng)),
-                       dim3(64 * 2 * (NT / 32) * KS), 0, st, (const bf16 *)x, (const bf16 *)B, G2,
-                       wT, h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G,
-                       (int)s.N, (int)s.nc, (int)s.Lp, ntiles, K, ng, xcd);
+    const int units = (int)(s.b * s.H * (s.N / NR));
+    const int xcd = (ng % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NR, kSpDepth>), dim3((unsigned)(units * ng)),
+                       dim3(SpCfg<Q, NR>::NTHR), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT,
+                       h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
+                       (int)s.nc, (int)s.Lp, K, ng, xcd);
     return hipGetLastError();
+}
+
+// columns per state-pass workgroup: the largest of 256, 128, 64 dividing N
+static int sp_cols(const Shape &s) { return (s.N % 256 == 0) ? 256 : (s.N % 128 == 0) ? 128 : 64; }
+
+template <int Q>
+static hipError_t sp_dispatch_q(const Shape &s, const void *x, const void *B, const float *G2,
+                                const float *wT, const float *h0, void *S, float *hT, float *Ug,
+                                float *gam, float *beta, int K, int ng, hipStream_t st)
+{
+    switch (sp_cols(s)) {
+    case 256: return sp_launch<Q, 256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_launch<Q, 128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_launch<Q, 64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    }
 }
 
 static hipError_t sp_dispatch(const Shape &s, const void *x, const void *B, const float *G2,
@@ -613,9 +740,9 @@ static hipError_t sp_dispatch(const Shape &s, const void *x, const void *B, cons
                               float *gam, float *beta, int K, int ng, hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return sp_launch<64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return sp_launch<128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return sp_launch<256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 64: return sp_dispatch_q<64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_dispatch_q<128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_dispatch_q<256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
@@ -634,11 +761,10 @@ Grouping state_pass_groups(const Shape &s)
         gp.ng = 1;
         return gp;
     }
-    // aim for about four state-pass workgroups per CU (two are resident at a
-    // time) while keeping at least two chunks per group
-    const int64_t units = s.b * s.H * (s.N / 32);
-    int64_t ng = (1024 + units - 1) / units;
-    ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc / 2));
+    // about one state-pass workgroup per CU (each takes most of a CU's LDS)
+    const int64_t units = s.b * s.H * (s.N / sp_cols(s));
+    int64_t ng = (256 + units - 1) / units;
+    ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc));
     const int64_t K = (s.nc + ng - 1) / ng;
     gp.K = (int)K;
     gp.ng = (int)((s.nc + K - 1) / K);
