@@ -50,7 +50,7 @@ ssd::Shape make_shape(const ssd_problem *p)
 }
 
 struct Layout {
-    size_t g2, dtt, wt, S, ug, gam, beta, total;
+    size_t g2, dtt, wt, S, ug, gam, beta, hb, total;
     ssd::Grouping gp;
 };
 
@@ -72,7 +72,8 @@ Layout layout_of(const ssd::Shape &s)
     l.ug = l.S + align_up(snap);
     l.gam = l.ug + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * sizeof(float)) : 0);
     l.beta = l.gam + (grouped ? align_up(bh * l.gp.ng * sizeof(float)) : 0);
-    l.total = l.beta + (grouped ? align_up(bh * s.nc * sizeof(float)) : 0);
+    l.hb = l.beta + (grouped ? align_up(bh * s.nc * sizeof(float)) : 0);
+    l.total = l.hb + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * 2) : 0);
     return l;
 }
 
@@ -162,6 +163,7 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     float *Ug = reinterpret_cast<float *>(ws + l.ug);
     float *gam = reinterpret_cast<float *>(ws + l.gam);
     float *beta = reinterpret_cast<float *>(ws + l.beta);
+    void *Hb = ws + l.hb;
     hipStream_t hs = (hipStream_t)stream;
     auto mark = [&](int i) -> ssd_status {
         return events ? hip_status(hipEventRecord((hipEvent_t)events[i], hs)) : SSD_OK;
@@ -171,12 +173,12 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     if (r == SSD_OK) r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
     if (r == SSD_OK) r = mark(1);
     if (r == SSD_OK)
-        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam,
-                                                      beta, hs));
+        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, Hb,
+                                                      gam, beta, hs));
     if (r == SSD_OK) r = mark(2);
     if (r == SSD_OK)
         r = hip_status(
-            ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, beta, hs));
+            ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, Hb, beta, hs));
     if (r == SSD_OK) r = mark(3);
     return r;
 }

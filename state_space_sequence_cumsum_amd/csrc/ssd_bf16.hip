@@ -11,6 +11,7 @@
 // the gfx950 LDS transpose read (ds_read_b64_tr_b16), so no element-wise
 // transposition happens on the way in.
 #include <algorithm>
+#include <type_traits>
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -404,20 +405,29 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
 // ===========================================================================
 // Group scan.  For each (batch*head, state element): walk the groups in order,
 // H_1 = U_0 and H_{g+1} = gamma_g H_g + U_g; H_g (the true state at group g's
-// start) replaces U_g in place, and the state after the last group is hT.
+// start) replaces U_g in place (g >= 1), a bf16 copy goes to Hb (zeros for
+// group 0, which needs no correction), and the state after the last group is hT.
 // ===========================================================================
 __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
                                                          const float *__restrict__ gam,
-                                                         float *__restrict__ hT, int PN, int ng)
+                                                         float *__restrict__ hT,
+                                                         bf16 *__restrict__ Hb, int PN, int ng)
 {
     const int bh = blockIdx.y;
     const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
     f32x4 hcar = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int g = 0; g < ng; ++g) {
-        f32x4 *u = reinterpret_cast<f32x4 *>(Ug + ((int64_t)bh * ng + g) * PN + e);
+        const int64_t off = ((int64_t)bh * ng + g) * PN + e;
+        f32x4 *u = reinterpret_cast<f32x4 *>(Ug + off);
         const f32x4 v = *u;
         if (g > 0) *u = hcar;
+        if (Hb != nullptr) {
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (bf16)hcar[r];   // zero for g == 0
+            *reinterpret_cast<bf16x4 *>(Hb + off) = o;
+        }
         const float gm = gam[(int64_t)bh * ng + g];
 #pragma unroll
         for (int r = 0; r < 4; ++r) hcar[r] = gm * hcar[r] + v[r];
@@ -430,15 +440,17 @@ __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
 // owns one 32-token row tile I = rowtile(w).  Waves w and w + Q/64 (which the
 // hardware places on the same SIMD) get tiles that add up to Q/32 - 1, so every
 // SIMD does the same number, Q/32 + 1, of causal tile pairs (J, I), J <= I.
-// Two waves per SIMD let one wave's loads, barriers and exponentials overlap
-// the other's matrix products.  The output is built transposed, Y^T [64 p x 32
-// tokens] per row tile.
+// The output is built transposed, Y^T [64 p x 32 tokens] per row tile.
 //
-// Phase 1 streams N in slices of 64: the slice of B (all chunk rows) and of S
-// (all p) is staged in LDS, the wave's C rows come from global memory, and the
-// next slice is loaded into registers while the current one is multiplied:
+// Prologue: the (dt x)^T tile, the chunk's decays and the chunk-start state
+// S_eff [64 x N] (bf16, whole width) go to LDS; these per-item loads are all
+// issued together so their latencies overlap.
+// Phase 1 streams N in slices of 64: the slice of B (all chunk rows) is staged
+// in LDS, the wave's C rows come from global memory, and the next slice is
+// loaded while the current one is multiplied (B and C are shared by all heads
+// of the chunk, so these loads mostly hit L2):
 //   * CB_J = (B C^T)[tile J, tile I] for J <= I (accumulators indexed by J);
-//   * Y^T += S C^T (the inter-chunk term).
+//   * Y^T += S_eff C^T (the inter-chunk term).
 // Phase 2, per J <= I: the C B^T tile becomes the decay matrix
 //   M[j, i] = (i >= j) ? CB[j, i] * exp2(G_i - G_j) : 0      (selection, never a product with a mask)
 // rounded to bf16 and fed to MFMA straight from registers against (dt x)^T.
@@ -447,22 +459,32 @@ __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
 // <= 1, the second a per-token table, so such a tile costs one exp2 per lane.
 // The Y^T accumulator is scaled by exp2(G_i) between the two phases.
 //
-// Chunk-start state handed over by a grouped state pass (Hg != NULL): S holds
-// the state relative to the start of the chunk's group, to which beta_c H_g is
-// added while staging (group 0 already started from the true initial state).
+// Chunk-start state handed over by a grouped state pass (CORR): S holds the
+// state relative to the start of the chunk's group and S_eff = S + beta_c H_g
+// (group 0 already started from the true initial state; beta is 0 there, so it
+// reads its group's slot and adds nothing).
+//
+// Rows past L are not zeroed: they are clamped to row L-1.  Their dt is 0 (stage
+// 1 writes zeros there), so their (dt x) rows vanish and the outputs of such
+// rows are never stored.  With no per-lane predicates and no branches around
+// the slice loads, the wait counts keep the next slice in flight while the
+// current one is multiplied.
 // ===========================================================================
-template <int Q>
+constexpr int kMaxN = 512;
+
+template <int Q, bool CORR>
 __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
     const float *__restrict__ D, bf16 *__restrict__ y, const float *__restrict__ Hg,
     const float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng,
-    int xcd)
+    int c_first, int nc_grid, int xcd)
 {
     constexpr int P = 64, NI = Q / 32, NW = Q / 32, NTHR = 2 * Q, NS = 64;
-    constexpr int XP = Q + 8, BP = frag_pitch(NS), SP = frag_pitch(NS);
+    constexpr int XP = Q + 8, BP = frag_pitch(NS);
     constexpr int BPC = Q * (NS / 8) / NTHR;   // 16-byte B pieces per thread per slice
-    constexpr int SPC = P * (NS / 8) / NTHR;   // 16-byte S pieces per thread per slice
+    constexpr int SPC = P * (NS / 8) / NTHR;   // 16-byte S pieces per thread per 64 columns
+    constexpr int SPART = 256;                 // S_eff columns staged per round
     static_assert(BPC >= 1 && SPC >= 1, "slice staging cover");
     // (dt x)^T [p][position]: within each 16-token group the token at offset o is
     // kept at position o with its middle two 4-token blocks swapped, so the
@@ -470,103 +492,125 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     // consecutive positions.
     __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
     __shared__ __attribute__((aligned(16))) bf16 Bs[Q * BP];
-    __shared__ __attribute__((aligned(16))) bf16 Ss[P * SP];
+    // S_eff rows of N + 8 elements: an odd number of 16-byte units, so 16
+    // consecutive rows read at the same column hit 16 distinct bank groups
+    __shared__ __attribute__((aligned(16))) bf16 Sf[P * (kMaxN + 8)];
     __shared__ __attribute__((aligned(16))) float Gs[Q];
     __shared__ __attribute__((aligned(16))) float We[Q];   // exp2(G_e - G_j), e = end of j's tile
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int I = (w < NW / 2) ? w : NW - 1 - (w - NW / 2);
+    const int SFP = N + 8;
 
-    // Workgroup -> (chunk, batch*head), heads innermost.  With `xcd` set (nc a
-    // multiple of 8) XCD x gets the contiguous chunk range [x nc/8, (x+1) nc/8):
-    // a chunk's B and C rows are shared by all its heads and a state-pass group's
-    // carried state by its consecutive chunks, and both then stay in one L2.
-    const int bH = gridDim.x / nc;
+    // Workgroup -> (chunk c_first + k, batch*head), k < nc_grid, heads innermost.
+    // With `xcd` set (nc_grid a multiple of 8) XCD x gets the contiguous chunk
+    // range [x nc_grid/8, (x+1) nc_grid/8): a chunk's B and C rows are shared by
+    // all its heads and a state-pass group's carried state by its consecutive
+    // chunks, and both then stay in one L2.
+    const int bH = gridDim.x / nc_grid;
     int c, bh;
     if (xcd) {
         const int xx = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        c = xx * (nc / 8) + slot / bH;
+        c = xx * (nc_grid / 8) + slot / bH;
         bh = slot % bH;
     } else {
         c = blockIdx.x / bH;
         bh = blockIdx.x % bH;
     }
+    c += c_first;
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int t0 = c * Q;
-    const bool full = t0 + Q <= L;
+    const int nvalid = min(Q, L - t0);          // rows of this chunk inside the sequence
     const int64_t xstride = (int64_t)H * P, cstride = (int64_t)G * N;
     const bf16 *xb = x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
-    const bf16 *Bb = Bm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N;
-    const bf16 *Cb = Cm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N;
-    const bf16 *Sb = S + ((int64_t)bh * nc + c) * P * N;
+    const char *Bb = reinterpret_cast<const char *>(Bm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
+    const char *Cb = reinterpret_cast<const char *>(Cm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
+    const char *Sb = reinterpret_cast<const char *>(S + ((int64_t)bh * nc + c) * P * N);
     const float *Gh = G2 + (int64_t)bh * Lp + t0;
     const float *dh = dtT + (int64_t)bh * Lp + t0;
     const int kq = 8 * (lane >> 5);
-    const int cgrp = (Hg != nullptr) ? c / K : 0;
-    const float *Hc = (cgrp > 0) ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr;
-    const float bc = (cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
+    const int cgrp = CORR ? c / K : 0;
+    const char *Hc = reinterpret_cast<const char *>(CORR ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr);
+    const float bc = (CORR && cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
 
     const int i_loc = I * 32 + (lane & 31);
-    const bool iv = full || t0 + i_loc < L;
-    const bf16 *crow = Cb + i_loc * (int)cstride + kq;
+    const bool iv = i_loc < nvalid;
+    const int crow_off = min(i_loc, nvalid - 1) * (int)cstride * 2 + kq * 2;   // bytes
+    const int brow = (int)cstride * 2;
 
-    // registers holding the next N slice while the current one is multiplied
-    bf16x8 bq[BPC], sq[SPC], cn[NS / 16];
-    f32x4 hq[SPC][2];
+    // ---- slice registers: the next B / C slice while the current one is multiplied
+    bf16x8 bq[BPC], cn[NS / 16];
+    int bo[BPC];
+#pragma unroll
+    for (int r = 0; r < BPC; ++r) {
+        const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
+        bo[r] = min(t, nvalid - 1) * brow + oct * 16;
+    }
     auto load_slice = [&](int n0) {
-        if (full) {   // uniform: no per-lane predication
 #pragma unroll
-            for (int r = 0; r < BPC; ++r) {
-                const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-                bq[r] = ld16(Bb + t * (int)cstride + n0 + oct * 8);
-            }
+        for (int r = 0; r < BPC; ++r) bq[r] = *reinterpret_cast<const bf16x8 *>(Bb + (uint32_t)(bo[r] + n0 * 2));
 #pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) cn[ks] = ld16(crow + n0 + ks * 16);
-        } else {
-#pragma unroll
-            for (int r = 0; r < BPC; ++r) {
-                const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
-                bq[r] = (t0 + t < L) ? ld16(Bb + t * (int)cstride + n0 + oct * 8) : zero8();
-            }
-#pragma unroll
-            for (int ks = 0; ks < NS / 16; ++ks) cn[ks] = iv ? ld16(crow + n0 + ks * 16) : zero8();
-        }
-#pragma unroll
-        for (int r = 0; r < SPC; ++r) {
-            const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
-            sq[r] = ld16(Sb + p * N + n0 + oct * 8);
-            if (Hc != nullptr) {
-                hq[r][0] = *reinterpret_cast<const f32x4 *>(Hc + p * N + n0 + oct * 8);
-                hq[r][1] = *reinterpret_cast<const f32x4 *>(Hc + p * N + n0 + oct * 8 + 4);
-            }
-        }
+        for (int ks = 0; ks < NS / 16; ++ks)
+            cn[ks] = *reinterpret_cast<const bf16x8 *>(Cb + (uint32_t)(crow_off + (n0 + ks * 16) * 2));
     };
 
-    // (dt x)^T tile and the chunk's decays; the first N slice is requested right
-    // behind the x tile so both latencies overlap.  Thread = one 8-token x 4-p
-    // block: rows loaded token-major, scaled by dt, packed per p column.  A wave
-    // covers 8 token groups (lane % 8) x 8 column groups (lane / 8).
+    // ---- S_eff staging: piece r of 64-column block q is row p, 8 columns
+    auto s_piece = [&](int r) { return tid + NTHR * r; };
+    auto stage_state = [&](int nb) {   // columns [nb, nb + SPART) (those below N)
+        bf16x8 sq[SPART / 64][SPC];
+        f32x4 hq[SPART / 64][SPC][2];
+#pragma unroll
+        for (int q = 0; q < SPART / 64; ++q) {
+            if (nb + 64 * q < N) {
+#pragma unroll
+                for (int r = 0; r < SPC; ++r) {
+                    const int id = s_piece(r), p = id >> 3, col = nb + 64 * q + (id & 7) * 8;
+                    sq[q][r] = *reinterpret_cast<const bf16x8 *>(Sb + (uint32_t)((p * N + col) * 2));
+                    if constexpr (CORR) {
+                        hq[q][r][0] = *reinterpret_cast<const f32x4 *>(Hc + (uint32_t)((p * N + col) * 4));
+                        hq[q][r][1] = *reinterpret_cast<const f32x4 *>(Hc + (uint32_t)((p * N + col) * 4 + 16));
+                    }
+                }
+            }
+        }
+        return [&, nb, sq, hq]() {
+#pragma unroll
+            for (int q = 0; q < SPART / 64; ++q) {
+                if (nb + 64 * q < N) {
+#pragma unroll
+                    for (int r = 0; r < SPC; ++r) {
+                        const int id = s_piece(r), p = id >> 3, col = nb + 64 * q + (id & 7) * 8;
+                        bf16x8 sv = sq[q][r];
+                        if constexpr (CORR) {
+#pragma unroll
+                            for (int e2 = 0; e2 < 8; ++e2)
+                                sv[e2] = (bf16)((float)sv[e2] + bc * hq[q][r][e2 >> 2][e2 & 3]);
+                        }
+                        *reinterpret_cast<bf16x8 *>(&Sf[p * SFP + col]) = sv;
+                    }
+                }
+            }
+        };
+    };
+
+    // (dt x)^T tile and the chunk's decays; the chunk-start state and the first
+    // N slice are requested right behind the x tile so all latencies overlap.
+    // Thread = one 8-token x 4-p block: rows loaded token-major, scaled by dt,
+    // packed per p column.  A wave covers 8 token groups (lane % 8) x 8 column
+    // groups (lane / 8).
     {
         const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + (lane >> 3);
+        const char *xbb = reinterpret_cast<const char *>(xb);
         u32x2 xv[8];
-        if (full) {
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                xv[r] = *reinterpret_cast<const u32x2 *>(xb + (tg * 8 + r) * (int)xstride + cg * 4);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                xv[r] = (t0 + tg * 8 + r < L)
-                            ? *reinterpret_cast<const u32x2 *>(xb + (tg * 8 + r) * (int)xstride + cg * 4)
-                            : u32x2{0u, 0u};
-        }
+        for (int r = 0; r < 8; ++r)
+            xv[r] = *reinterpret_cast<const u32x2 *>(
+                xbb + (uint32_t)((min(tg * 8 + r, nvalid - 1) * (int)xstride + cg * 4) * 2));
         const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dh + tg * 8);
         const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dh + tg * 8 + 4);
-        float gt = 0.0f, ge = 0.0f;
-        if (tid < Q) {
-            gt = Gh[tid];
-            ge = Gh[tid | 31];
-        }
+        const int tq = tid & (Q - 1);
+        const float gt = Gh[tq], ge = Gh[tq | 31];
+        auto commit0 = stage_state(0);
         load_slice(0);
         const float d[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
         // positions of this block's tokens: 8 tokens at offset 0 or 8 of a 16-group
@@ -592,30 +636,23 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
             Gs[tid] = gt;
             We[tid] = fast_exp2(ge - gt);
         }
+        commit0();
+        for (int nb = SPART; nb < N; nb += SPART) stage_state(nb)();
     }
 
     f32x16 cb[NI];
 #pragma unroll
     for (int J = 0; J < NI; ++J) cb[J] = zero_acc();
     f32x16 ya[2] = {zero_acc(), zero_acc()};
+    const bf16 *sfrow = Sf + (lane & 31) * SFP + kq;
 
-    // ---------------- phase 1: C B^T tiles and S C^T over N slices ----------------
+    // ---------------- phase 1: C B^T tiles and S_eff C^T over N slices ----------------
     for (int n0 = 0; n0 < N; n0 += NS) {
-        __syncthreads();   // previous slice consumed; first time: Xd, Gs, We written
+        __syncthreads();   // previous slice consumed; first time: Xd, Gs, We, Sf written
 #pragma unroll
         for (int r = 0; r < BPC; ++r) {
             const int id = tid + NTHR * r, t = id >> 3, oct = id & 7;
             *reinterpret_cast<bf16x8 *>(&Bs[t * BP + oct * 8]) = bq[r];
-        }
-#pragma unroll
-        for (int r = 0; r < SPC; ++r) {
-            const int id = tid + NTHR * r, p = id >> 3, oct = id & 7;
-            bf16x8 sv = sq[r];
-            if (Hc != nullptr) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sv[e] = (bf16)((float)sv[e] + bc * hq[r][e >> 2][e & 3]);
-            }
-            *reinterpret_cast<bf16x8 *>(&Ss[p * SP + oct * 8]) = sv;
         }
         bf16x8 cf[NS / 16];
 #pragma unroll
@@ -635,7 +672,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
         }
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-            const bf16 *srow = Ss + (pp * 32 + (lane & 31)) * SP + kq;
+            const bf16 *srow = sfrow + pp * 32 * SFP + n0;
 #pragma unroll
             for (int ks = 0; ks < NS / 16; ++ks)
                 mma(ya[pp], *reinterpret_cast<const bf16x8 *>(srow + ks * 16), cf[ks]);
@@ -695,6 +732,328 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pp][4 * q + r] + Dh * (float)xv[r]);
                 *reinterpret_cast<bf16x4 *>(yb + yo + p) = o;
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Chunk output, head-blocked.  C B^T depends only on the chunk and the group,
+// so a workgroup takes one (chunk, batch, group) and a block of HB heads of that
+// group.  It computes the causal C B^T tiles once (fp32 MFMA accumulation),
+// rounds them to bf16 into LDS, keeps the wave's C rows in registers, and then
+// runs the per-head work head after head:
+//   * Y^T = S_eff C^T (inter-chunk term, S_eff = S + beta_c H_g when grouped);
+//   * Y^T = exp2(G_i) Y^T + sum_{j <= i} M'[j, i] x_j with the decay matrix
+//     M'[j, i] = CB[j, i] exp2(G_i - G_j) dt_j, selected on i >= j; the raw x
+//     tile is the MFMA operand and dt_j rides in M' (a per-token table off the
+//     diagonal, one extra product on it);
+//   * y = Y + D x, the raw x read back from the same LDS tile.
+// The next head's x, dt and decays are loaded a whole head ahead and its
+// chunk-start state right after the decay-matrix work.
+//
+// Waves own 32-token row tiles I(w), SIMD-balanced as in the single-head
+// kernel; the output is built transposed, Y^T [64 p x 32 tokens].  The decay
+// matrix tiles J < I use the exact factorization exp2(G_i - G_e) exp2(G_e - G_j),
+// e the last token of tile J (both factors <= 1).
+// Rounding: C B^T is rounded to bf16 once after its fp32 accumulation and the
+// decay matrix again as the MFMA operand; H_g arrives in bf16.
+// Chunks are full (a ragged last chunk is left to the single-head kernel).
+// ===========================================================================
+template <int Q, int NN, bool CORR>
+__global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+    const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
+    const float *__restrict__ D, bf16 *__restrict__ y, const bf16 *__restrict__ Hb,
+    const float *__restrict__ beta, int L, int H, int G, int nc, int Lp, int K, int ng, int HB,
+    int nc_full, int xcd)
+{
+    constexpr int P = 64, NI = Q / 32, NW = Q / 32, NTHR = 2 * Q, NS = 64;
+    constexpr int NSL = (NN + NS - 1) / NS;     // B slices
+    constexpr int NSW = NN < NS ? NN : NS;      // slice width
+    constexpr int NF = NN / 16;                 // C fragments per lane
+    constexpr int XP = Q + 8, BP = frag_pitch(NSW), SFP = NN + 8;
+    constexpr int BPC = Q * (NSW / 8) / NTHR;   // 16-byte B pieces per thread per slice
+    constexpr int SPT = P * (NN / 8) / NTHR;    // 16-byte S pieces per thread
+    static_assert(BPC >= 1 && SPT >= 1 && NN % 16 == 0, "staging cover");
+    constexpr int NTILE = NI * (NI + 1) / 2;    // causal tiles
+    constexpr int CB_EL = NTILE * 32 * 32;      // bf16 C B^T tiles
+    constexpr int U_EL = (Q * BP > CB_EL) ? Q * BP : CB_EL;
+    // raw x^T [p][position] (token order permuted within 16-token groups: the
+    // middle two 4-token blocks swapped, so the accumulator token order of a lane
+    // becomes 8 consecutive positions); Un holds the B slice during C B^T and then
+    // the bf16 C B^T tiles: tile (I, J) at (I(I+1)/2 + J) * 1024 elements, lane l's
+    // elements 0..7 at 8 l and 8..15 at 512 + 8 l
+    __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
+    __shared__ __attribute__((aligned(16))) bf16 Un[U_EL];
+    __shared__ __attribute__((aligned(16))) bf16 Sf[P * SFP];
+    __shared__ __attribute__((aligned(16))) float Gs[Q];
+    __shared__ __attribute__((aligned(16))) float Wd[Q];   // exp2(G_e - G_j) dt_j
+    __shared__ __attribute__((aligned(16))) float Dt[Q];   // dt_j
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int I = (w < NW / 2) ? w : NW - 1 - (w - NW / 2);
+
+    // workgroup -> (chunk, (batch, group, head block)); with `xcd` (nc_full a
+    // multiple of 8) XCD x gets the contiguous chunk range [x nc/8, (x+1) nc/8)
+    const int HPG = H / G, nhb = HPG / HB;
+    const int minors = gridDim.x / nc_full;
+    int c, minor;
+    if (xcd) {
+        const int xx = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        c = xx * (nc_full / 8) + slot / minors;
+        minor = slot % minors;
+    } else {
+        c = blockIdx.x / minors;
+        minor = blockIdx.x % minors;
+    }
+    const int bg = minor / nhb, hblk = minor % nhb;
+    const int b = bg / G, g = bg % G;
+    const int h_first = g * HPG + hblk * HB;
+    const int t0 = c * Q;
+    const int N = NN;
+    const int64_t xstride = (int64_t)H * P, cstride = (int64_t)G * N;
+    const char *Bb = reinterpret_cast<const char *>(Bm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
+    const char *Cb = reinterpret_cast<const char *>(Cm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
+    const int kq = 8 * (lane >> 5);
+    const int i_loc = I * 32 + (lane & 31);
+    const int brow = (int)cstride * 2;
+    bf16 *cbl = Un + (I * (I + 1) / 2) * 1024 + 8 * lane;   // this wave's C B^T tiles
+
+    // ================= C B^T, once per workgroup =================
+    bf16x8 cfa[NF];                // this wave's C rows, all N: fragment f = columns 16 f ..
+    {
+        const int crow_off = i_loc * brow + kq * 2;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+            cfa[f] = *reinterpret_cast<const bf16x8 *>(Cb + (uint32_t)(crow_off + f * 32));
+        int bo[BPC];
+#pragma unroll
+        for (int r = 0; r < BPC; ++r) {
+            const int id = tid + NTHR * r, t = id / (NSW / 8), oc = id % (NSW / 8);
+            bo[r] = t * brow + oc * 16;
+        }
+        bf16x8 bq[BPC];
+        auto load_b = [&](int n0) {
+#pragma unroll
+            for (int r = 0; r < BPC; ++r) bq[r] = *reinterpret_cast<const bf16x8 *>(Bb + (uint32_t)(bo[r] + n0 * 2));
+        };
+        f32x16 cb[NI];
+#pragma unroll
+        for (int J = 0; J < NI; ++J) cb[J] = zero_acc();
+        load_b(0);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+            __syncthreads();   // previous slice consumed
+#pragma unroll
+            for (int r = 0; r < BPC; ++r) {
+                const int id = tid + NTHR * r, t = id / (NSW / 8), oc = id % (NSW / 8);
+                *reinterpret_cast<bf16x8 *>(&Un[t * BP + oc * 8]) = bq[r];
+            }
+            if (sl + 1 < NSL) load_b((sl + 1) * NSW);
+            __syncthreads();
+#pragma unroll
+            for (int J = 0; J < NI; ++J) {
+                if (J <= I) {
+                    const bf16 *brw = Un + (J * 32 + (lane & 31)) * BP + kq;
+#pragma unroll
+                    for (int ks = 0; ks < NSW / 16; ++ks)
+                        mma(cb[J], *reinterpret_cast<const bf16x8 *>(brw + ks * 16), cfa[sl * (NSW / 16) + ks]);
+                }
+            }
+        }
+        __syncthreads();   // the B slice area becomes the C B^T store
+#pragma unroll
+        for (int J = 0; J < NI; ++J) {
+            if (J <= I) {
+                u32x4 lo, hi;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    lo[k2] = pack_bf16(cb[J][2 * k2], cb[J][2 * k2 + 1]);
+                    hi[k2] = pack_bf16(cb[J][8 + 2 * k2], cb[J][9 + 2 * k2]);
+                }
+                *reinterpret_cast<u32x4 *>(cbl + J * 1024) = lo;
+                *reinterpret_cast<u32x4 *>(cbl + J * 1024 + 512) = hi;
+            }
+        }
+    }
+
+    // ================= per-head work =================
+    const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + (lane >> 3);
+    struct XRegs {
+        u32x2 xv[8];
+        float gt, ge, dt;
+    };
+    struct SRegs {
+        bf16x8 sq[SPT];
+        bf16x8 hq[CORR ? SPT : 1];
+        float bc;
+    };
+    const int tq = tid & (Q - 1);
+    auto load_x = [&](XRegs &R, int hl) {
+        hl = min(hl, HB - 1);
+        const int h = h_first + hl, bh = b * H + h;
+        const char *xbb = reinterpret_cast<const char *>(x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            R.xv[r] = *reinterpret_cast<const u32x2 *>(xbb + (uint32_t)(((tg * 8 + r) * (int)xstride + cg * 4) * 2));
+        const float *Gh = G2 + (int64_t)bh * Lp + t0;
+        R.gt = Gh[tq];
+        R.ge = Gh[tq | 31];
+        R.dt = dtT[(int64_t)bh * Lp + t0 + tq];
+    };
+    auto load_s = [&](SRegs &R, int hl) {
+        hl = min(hl, HB - 1);
+        const int h = h_first + hl, bh = b * H + h;
+        const char *Sb = reinterpret_cast<const char *>(S + ((int64_t)bh * nc + c) * P * N);
+#pragma unroll
+        for (int r = 0; r < SPT; ++r) {
+            const int id = tid + NTHR * r, pp = id / (NN / 8), oc = id % (NN / 8);
+            R.sq[r] = *reinterpret_cast<const bf16x8 *>(Sb + (uint32_t)((pp * N + oc * 8) * 2));
+        }
+        if constexpr (CORR) {
+            const int cgrp = c / K;
+            const char *Hc = reinterpret_cast<const char *>(Hb + ((int64_t)bh * ng + cgrp) * P * N);
+#pragma unroll
+            for (int r = 0; r < SPT; ++r) {
+                const int id = tid + NTHR * r, pp = id / (NN / 8), oc = id % (NN / 8);
+                R.hq[r] = *reinterpret_cast<const bf16x8 *>(Hc + (uint32_t)((pp * N + oc * 8) * 2));
+            }
+            int bi = bh * nc + c;
+            asm volatile("" : "+v"(bi));   // per-lane load: keeps it off the scalar path
+            R.bc = beta[bi] * (cgrp > 0 ? 1.0f : 0.0f);
+        } else {
+            R.bc = 0.0f;
+        }
+    };
+    // head registers -> LDS: raw x^T (permuted positions), decay tables, S_eff
+    auto stage_head = [&](const XRegs &R, const SRegs &T) {
+        const int pos0 = (tg >> 1) * 16 + ((tg & 1) ? 4 : 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x2 lo, hi;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                lo[k] = pack_halves(R.xv[2 * k][j >> 1], R.xv[2 * k + 1][j >> 1], j & 1);
+                hi[k] = pack_halves(R.xv[4 + 2 * k][j >> 1], R.xv[5 + 2 * k][j >> 1], j & 1);
+            }
+            bf16 *row = Xd + (cg * 4 + j) * XP + pos0;
+            *reinterpret_cast<u32x2 *>(row) = lo;
+            *reinterpret_cast<u32x2 *>(row + 8) = hi;
+        }
+        if (tid < Q) {
+            Gs[tid] = R.gt;
+            Wd[tid] = fast_exp2(R.ge - R.gt) * R.dt;
+            Dt[tid] = R.dt;
+        }
+#pragma unroll
+        for (int r = 0; r < SPT; ++r) {
+            const int id = tid + NTHR * r, pp = id / (NN / 8), oc = id % (NN / 8);
+            bf16x8 sv = T.sq[r];
+            if constexpr (CORR) {
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) sv[e2] = (bf16)((float)sv[e2] + T.bc * (float)T.hq[r][e2]);
+            }
+            *reinterpret_cast<bf16x8 *>(&Sf[pp * SFP + oc * 8]) = sv;
+        }
+    };
+
+    const int offX = (lane & 31) * XP + 8 * (lane >> 5);
+    const bf16 *sfrow = Sf + (lane & 31) * SFP + kq;
+    // skip-term transpose reads: the addressing lane 4e + k of a 16-lane group
+    // points at row p0 + e and the 4-token block of tokens 4k .. 4k+3 of this
+    // group's 16 tokens, so lane i receives x at its own token for rows p0 .. p0+3
+    const int m16 = lane & 15;
+    const int tok16 = I * 32 + 16 * ((lane >> 4) & 1);           // first token of the group
+    const int blk = m16 & 3;                                       // 4-token block k
+    const int blkpos = (blk == 1) ? 2 : (blk == 2) ? 1 : blk;      // its position block
+    const int skip_off = (m16 >> 2) * XP + tok16 + 4 * blkpos + 4 * (lane >> 5) * XP;
+    XRegs RX;
+    SRegs RS;
+    load_x(RX, 0);
+    load_s(RS, 0);
+    for (int hl = 0; hl < HB; ++hl) {
+        const int h = h_first + hl;
+        __syncthreads();   // the previous head's tiles are consumed (first time: C B^T stored)
+        stage_head(RX, RS);
+        load_x(RX, hl + 1);   // next head (the last one re-requests itself; never used)
+        __syncthreads();
+
+        // inter-chunk term: Y^T = S_eff C^T
+        f32x16 ya[2] = {zero_acc(), zero_acc()};
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+                mma(ya[pp], *reinterpret_cast<const bf16x8 *>(sfrow + pp * 32 * SFP + f * 16), cfa[f]);
+
+        // Y^T = exp2(G_i) Y^T + M' x
+        const float gi = Gs[i_loc];
+        const float si = fast_exp2(gi);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { ya[0][v] *= si; ya[1][v] *= si; }
+        auto mfma_tile = [&](int J, const bf16x8 (&m)[2]) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+                const bf16 *xt = Xd + offX + J * 32 + 16 * sub;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) mma(ya[pp], ld16(xt + pp * 32 * XP), m[sub]);
+            }
+        };
+        for (int J = 0; J < I; ++J) {   // off the diagonal
+            const int jrow = J * 32 + 4 * (lane >> 5);   // + 8q + r for element 4q + r
+            const float ci = fast_exp2(gi - Gs[J * 32 + 31]);
+            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(cbl + J * 1024);
+            const u32x4 c1 = *reinterpret_cast<const u32x4 *>(cbl + J * 1024 + 512);
+            bf16x8 m[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 wd = *reinterpret_cast<const f32x4 *>(&Wd[jrow + 8 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const int v = 4 * q + r;
+                    const uint32_t pr = (v < 8) ? c0[v >> 1] : c1[(v - 8) >> 1];
+                    m[q >> 1][4 * (q & 1) + r] = (bf16)(bf_lo(pr) * wd[r] * ci);
+                    m[q >> 1][4 * (q & 1) + r + 1] = (bf16)(bf_hi(pr) * wd[r + 1] * ci);
+                }
+            }
+            mfma_tile(J, m);
+        }
+        {   // the diagonal tile, selected on i >= j
+            const int jrow = I * 32 + 4 * (lane >> 5);
+            const u32x4 c0 = *reinterpret_cast<const u32x4 *>(cbl + I * 1024);
+            const u32x4 c1 = *reinterpret_cast<const u32x4 *>(cbl + I * 1024 + 512);
+            bf16x8 m[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gs[jrow + 8 * q]);
+                const f32x4 dj = *reinterpret_cast<const f32x4 *>(&Dt[jrow + 8 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int v = 4 * q + r;
+                    const uint32_t pr = (v < 8) ? c0[v >> 1] : c1[(v - 8) >> 1];
+                    const float cbv = (r & 1) ? bf_hi(pr) : bf_lo(pr);
+                    const float val = cbv * fast_exp2(gi - gj[r]) * dj[r];
+                    m[q >> 1][4 * (q & 1) + r] = (bf16)((i_loc >= jrow + 8 * q + r) ? val : 0.0f);
+                }
+            }
+            mfma_tile(I, m);
+        }
+        load_s(RS, hl + 1);   // next head's chunk-start state
+
+        // y = Y + D x
+        const float Dh = D[h];
+        bf16 *yb = y + ((int64_t)b * L + t0 + i_loc) * xstride + (int64_t)h * P;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
+                const bf16x4 xv = tr_read4(Xd + skip_off + (pp * 32 + 8 * q) * XP);
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pp][4 * q + r] + Dh * (float)xv[r]);
+                *reinterpret_cast<bf16x4 *>(yb + p) = o;
             }
         }
     }
@@ -773,15 +1132,15 @@ Grouping state_pass_groups(const Shape &s)
 
 hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
                                      const void *B, const float *G2, const float *wT,
-                                     const float *h0, void *S, float *hT, float *Ug, float *gam,
-                                     float *beta, hipStream_t st)
+                                     const float *h0, void *S, float *hT, float *Ug, void *Hb,
+                                     float *gam, float *beta, hipStream_t st)
 {
     if (!s.bf16 || gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
     hipError_t e = sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st);
     if (e != hipSuccess) return e;
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
-    hipLaunchKernelGGL(group_scan_kernel, grid, dim3(256), 0, st, Ug, gam, hT, PN, gp.ng);
+    hipLaunchKernelGGL(group_scan_kernel, grid, dim3(256), 0, st, Ug, gam, hT, (bf16 *)Hb, PN, gp.ng);
     return hipGetLastError();
 }
 
@@ -789,26 +1148,101 @@ template <int Q>
 static hipError_t co_launch(const Shape &s, const void *x, const void *B, const void *C,
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, const float *Hg, const float *beta, int K, int ng,
+                            int c_first, int nc_grid, hipStream_t st)
+{
+    const int xcd = (nc_grid % 8 == 0) ? 1 : 0;
+    const dim3 grid((unsigned)(nc_grid * s.b * s.H)), block(2 * Q);
+    if (Hg != nullptr)
+        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, true>), grid, block, 0, st, (const bf16 *)x,
+                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
+                           Hg, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp,
+                           K, ng, c_first, nc_grid, xcd);
+    else
+        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, false>), grid, block, 0, st, (const bf16 *)x,
+                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
+                           Hg, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp,
+                           K, ng, c_first, nc_grid, xcd);
+    return hipGetLastError();
+}
+
+// heads per workgroup of the head-blocked chunk output: the largest divisor of
+// the heads per group that still gives at least one workgroup per CU
+static int heads_per_block(const Shape &s)
+{
+    const int hpg = (int)(s.H / s.G);
+    const int64_t units = s.nc * s.b * s.G;
+    int best = 1;
+    for (int hb = 1; hb <= hpg; ++hb)
+        if (hpg % hb == 0 && units * (hpg / hb) >= 256) best = hb;
+    return best;
+}
+
+template <int Q, int NN>
+static hipError_t hb_launch(const Shape &s, const void *x, const void *B, const void *C,
+                            const float *G2, const float *dtT, const void *S, const float *D,
+                            void *y, const void *Hb, const float *beta, int K, int ng, int nc_full,
                             hipStream_t st)
 {
-    const int xcd = (s.nc % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_out_bf16_kernel<Q>), dim3((unsigned)(s.nc * s.b * s.H)), dim3(2 * Q), 0,
-                       st, (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
-                       (const bf16 *)S, D, (bf16 *)y, Hg, beta, (int)s.L, (int)s.H, (int)s.G,
-                       (int)s.N, (int)s.nc, (int)s.Lp, K, ng, xcd);
+    const int HB = heads_per_block(s);
+    const int xcd = (nc_full % 8 == 0) ? 1 : 0;
+    const dim3 grid((unsigned)(nc_full * s.b * s.G * (s.H / s.G / HB))), block(2 * Q);
+    if (Hb != nullptr)
+        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, true>), grid, block, 0, st, (const bf16 *)x,
+                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
+                           (const bf16 *)Hb, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
+                           (int)s.Lp, K, ng, HB, nc_full, xcd);
+    else
+        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, false>), grid, block, 0, st, (const bf16 *)x,
+                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
+                           (const bf16 *)nullptr, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
+                           (int)s.Lp, K, ng, HB, nc_full, xcd);
     return hipGetLastError();
+}
+
+template <int Q>
+static hipError_t hb_dispatch_q(const Shape &s, const void *x, const void *B, const void *C,
+                                const float *G2, const float *dtT, const void *S, const float *D,
+                                void *y, const void *Hb, const float *beta, int K, int ng,
+                                hipStream_t st)
+{
+    const int nc_full = (int)(s.L / s.Q);
+    switch (s.N) {
+    case 64: return hb_launch<Q, 64>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    case 128: return hb_launch<Q, 128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    default: return hb_launch<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    }
+}
+
+// Head-blocked kernel: chunks of 128 or 256 tokens with N of 64, 128 or 256; the
+// single-head kernel covers the rest.
+static bool head_blocked(const Shape &s)
+{
+    return (s.Q == 128 || s.Q == 256) && (s.N == 64 || s.N == 128 || s.N == 256);
 }
 
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
-                                 void *y, const float *Hg, const float *beta, int K, int ng,
-                                 hipStream_t st)
+                                 void *y, const float *Hg, const void *Hb, const float *beta, int K,
+                                 int ng, hipStream_t st)
 {
-    switch (s.Q) {
-    case 64: return co_launch<64>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
-    case 128: return co_launch<128>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
-    default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    auto single = [&](int c_first, int nc_grid) {
+        switch (s.Q) {
+        case 64: return co_launch<64>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
+        case 128: return co_launch<128>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
+        default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
+        }
+    };
+    if (!head_blocked(s)) return single(0, (int)s.nc);
+    // full chunks head-blocked, a ragged last chunk on the single-head kernel
+    const int nc_full = (int)(s.L / s.Q);
+    hipError_t e = hipSuccess;
+    if (nc_full > 0) {
+        e = (s.Q == 128) ? hb_dispatch_q<128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, st)
+                         : hb_dispatch_q<256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, st);
+        if (e != hipSuccess) return e;
     }
+    if (nc_full < s.nc) e = single(nc_full, 1);
+    return e;
 }
 
 }  // namespace ssd

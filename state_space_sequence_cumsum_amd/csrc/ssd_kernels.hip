@@ -392,7 +392,7 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, hipStream_t st)
 {
-    return s.bf16 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr,
+    return s.bf16 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, nullptr,
                                           (int)s.nc, 1, st)
                   : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, st);
 }
@@ -400,10 +400,11 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
 hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const void *x,
                                       const void *B, const void *C, const float *G2,
                                       const float *dtT, const void *S, const float *D, void *y,
-                                      const float *Hg, const float *beta, hipStream_t st)
+                                      const float *Hg, const void *Hb, const float *beta,
+                                      hipStream_t st)
 {
     if (!s.bf16 || gp.ng <= 1) return launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, st);
-    return launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, Hg, beta, gp.K, gp.ng, st);
+    return launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, Hg, Hb, beta, gp.K, gp.ng, st);
 }
 
 }  // namespace ssd

@@ -33,18 +33,20 @@ Grouping state_pass_groups(const Shape &s);
 // chunk-start states relative to their group, Ug the true group-start states
 // H_g (after the group scan), beta the per-chunk decay since the group start;
 // hT is the true final state.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng],
-// beta [b*H, nc], all fp32.  fp32 problems always use one group.
+// beta [b*H, nc], all fp32, and Hb [b*H, ng, P, N] bf16 (H_g rounded, zeros for
+// group 0).  fp32 problems always use one group.
 hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
                                      const void *B, const float *G2, const float *wT,
-                                     const float *h0, void *S, float *hT, float *Ug, float *gam,
-                                     float *beta, hipStream_t st);
+                                     const float *h0, void *S, float *hT, float *Ug, void *Hb,
+                                     float *gam, float *beta, hipStream_t st);
 
 // Chunk output that adds beta_c H_g to the handed-over chunk-start states
-// (Hg == NULL: S already holds true states).
+// (Hg == NULL: S already holds true states).  Hg is fp32, Hb its bf16 copy.
 hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const void *x,
                                       const void *B, const void *C, const float *G2,
                                       const float *dtT, const void *S, const float *D, void *y,
-                                      const float *Hg, const float *beta, hipStream_t st);
+                                      const float *Hg, const void *Hb, const float *beta,
+                                      hipStream_t st);
 
 // bf16 kernels (ssd_bf16.hip)
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
@@ -52,7 +54,7 @@ hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, 
                                   hipStream_t st);
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
-                                 void *y, const float *Hg, const float *beta, int K, int ng,
-                                 hipStream_t st);
+                                 void *y, const float *Hg, const void *Hb, const float *beta, int K,
+                                 int ng, hipStream_t st);
 
 }  // namespace ssd
