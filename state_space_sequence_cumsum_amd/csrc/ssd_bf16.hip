@@ -405,32 +405,48 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
 // ===========================================================================
 // Group scan.  For each (batch*head, state element): walk the groups in order,
 // H_1 = U_0 and H_{g+1} = gamma_g H_g + U_g; H_g (the true state at group g's
-// start) replaces U_g in place (g >= 1), a bf16 copy goes to Hb (zeros for
-// group 0, which needs no correction), and the state after the last group is hT.
+// start) replaces U_g in place for the groups g >= g_f32 (the chunk outputs that
+// read fp32 states), a bf16 copy goes to Hb (zeros for group 0, which needs no
+// correction), and the state after the last group is hT.
 // ===========================================================================
+template <int NGMAX>
 __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
                                                          const float *__restrict__ gam,
                                                          float *__restrict__ hT,
-                                                         bf16 *__restrict__ Hb, int PN, int ng)
+                                                         bf16 *__restrict__ Hb, int PN, int ng,
+                                                         int g_f32)
 {
     const int bh = blockIdx.y;
     const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
     f32x4 hcar = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int g = 0; g < ng; ++g) {
-        const int64_t off = ((int64_t)bh * ng + g) * PN + e;
-        f32x4 *u = reinterpret_cast<f32x4 *>(Ug + off);
-        const f32x4 v = *u;
-        if (g > 0) *u = hcar;
-        if (Hb != nullptr) {
-            bf16x4 o;
+    // groups in batches of NGMAX: all loads of a batch are issued before its
+    // in-place stores, so their latencies overlap
+    for (int g0 = 0; g0 < ng; g0 += NGMAX) {
+        f32x4 v[NGMAX];
+        float gm[NGMAX];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = (bf16)hcar[r];   // zero for g == 0
-            *reinterpret_cast<bf16x4 *>(Hb + off) = o;
+        for (int k = 0; k < NGMAX; ++k) {
+            const int g = min(g0 + k, ng - 1);
+            v[k] = *reinterpret_cast<const f32x4 *>(Ug + ((int64_t)bh * ng + g) * PN + e);
+            gm[k] = gam[(int64_t)bh * ng + g];
         }
-        const float gm = gam[(int64_t)bh * ng + g];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hcar[r] = gm * hcar[r] + v[r];
+        for (int k = 0; k < NGMAX; ++k) {
+            const int g = g0 + k;
+            if (g < ng) {
+                const int64_t off = ((int64_t)bh * ng + g) * PN + e;
+                if (g > 0 && g >= g_f32) *reinterpret_cast<f32x4 *>(Ug + off) = hcar;
+                if (Hb != nullptr) {
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = (bf16)hcar[r];   // zero for g == 0
+                    *reinterpret_cast<bf16x4 *>(Hb + off) = o;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hcar[r] = gm[k] * hcar[r] + v[k][r];
+            }
+        }
     }
     if (hT != nullptr) *reinterpret_cast<f32x4 *>(hT + (int64_t)bh * PN + e) = hcar;
 }
@@ -1062,6 +1078,13 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
 // ===========================================================================
 // Launchers
 // ===========================================================================
+// Head-blocked kernel: chunks of 128 or 256 tokens with N of 64, 128 or 256; the
+// single-head kernel covers the rest.
+static bool head_blocked(const Shape &s)
+{
+    return (s.Q == 128 || s.Q == 256) && (s.N == 64 || s.N == 128 || s.N == 256);
+}
+
 // register ring depth of the state pass (sub-steps in flight)
 constexpr int kSpDepth = 2;
 
@@ -1140,7 +1163,11 @@ hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const v
     if (e != hipSuccess) return e;
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
-    hipLaunchKernelGGL(group_scan_kernel, grid, dim3(256), 0, st, Ug, gam, hT, (bf16 *)Hb, PN, gp.ng);
+    // fp32 group-start states are read only by single-head chunk-output launches
+    int g_f32 = 1;
+    if (head_blocked(s)) g_f32 = (s.L % s.Q != 0) ? (int)((s.nc - 1) / gp.K) : gp.ng;
+    hipLaunchKernelGGL(group_scan_kernel<8>, grid, dim3(256), 0, st, Ug, gam, hT, (bf16 *)Hb, PN,
+                       gp.ng, g_f32);
     return hipGetLastError();
 }
 
@@ -1213,12 +1240,6 @@ static hipError_t hb_dispatch_q(const Shape &s, const void *x, const void *B, co
     }
 }
 
-// Head-blocked kernel: chunks of 128 or 256 tokens with N of 64, 128 or 256; the
-// single-head kernel covers the rest.
-static bool head_blocked(const Shape &s)
-{
-    return (s.Q == 128 || s.Q == 256) && (s.N == 64 || s.N == 128 || s.N == 256);
-}
 
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
