@@ -590,6 +590,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
             }
         }
         return [&, nb, sq, hq]() {
+            (void)hq;   // read only with the correction
 #pragma unroll
             for (int q = 0; q < SPART / 64; ++q) {
                 if (nb + 64 * q < N) {
@@ -1003,6 +1004,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
             for (int pp = 0; pp < 2; ++pp)
                 mma(ya[pp], *reinterpret_cast<const bf16x8 *>(sfrow + pp * 32 * SFP + f * 16), cfa[f]);
 
+        load_s(RS, hl + 1);
         // Y^T = exp2(G_i) Y^T + M' x
         const float gi = Gs[i_loc];
         const float si = fast_exp2(gi);
@@ -1055,7 +1057,6 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
             }
             mfma_tile(I, m);
         }
-        load_s(RS, hl + 1);   // next head's chunk-start state
 
         // y = Y + D x
         const float Dh = D[h];
