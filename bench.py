@@ -10,6 +10,12 @@ its algorithmic bytes and flops; and the fp64 CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--copy-mib M]
+    python bench.py --step B     # the decode step (ssd_step) at batch B instead
+
+With ``--step B`` one step is one ``ssd_step`` call (one token for each of B
+sequences) on the heads of the workload (default: 32 heads, P=64, N=256, bf16),
+its fp32 state resident in HBM; the line reports tokens/s and the step's HBM
+roofline (it reads and writes the whole state once).
 
 HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of this
 script (FETCH_SIZE, then WRITE_SIZE), each with ``--copy-mib`` so that a plain
@@ -74,6 +80,16 @@ def algorithmic(w):
         "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),
                       "flops": th * (2 * N * P + (Q + 1) * P + (Q + 1) * N * G / H)},
     }
+
+
+def step_algorithmic(w, batch):
+    """Bytes the decode step must move for `batch` sequences: the fp32 state read and
+    written, x, dt and y per head, B and C per group, A and D."""
+    e = 2 if w.dtype == "bf16" else 4
+    bh = batch * w.nheads
+    return {"bytes": bh * (8 * w.headdim * w.dstate + 2 * e * w.headdim + e)
+            + batch * w.ngroups * 2 * e * w.dstate + 8 * w.nheads,
+            "flops": bh * w.headdim * w.dstate * 5}
 
 
 def cpu_baseline(w, inp, budget_s=20.0):
@@ -162,6 +178,71 @@ def summarize_pmc(w, fetch_dir, write_dir, copy_mib):
     print(json.dumps(out, indent=1))
 
 
+def bench_step(args):
+    """Decode-step throughput: K ssd_step calls back to back on one stream."""
+    import torch
+    import oracle
+    import state_space_sequence_cumsum_amd as ssd
+    from state_space_sequence_cumsum_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+
+    base = WORKLOADS[args.workload or HEADLINE]
+    w = base.with_(name=f"step_b{args.step}", batch=args.step, seqlen=1, has_h0=True)
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w, seed=0)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    x, dt = d["x"].reshape(b, H, P), d["dt"].reshape(b, H)
+    B, C = d["B"].reshape(b, G, N), d["C"].reshape(b, G, N)
+    h = d["h0"].clone()
+    y = torch.empty(b, H, P, device=dev, dtype=x.dtype)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.ssd_step(x, dt, d["A"], B, C, d["D"], h, y=y, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mean_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    alg = step_algorithmic(w, b)
+    gbs = alg["bytes"] / (mean_us * 1e-6) / 1e9
+    out = {
+        "metric": f"SSD decode step tokens/s (batch {b}, H{H} P{P} N{N})",
+        "value": b * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": b, "nheads": H, "headdim": P, "dstate": N,
+                   "ngroups": G, "state": "fp32"},
+        "roofline": {"bound": "hbm", "kernel": "decode_step", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": int(alg["bytes"]),
+                     "mean_launch_us": round(mean_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        reps, t_cpu = 0, 0.0
+        while t_cpu < min(args.cpu_budget, 5.0) or reps < 3:
+            t1 = time.perf_counter()
+            oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                           inp["h0"], want_y=True, nthreads=oracle.default_threads())
+            t_cpu += time.perf_counter() - t1
+            reps += 1
+        out["cpu_baseline"] = {"value": b * reps / t_cpu, "unit": "tokens/s",
+                               "cores": min(oracle.default_threads(), b * H), "kind": "oracle",
+                               "sample": f"{reps} whole steps (all {b * H} (batch, head) units, "
+                                         f"fp64 recurrence over one token), wall {t_cpu:.2f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +254,8 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--step", type=int, default=0, metavar="B",
+                    help="time the decode step at batch B instead of the forward pass")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -184,6 +267,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.step > 0:
+        bench_step(args)
+        return
 
     import torch
     import state_space_sequence_cumsum_amd as ssd

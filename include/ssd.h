@@ -10,7 +10,8 @@
  *                           start, by the jump h_next = exp(G_last) h + (exp(G_last - G) dt B)^T X;
  *   3. ssd_chunk_out     -- section "Kernel 3：compute_out": per chunk
  *                           Y = exp(G) C h^T + (exp(G_i - G_j) (C B^T) causal-mask) (dt X) + D X.
- * ssd_forward runs the three in order on one stream.
+ * ssd_forward runs the three in order on one stream.  ssd_step advances the
+ * recurrence by one token per sequence (decode), continuing from the final state.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -25,6 +26,11 @@
  *     G2, dtT, wT [b, H, Lp]    float32 (stage-1 outputs, token-contiguous per head)
  *     S       [b, H, nc, P, N]  bfloat16 when dtype is SSD_BF16, float32 when SSD_F32
  * `problem` is a host pointer.  `stream` is a hipStream_t (NULL = the null stream).
+ *
+ * Alignment: x, y, B, C, S, G2, dtT, wT, h0, hT, h and the workspace are read or
+ * written with 8- and 16-byte vector accesses and must start on a 16-byte boundary
+ * (hipMalloc and torch allocations do); dt, A and D need only their element
+ * alignment.  A misaligned pointer returns SSD_ERR_MISALIGNED.
  *
  * Every call validates its arguments on the host before any launch and returns a
  * status; nothing is launched when it is not SSD_OK.  The library never allocates
@@ -60,7 +66,8 @@ typedef enum {
     SSD_ERR_BAD_SHAPE = 2,    /* a dimension <= 0, or nheads not divisible by ngroups */
     SSD_ERR_UNSUPPORTED = 3,  /* outside the supported dtype / headdim / dstate / chunk set */
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than ssd_workspace_bytes() */
-    SSD_ERR_HIP = 5           /* a HIP launch failed; see ssd_last_hip_error()        */
+    SSD_ERR_HIP = 5,          /* a HIP launch failed; see ssd_last_hip_error()        */
+    SSD_ERR_MISALIGNED = 6    /* a vector-accessed array does not start on 16 bytes  */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -132,6 +139,23 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
                              const float *A, const void *B, const void *C, const float *D,
                              const float *h0, void *y, float *hT, void *workspace,
                              size_t workspace_bytes, void *stream, void *const *events);
+
+/* One decode step (the recurrence of section "Mamba-2 架构" applied to a single token
+ * per sequence; section "Kernel 2: fwd_pass_state" notes that at inference the final
+ * state is handed to the next call as its initial state).  For every (b, h), with
+ * g = h / (H / G):
+ *     h[b,h,p,n] <- exp(A[h] dt[b,h]) h[b,h,p,n] + dt[b,h] x[b,h,p] B[b,g,n]
+ *     y[b,h,p]    = sum_n h[b,h,p,n] C[b,g,n] + D[h] x[b,h,p]      (the updated h)
+ * Shapes: x, y [b, H, P] and dt [b, H] and B, C [b, G, N] in element type `dtype`;
+ * A, D [H] float32; h [b, H, P, N] float32, read and overwritten in place (the hT
+ * layout of ssd_forward, so a forward's final state continues directly).
+ * problem->seqlen must be 1 and problem->chunk is ignored; any headdim >= 1 and
+ * dstate a multiple of 64 up to 512.  The exponential is exp2 of A dt log2(e) in
+ * fp32, the update and the dot product are fp32, y is rounded to `dtype`.  All
+ * pointers are required. */
+ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, const float *A,
+                    const void *B, const void *C, const float *D, float *h, void *y,
+                    void *stream);
 
 /* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,

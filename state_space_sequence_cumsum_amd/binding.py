@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
 
 SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP"}
+          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED"}
 
 
 class SsdError(RuntimeError):
@@ -66,6 +66,7 @@ def lib():
         L.ssd_forward.restype = st
         L.ssd_forward_timed.argtypes = L.ssd_forward.argtypes + [ctypes.POINTER(vp)]
         L.ssd_forward_timed.restype = st
+        L.ssd_step.argtypes, L.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
         L.ssd_last_hip_error.argtypes, L.ssd_last_hip_error.restype = [], ctypes.c_int
         _lib = L
@@ -266,6 +267,31 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
         arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
         _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
     return y, hT
+
+def ssd_step(x, dt, A, B, C, D, h, *, y=None, stream=None):
+    """One decode step.  x [b,H,P], dt [b,H], B and C [b,G,N] (input dtype), A and D [H]
+    float32, h [b,H,P,N] float32 (updated in place).  Returns y [b,H,P]."""
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("ssd_step takes x [b,H,P] and B [b,G,N]")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    problem = make_problem(b, 1, H, G, P, N, 0, x.dtype)
+    io = _io_dtype(problem)
+    dev = x.device
+    _dev(x, "x", io, (b, H, P), None)
+    _dev(dt, "dt", io, (b, H), dev)
+    _dev(A, "A", torch.float32, (H,), dev)
+    _dev(B, "B", io, (b, G, N), dev)
+    _dev(C, "C", io, (b, G, N), dev)
+    _dev(D, "D", torch.float32, (H,), dev)
+    _dev(h, "h", torch.float32, (b, H, P, N), dev)
+    if y is None:
+        y = torch.empty(b, H, P, device=dev, dtype=io)
+    _dev(y, "y", io, (b, H, P), dev)
+    _raise(lib().ssd_step(ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                          _ptr(D), _ptr(h), _ptr(y), _stream(stream, dev)), "ssd_step")
+    return y
+
 
 def workspace_views(problem: SsdProblem, workspace: torch.Tensor) -> dict:
     """Typed views (G2, dtT, wT, S) of an ssd_forward workspace tensor."""

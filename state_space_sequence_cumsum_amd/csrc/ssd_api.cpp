@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "ssd_launch.h"
 
 namespace {
@@ -13,6 +15,15 @@ thread_local int g_last_hip_error = 0;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Arrays the kernels touch with 8- and 16-byte vector accesses must start on 16
+// bytes; NULL (an absent optional array) passes.
+bool aligned16(std::initializer_list<const void *> ptrs)
+{
+    for (const void *p : ptrs)
+        if ((reinterpret_cast<uintptr_t>(p) & 15) != 0) return false;
+    return true;
+}
 
 ssd_status check_shape(const ssd_problem *p)
 {
@@ -35,6 +46,24 @@ ssd_status check_shape(const ssd_problem *p)
     if (p->chunk * p->ngroups * p->dstate >= (int64_t(1) << 31)) return SSD_ERR_UNSUPPORTED;
     if (p->seqlen * p->nheads * p->headdim >= (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
     if (p->seqlen * p->ngroups * p->dstate >= (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+// The decode step's own set: one token per sequence, no chunking.
+ssd_status check_step_shape(const ssd_problem *p)
+{
+    if (p == nullptr) return SSD_ERR_NULL_ARG;
+    if (p->batch <= 0 || p->seqlen <= 0 || p->nheads <= 0 || p->ngroups <= 0 || p->headdim <= 0 ||
+        p->dstate <= 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (p->seqlen != 1 || p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (p->dstate % 64 != 0 || p->dstate > 512) return SSD_ERR_UNSUPPORTED;
+    // 32-bit head and row indices, and a grid of at most 2^31 workgroups
+    if (p->batch > (int64_t(1) << 31) || p->nheads > (int64_t(1) << 30) ||
+        p->headdim > (int64_t(1) << 30))
+        return SSD_ERR_UNSUPPORTED;
+    if (p->batch * p->nheads > (int64_t(1) << 31) / p->headdim) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -116,6 +145,7 @@ ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const fl
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!dt || !A || !G2 || !dtT || !wT) return SSD_ERR_NULL_ARG;
+    if (!aligned16({G2, dtT, wT})) return SSD_ERR_MISALIGNED;
     return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT, wT,
                                                (hipStream_t)stream));
 }
@@ -127,6 +157,7 @@ ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void 
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!x || !B || !G2 || !wT || !S) return SSD_ERR_NULL_ARG;
+    if (!aligned16({x, B, G2, wT, h0, S, hT})) return SSD_ERR_MISALIGNED;
     return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, wT, h0, S, hT,
                                              (hipStream_t)stream));
 }
@@ -138,6 +169,7 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!x || !B || !C || !G2 || !dtT || !S || !D || !y) return SSD_ERR_NULL_ARG;
+    if (!aligned16({x, B, C, G2, dtT, S, y})) return SSD_ERR_MISALIGNED;
     return hip_status(ssd::launch_chunk_out(make_shape(problem), x, B, C, G2, dtT, S, D, y,
                                             (hipStream_t)stream));
 }
@@ -155,6 +187,7 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     const ssd::Shape s = make_shape(problem);
     const Layout l = layout_of(s);
     if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
+    if (!aligned16({x, B, C, h0, y, hT, workspace})) return SSD_ERR_MISALIGNED;
     char *ws = static_cast<char *>(workspace);
     float *G2 = reinterpret_cast<float *>(ws + l.g2);
     float *dtT = reinterpret_cast<float *>(ws + l.dtt);
@@ -191,6 +224,20 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
                              stream, nullptr);
 }
 
+ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, const float *A,
+                    const void *B, const void *C, const float *D, float *h, void *y, void *stream)
+{
+    const ssd_status st = check_step_shape(problem);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !D || !h || !y) return SSD_ERR_NULL_ARG;
+    if (!aligned16({x, B, C, h, y})) return SSD_ERR_MISALIGNED;
+    ssd::Shape s;
+    s.b = problem->batch; s.L = 1; s.H = problem->nheads; s.G = problem->ngroups;
+    s.P = problem->headdim; s.N = problem->dstate; s.Q = 1; s.nc = 1; s.Lp = 1;
+    s.bf16 = problem->dtype == SSD_BF16;
+    return hip_status(ssd::launch_decode_step(s, x, dt, A, B, C, D, h, y, (hipStream_t)stream));
+}
+
 const char *ssd_status_string(ssd_status status)
 {
     switch (status) {
@@ -200,6 +247,7 @@ const char *ssd_status_string(ssd_status status)
     case SSD_ERR_UNSUPPORTED: return "unsupported dtype/headdim/dstate/chunk";
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_HIP: return "HIP launch failed";
+    case SSD_ERR_MISALIGNED: return "a vector-accessed array does not start on a 16-byte boundary";
     }
     return "unknown status";
 }

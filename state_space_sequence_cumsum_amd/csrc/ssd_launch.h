@@ -48,6 +48,11 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const 
                                       const float *Hg, const void *Hb, const float *beta,
                                       hipStream_t st);
 
+// One decode step per (batch, head), h updated in place (ssd_step.hip).
+hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D, float *h, void *y,
+                              hipStream_t st);
+
 // bf16 kernels (ssd_bf16.hip)
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
                                   const float *wT, const float *h0, void *S, float *hT,

@@ -44,8 +44,8 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads of the study, smallest first.  The 16K-token, N=256 one is
-# the headline throughput case.
+# The five workloads of the study, smallest first, then the pages' own usage
+# example.  The 16K-token, N=256 one is the headline throughput case.
 WORKLOADS = {
     w.name: w
     for w in [
@@ -56,6 +56,10 @@ WORKLOADS = {
         Workload("bf16_b1_L65536_H32_P64_N512_Q128", "bf16", 1, 65536, 32, 64, 512, 1, 128),
         Workload("bf16_b1_L262144_H16_G2_P64_N128_Q256", "bf16", 1, 262144, 16, 64, 128, 2, 256,
                  dt_shift=-6.0, has_h0=True),
+        # the usage example of the dbyun.net page (section "Mamba-2 前向传播性能基准测试"):
+        # batch 4, 16K tokens, 8 heads, one group, state 128, head 64, chunk 128, bf16
+        # inputs with an fp32 state; the example passes no initial state
+        Workload("bf16_b4_L16384_H8_P64_N128_Q128", "bf16", 4, 16384, 8, 64, 128, 1, 128),
     ]
 }
 HEADLINE = "bf16_b1_L16384_H32_P64_N256_Q256"

@@ -11,7 +11,8 @@ from state_space_sequence_cumsum_amd import binding
 
 def test_library_exports_every_declared_symbol():
     names = binding.header_functions()
-    assert {"ssd_chunk_cumsum", "ssd_state_pass", "ssd_chunk_out", "ssd_forward"} <= set(names)
+    assert {"ssd_chunk_cumsum", "ssd_state_pass", "ssd_chunk_out", "ssd_forward",
+            "ssd_step"} <= set(names)
     lib = binding.lib()
     for n in names:
         assert hasattr(lib, n), f"libssd.so does not export {n}"
@@ -93,8 +94,54 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.ssd_last_hip_error() == 0
 
 
+def test_misaligned_pointers_are_rejected_without_launching():
+    lib = binding.lib()
+    p = _p()
+    ok = ctypes.c_void_p(4096)
+    off = ctypes.c_void_p(4096 + 8)   # element-aligned, not on 16 bytes
+    assert lib.ssd_chunk_cumsum(ctypes.byref(p), off, ok, ok, off, ok, None) == 6
+    assert lib.ssd_state_pass(ctypes.byref(p), off, ok, ok, ok, None, ok, None, None) == 6
+    assert lib.ssd_state_pass(ctypes.byref(p), ok, ok, ok, ok, off, ok, None, None) == 6
+    assert lib.ssd_chunk_out(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, off, None) == 6
+    assert lib.ssd_forward(ctypes.byref(p), ok, ok, ok, ok, ok, ok, None, ok, None, off, 10**12,
+                           None) == 6
+    assert lib.ssd_forward(ctypes.byref(p), ok, ok, ok, off, ok, ok, None, ok, None, ok, 10**12,
+                           None) == 6
+    sp = _p(seqlen=1)
+    assert lib.ssd_step(ctypes.byref(sp), ok, off, off, ok, ok, off, off, ok, None) == 6
+    assert lib.ssd_last_hip_error() == 0
+
+
+def _sp(**kw):
+    base = dict(batch=4, seqlen=1, nheads=32, ngroups=1, headdim=64, dstate=256, chunk=0,
+                dtype="bf16")
+    base.update(kw)
+    return ssd.make_problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 1),                       # valid shape: reaches the NULL-pointer check
+    (dict(dstate=512, headdim=7, dtype="fp32", nheads=6, ngroups=3), 1),
+    (dict(seqlen=2), 2),
+    (dict(seqlen=0), 2),
+    (dict(batch=0), 2),
+    (dict(nheads=6, ngroups=4), 2),
+    (dict(dstate=96), 3),
+    (dict(dstate=576), 3),
+    (dict(dtype=9), 3),
+    (dict(batch=1 << 20, nheads=1 << 12, headdim=64), 3),
+])
+def test_step_validates_before_launching(kw, status):
+    lib = binding.lib()
+    p = _sp(**kw)
+    ok = ctypes.c_void_p(4096)
+    # every pointer given except y: a valid problem stops at SSD_ERR_NULL_ARG
+    assert lib.ssd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, None, None) == status
+    assert lib.ssd_step(None, ok, ok, ok, ok, ok, ok, ok, ok, None) == 1
+
+
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert ssd.ssd_status_string(s)
     assert "unknown" in ssd.ssd_status_string(42)
 

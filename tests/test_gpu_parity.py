@@ -260,7 +260,7 @@ def test_errors_before_launch():
 
 
 # ---------------------------------------------------------------------------
-# the five study workloads at full size, in the benchmark's launch configuration;
+# the study workloads and the pages' example at full size, in the benchmark's launch configuration;
 # the oracle computes a sample of (batch, head) units over the whole sequence
 # ---------------------------------------------------------------------------
 FULL = [(name, units) for name, units in [
@@ -269,6 +269,7 @@ FULL = [(name, units) for name, units in [
     ("bf16_b1_L16384_H32_P64_N256_Q256", [0, 17, 31]),
     ("bf16_b1_L65536_H32_P64_N512_Q128", [5, 30]),
     ("bf16_b1_L262144_H16_G2_P64_N128_Q256", [2, 12]),
+    ("bf16_b4_L16384_H8_P64_N128_Q128", [0, 11, 31]),
 ]]
 
 

@@ -1,0 +1,134 @@
+"""GPU parity of the decode step (ssd_step) against the fp64 oracle.
+
+One step of the recurrence is the oracle's sequential forward over a single token
+with the step's state as initial state; a chain of steps after a forward pass is
+the oracle's forward over the whole sequence.  Same bar as the forward: per tensor
+max|out - ref| <= tau * max|ref|, tau = 1e-4 (fp32 inputs) or 2e-2 (bf16 inputs).
+"""
+import pytest
+import torch
+
+import oracle
+import state_space_sequence_cumsum_amd as ssd
+from state_space_sequence_cumsum_amd.inputs import Workload, make_inputs
+from gpu_util import TOL, check, f64, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _step_case(dtype, b, H, G, P, N, seed=0, h_scale=10.0):
+    w = Workload("step", dtype, b, 1, H, P, N, G, 64, has_h0=True)
+    inp = make_inputs(w, seed)
+    inp["h0"] = inp["h0"] * h_scale       # a state of the size a long sequence leaves
+    return w, inp
+
+
+def _run_step(inp, dev, dt_off=0):
+    """The step on cuda:0; dt_off > 0 passes dt, A and D as views that start dt_off
+    elements into larger buffers (element-aligned, not 16-byte aligned)."""
+    d = to_dev(inp, dev)
+    b, _, H, P = d["x"].shape
+    G, N = d["B"].shape[2], d["B"].shape[3]
+    x = d["x"].reshape(b, H, P)
+    dt = d["dt"].reshape(b, H)
+    A, D = d["A"], d["D"]
+    if dt_off:
+        def shifted(t):
+            buf = torch.zeros(t.numel() + dt_off, device=dev, dtype=t.dtype)
+            buf[dt_off:] = t.reshape(-1)
+            return buf[dt_off:].view(t.shape)
+        dt, A, D = shifted(dt), shifted(A), shifted(D)
+    h = d["h0"].clone()
+    y = torch.full((b, H, P), float("nan"), device=dev, dtype=x.dtype)
+    ssd.ssd_step(x, dt, A, d["B"].reshape(b, G, N), d["C"].reshape(b, G, N), D, h, y=y)
+    torch.cuda.synchronize()
+    return y, h
+
+
+STEP_CASES = [
+    # dtype, b, H, G, P, N
+    ("fp32", 2, 4, 1, 64, 64),
+    ("bf16", 2, 4, 2, 64, 128),
+    ("bf16", 1, 32, 1, 64, 256),      # the headline model's heads
+    ("bf16", 3, 6, 3, 37, 192),       # ragged row blocks, N = 3 x 64
+    ("fp32", 2, 8, 8, 16, 320),       # G = H
+    ("bf16", 2, 4, 1, 64, 384),
+    ("fp32", 1, 2, 1, 5, 448),
+    ("bf16", 4, 16, 2, 64, 512),
+]
+
+
+@pytest.mark.parametrize("dtype,b,H,G,P,N", STEP_CASES,
+                         ids=[f"{c[0]}-b{c[1]}H{c[2]}G{c[3]}P{c[4]}N{c[5]}" for c in STEP_CASES])
+def test_step_matches_oracle(dtype, b, H, G, P, N):
+    dev = require_gpu()
+    w, inp = _step_case(dtype, b, H, G, P, N)
+    print(f"step case {dtype} b{b} H{H} G{G} P{P} N{N}", flush=True)
+    y, h = _run_step(inp, dev)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    tol = TOL[dtype]
+    check(f64(y), ref["y"][:, 0], tol, "y")
+    check(f64(h), ref["hT"], tol, "h")
+
+
+def test_step_element_aligned_scalars():
+    """dt, A and D are read element by element: views that start off a 16-byte boundary
+    give the same result as aligned ones, bit for bit."""
+    dev = require_gpu()
+    w, inp = _step_case("bf16", 2, 8, 2, 64, 256, seed=3)
+    y0, h0 = _run_step(inp, dev)
+    y1, h1 = _run_step(inp, dev, dt_off=1)
+    assert torch.equal(y0, y1) and torch.equal(h0, h1)
+
+
+def test_step_zero_dt_keeps_state_bitwise():
+    """dt = 0: exp(0) = 1 and no input, so h is unchanged bit for bit and y = C h^T + D x."""
+    dev = require_gpu()
+    w, inp = _step_case("fp32", 2, 4, 1, 64, 128, seed=4)
+    inp["dt"] = torch.zeros_like(inp["dt"])
+    y, h = _run_step(inp, dev)
+    assert torch.equal(h.cpu(), inp["h0"])
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    check(f64(y), ref["y"][:, 0], TOL["fp32"], "y")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_steps_continue_a_forward(dtype):
+    """A forward over the first L0 tokens, then one step per remaining token from its
+    final state, equals the oracle's forward over the whole sequence."""
+    dev = require_gpu()
+    L0, T = 256, 8
+    N = 64 if dtype == "fp32" else 256
+    w = Workload("chain", dtype, 2, L0 + T, 8, 64, N, 2, 64, has_h0=True)
+    inp = make_inputs(w, 5)
+    print(f"chain case {w}", flush=True)
+    d = to_dev(inp, dev)
+    head = {k: d[k][:, :L0].contiguous() for k in ("x", "dt", "B", "C")}
+    y0, h = ssd.ssd_forward(head["x"], head["dt"], d["A"], head["B"], head["C"], d["D"], d["h0"],
+                            chunk=w.chunk)
+    ys = []
+    for t in range(L0, L0 + T):
+        ys.append(ssd.ssd_step(d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                               d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"], h))
+    torch.cuda.synchronize()
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    tol = TOL[dtype]
+    check(f64(y0), ref["y"][:, :L0], tol, "y of the forward part")
+    check(f64(torch.stack(ys, 1)), ref["y"][:, L0:], tol, "y of the decode steps")
+    check(f64(h), ref["hT"], tol, "final state")
+
+
+def test_step_rejects_bad_arguments():
+    dev = require_gpu()
+    w, inp = _step_case("bf16", 1, 4, 1, 64, 64)
+    d = to_dev(inp, dev)
+    x = d["x"].reshape(1, 4, 64)
+    B = d["B"].reshape(1, 1, 64)
+    h = d["h0"].clone()
+    with pytest.raises(ValueError):      # state must be fp32
+        ssd.ssd_step(x, d["dt"].reshape(1, 4), d["A"], B, B, d["D"], h.to(torch.bfloat16))
+    Bbad = torch.zeros(1, 1, 96, device=dev, dtype=torch.bfloat16)
+    hbad = torch.zeros(1, 4, 64, 96, device=dev)
+    with pytest.raises(ssd.SsdError) as ei:
+        ssd.ssd_step(x, d["dt"].reshape(1, 4), d["A"], Bbad, Bbad, d["D"], hbad)
+    assert ei.value.status == 3
