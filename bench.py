@@ -3,14 +3,17 @@
 
 One step = one whole forward (chunk cumsum, state pass, chunk output) over the
 16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints one
-JSON line:  tokens/s of ``ssd_forward`` over K steps; per-stage durations from
-HIP events that the library records on the launch stream between its stages,
-over K further steps run right after; the roofline of the dominant stage from
-its algorithmic bytes and flops; and the fp64 CPU oracle timed on this host.
+JSON line:  tokens/s of ``ssd_forward`` over K steps back to back; per-stage
+durations (mean, median, p10, p90) from HIP events that the library records on
+the launch stream between its stages, over K further steps run right after; the
+roofline of the dominant stage from its algorithmic bytes and flops; ``cold``:
+the median forward when a 1 GiB write flushes L2 and the Infinity Cache before
+each rep; and the fp64 CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--copy-mib M]
     python bench.py --step B     # the decode step (ssd_step) at batch B instead
+    python bench.py --sweep      # the forward over 1K-256K tokens x state 64-512
 
 With ``--step B`` one step is one ``ssd_step`` call (one token for each of B
 sequences) on the heads of the workload (default: 32 heads, P=64, N=256, bf16),
@@ -53,6 +56,7 @@ KERNEL_SOURCES = ["state_space_sequence_cumsum_amd/csrc/ssd_bf16.hip",
 KERNEL_NAMES = {"chunk_cumsum": "chunk_cumsum_kernel", "state_pass": "state_pass",
                 "group_scan": "group_scan_kernel", "chunk_out": "chunk_out"}
 COPY_KERNEL = "copyBuffer"
+FLUSH_MIB = 1024                # written before each cold rep: > L2 + 256 MB Infinity Cache
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
@@ -80,6 +84,12 @@ def algorithmic(w):
         "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),
                       "flops": th * (2 * N * P + (Q + 1) * P + (Q + 1) * N * G / H)},
     }
+
+
+def pct(v, q):
+    """q-th percentile (nearest rank) of a list of numbers."""
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
 def step_algorithmic(w, batch):
@@ -243,6 +253,64 @@ def bench_step(args):
     print(json.dumps(out), flush=True)
 
 
+SWEEP_TOKENS = [1024, 4096, 16384, 65536, 262144]
+SWEEP_STATES = [64, 128, 256, 512]
+SWEEP_BASE = "bf16_b4_L16384_H8_P64_N128_Q128"
+
+
+def bench_sweep(args):
+    """The forward over the pages' comparison grid (1K-256K tokens x state 64-512) on the
+    usage example's model shape; one JSON line per shape, inputs drawn on the GPU."""
+    import torch
+    import state_space_sequence_cumsum_amd as ssd
+    from state_space_sequence_cumsum_amd.inputs import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    base = WORKLOADS[SWEEP_BASE]
+    for L in SWEEP_TOKENS:
+        for N in SWEEP_STATES:
+            w = base.with_(name=f"bf16_b{base.batch}_L{L}_H{base.nheads}_P{base.headdim}_N{N}"
+                                f"_Q{base.chunk}", seqlen=L, dstate=N)
+            d = make_inputs(w, seed=0, device=dev)
+            y = torch.empty_like(d["x"])
+            prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+            ws = ssd.workspace_for(prob, dev)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                   for _ in range(args.steps)]
+            for row in evs:
+                for e in row:
+                    e.record(stream)
+
+            def forward(events=None):
+                ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None,
+                                chunk=w.chunk, y=y, want_final=True, workspace=ws,
+                                stream=stream, events=events)
+
+            for _ in range(args.warmup):
+                forward()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                forward()
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) / args.steps
+            for k in range(args.steps):
+                forward(evs[k])
+            torch.cuda.synchronize()
+            st = {n: statistics.median(evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3
+                                       for k in range(args.steps))
+                  for i, n in enumerate(["chunk_cumsum", "state_pass", "chunk_out"])}
+            alg = algorithmic(w)
+            print(json.dumps({"workload": w.name, "tokens_per_s": round(w.batch * L / el),
+                              "us_per_forward": round(el * 1e6, 2),
+                              "stage_median_us": {n: round(v, 2) for n, v in st.items()},
+                              "frac_hbm": {n: round(alg[n]["bytes"] / (st[n] * 1e-6) / 1e9
+                                                    / HBM_PEAK_GBS, 4) for n in st}}),
+                  flush=True)
+            del d, y, ws
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +322,10 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="forwards timed after a cache flush each (0: skip)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the forward over the 1K-256K token x state 64-512 grid")
     ap.add_argument("--step", type=int, default=0, metavar="B",
                     help="time the decode step at batch B instead of the forward pass")
     args = ap.parse_args()
@@ -270,6 +342,9 @@ def main():
 
     if args.step > 0:
         bench_step(args)
+        return
+    if args.sweep:
+        bench_sweep(args)
         return
 
     import torch
@@ -327,7 +402,24 @@ def main():
     per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)]
            for i, n in enumerate(names)}   # microseconds
     kern = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
-                "min_us": min(v)} for n, v in per.items()}
+                "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v)}
+            for n, v in per.items()}
+
+    # --- cold region: each forward after a write of FLUSH_MIB through the caches, so
+    # that inputs come from HBM rather than L2 or the Infinity Cache ---
+    cold = []
+    if args.cold_reps > 0:
+        flush = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device=dev)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.cold_reps)]
+        for a, z in ce:
+            flush.fill_(0)
+            a.record(stream)
+            forward()
+            z.record(stream)
+        torch.cuda.synchronize()
+        cold = [a.elapsed_time(z) * 1e3 for a, z in ce]
+        del flush
 
     alg = algorithmic(w)
     for n in names:
@@ -375,6 +467,11 @@ def main():
         "stage_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
         "roofline": roof,
     }
+    if cold:
+        out["cold"] = {"reps": len(cold), "flush_mib": FLUSH_MIB,
+                       "median_us": round(statistics.median(cold), 2),
+                       "p10_us": round(pct(cold, 10), 2), "p90_us": round(pct(cold, 90), 2),
+                       "tokens_per_s": round(tokens / (statistics.median(cold) * 1e-6))}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -70,21 +70,25 @@ def torch_dtype(name: str) -> torch.dtype:
     return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
 
 
-def make_inputs(w: Workload, seed: int = 0) -> dict:
-    """Draw one set of inputs for workload ``w`` on the CPU.
+def make_inputs(w: Workload, seed: int = 0, device="cpu") -> dict:
+    """Draw one set of inputs for workload ``w``.
 
-    Returns torch CPU tensors: x [b,L,H,P], dt [b,L,H], A [H], B and C [b,L,G,N],
-    D [H], and h0 [b,H,P,N] or None.
+    Returns torch tensors on ``device``: x [b,L,H,P], dt [b,L,H], A [H], B and C
+    [b,L,G,N], D [H], and h0 [b,H,P,N] or None.  The generator lives on ``device``:
+    every parity input is drawn on the CPU; a GPU draw (same laws, other values)
+    only feeds timing runs too large to draw on the host quickly.
     """
-    g = torch.Generator().manual_seed(int(seed))
+    g = torch.Generator(device=device).manual_seed(int(seed))
     b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
-    A = -torch.exp(torch.empty(H).uniform_(math.log(1.0), math.log(16.0), generator=g))
-    D = torch.empty(H).uniform_(0.0, 1.0, generator=g)
-    dt = torch.nn.functional.softplus(torch.randn(b, L, H, generator=g) + w.dt_shift)
-    x = torch.randn(b, L, H, P, generator=g)
-    B = torch.randn(b, L, G, N, generator=g)
-    C = torch.randn(b, L, G, N, generator=g)
-    h0 = 0.1 * torch.randn(b, H, P, N, generator=g) if w.has_h0 else None
+    kw = {"generator": g, "device": device}
+    A = -torch.exp(torch.empty(H, device=device).uniform_(math.log(1.0), math.log(16.0),
+                                                          generator=g))
+    D = torch.empty(H, device=device).uniform_(0.0, 1.0, generator=g)
+    dt = torch.nn.functional.softplus(torch.randn(b, L, H, **kw) + w.dt_shift)
+    x = torch.randn(b, L, H, P, **kw)
+    B = torch.randn(b, L, G, N, **kw)
+    C = torch.randn(b, L, G, N, **kw)
+    h0 = 0.1 * torch.randn(b, H, P, N, **kw) if w.has_h0 else None
     td = torch_dtype(w.dtype)
     return {
         "x": x.to(td).contiguous(),

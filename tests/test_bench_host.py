@@ -69,3 +69,25 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_percentile_nearest_rank():
+    v = [float(i) for i in range(1, 11)]
+    assert bench.pct(v, 10) == 2.0 and bench.pct(v, 50) in (5.0, 6.0) and bench.pct(v, 90) == 9.0
+    assert bench.pct([3.0], 90) == 3.0
+    assert bench.pct([5.0, 1.0, 3.0], 0) == 1.0 and bench.pct([5.0, 1.0, 3.0], 100) == 5.0
+
+
+def test_step_algorithmic_bytes():
+    # batch 128 of the headline heads: fp32 state read and written dominates
+    w = WORKLOADS["bf16_b1_L16384_H32_P64_N256_Q256"]
+    a = bench.step_algorithmic(w, 128)
+    state = 128 * 32 * 64 * 256 * 4 * 2
+    io = 128 * 32 * (2 * 2 * 64 + 2) + 128 * 1 * 2 * 2 * 256 + 8 * 32
+    assert a["bytes"] == state + io
+
+
+def test_sweep_grid_covers_the_pages_range():
+    assert bench.SWEEP_TOKENS[0] == 1024 and bench.SWEEP_TOKENS[-1] == 262144
+    assert bench.SWEEP_STATES == [64, 128, 256, 512]
+    assert bench.SWEEP_BASE in WORKLOADS
