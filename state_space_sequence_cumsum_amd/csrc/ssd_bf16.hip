@@ -767,40 +767,51 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
 //     diagonal, one extra product on it);
 //   * y = Y + D x, the raw x read back from the same LDS tile.
 // The next head's x, dt and decays are loaded a whole head ahead and its
-// chunk-start state right after the decay-matrix work.
+// chunk-start state right after the S C^T products.
 //
 // Waves own 32-token row tiles I(w), SIMD-balanced as in the single-head
-// kernel; the output is built transposed, Y^T [64 p x 32 tokens].  The decay
+// kernel; the output is built transposed, Y^T [64 p x 32 tokens].
+// SPL = 2 (N = 512, where one wave cannot hold its C rows for every column in
+// registers): two waves share each row tile, on the same SIMD.  Wave half hf
+// holds C for columns [hf N/2, (hf+1) N/2), computes C B^T and S_eff C^T over
+// those columns and the decay tiles J with J % 2 == hf; the halves then swap
+// their partial Y^T through LDS, half hf finishing the 32 p rows pp = hf.  The decay
 // matrix tiles J < I use the exact factorization exp2(G_i - G_e) exp2(G_e - G_j),
 // e the last token of tile J (both factors <= 1).
 // Rounding: C B^T is rounded to bf16 once after its fp32 accumulation and the
 // decay matrix again as the MFMA operand; H_g arrives in bf16.
 // Chunks are full (a ragged last chunk is left to the single-head kernel).
 // ===========================================================================
-template <int Q, int NN, bool CORR>
-__global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
+template <int Q, int NN, bool CORR, int SPL>
+__global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
     const float *__restrict__ D, bf16 *__restrict__ y, const bf16 *__restrict__ Hb,
     const float *__restrict__ beta, int L, int H, int G, int nc, int Lp, int K, int ng, int HB,
     int nc_full, int xcd)
 {
-    constexpr int P = 64, NI = Q / 32, NW = Q / 32, NTHR = 2 * Q, NS = 64;
+    constexpr int P = 64, NI = Q / 32, NW = Q / 32, NTHR = 2 * Q * SPL, NS = 64;
     constexpr int NSL = (NN + NS - 1) / NS;     // B slices
     constexpr int NSW = NN < NS ? NN : NS;      // slice width
-    constexpr int NF = NN / 16;                 // C fragments per lane
+    constexpr int NIT = NSL / SPL;              // slice steps (SPL slices staged per step)
+    constexpr int NF = NN / 16 / SPL;           // C fragments per lane (its column half)
     constexpr int XP = Q + 8, BP = frag_pitch(NSW), SFP = NN + 8;
-    constexpr int BPC = Q * (NSW / 8) / NTHR;   // 16-byte B pieces per thread per slice
+    constexpr int SLICE_EL = Q * (NSW / 8);     // 16-byte pieces of one B slice
+    constexpr int BPC = SPL * SLICE_EL / NTHR;  // 16-byte B pieces per thread per step
     constexpr int SPT = P * (NN / 8) / NTHR;    // 16-byte S pieces per thread
-    static_assert(BPC >= 1 && SPT >= 1 && NN % 16 == 0, "staging cover");
+    static_assert(BPC >= 1 && SPT >= 1 && NN % 16 == 0 && NSL % SPL == 0, "staging cover");
+    static_assert(SPL == 1 || SPL == 2, "one or two column halves");
     constexpr int NTILE = NI * (NI + 1) / 2;    // causal tiles
     constexpr int CB_EL = NTILE * 32 * 32;      // bf16 C B^T tiles
-    constexpr int U_EL = (Q * BP > CB_EL) ? Q * BP : CB_EL;
+    constexpr int XC_EL = SPL == 2 ? NW * 2 * 1024 * 2 : 0;   // fp32 partial-Y swap area
+    constexpr int U_EL = (SPL * Q * BP > CB_EL + XC_EL) ? SPL * Q * BP : CB_EL + XC_EL;
+    static_assert(SPL == 1 || 4 * CB_EL <= 2 * P * SFP, "partial C B^T fits the S area");
     // raw x^T [p][position] (token order permuted within 16-token groups: the
     // middle two 4-token blocks swapped, so the accumulator token order of a lane
-    // becomes 8 consecutive positions); Un holds the B slice during C B^T and then
+    // becomes 8 consecutive positions); Un holds the B slices during C B^T and then
     // the bf16 C B^T tiles: tile (I, J) at (I(I+1)/2 + J) * 1024 elements, lane l's
-    // elements 0..7 at 8 l and 8..15 at 512 + 8 l
+    // elements 0..7 at 8 l and 8..15 at 512 + 8 l, followed (SPL = 2) by the
+    // partial-Y swap area
     __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
     __shared__ __attribute__((aligned(16))) bf16 Un[U_EL];
     __shared__ __attribute__((aligned(16))) bf16 Sf[P * SFP];
@@ -809,7 +820,9 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
     __shared__ __attribute__((aligned(16))) float Dt[Q];   // dt_j
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int I = (w < NW / 2) ? w : NW - 1 - (w - NW / 2);
+    const int hf = SPL == 1 ? 0 : w / NW;      // column half
+    const int wi = SPL == 1 ? w : w % NW;      // wave within the half
+    const int I = (wi < NW / 2) ? wi : NW - 1 - (wi - NW / 2);
 
     // workgroup -> (chunk, (batch, group, head block)); with `xcd` (nc_full a
     // multiple of 8) XCD x gets the contiguous chunk range [x nc/8, (x+1) nc/8)
@@ -840,15 +853,17 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
     // ================= C B^T, once per workgroup =================
     bf16x8 cfa[NF];                // this wave's C rows, all N: fragment f = columns 16 f ..
     {
-        const int crow_off = i_loc * brow + kq * 2;
+        const int crow_off = i_loc * brow + kq * 2 + hf * NF * 32;
 #pragma unroll
         for (int f = 0; f < NF; ++f)
             cfa[f] = *reinterpret_cast<const bf16x8 *>(Cb + (uint32_t)(crow_off + f * 32));
+        // step it stages slice it + s NIT (s < SPL) at Un + s Q BP: half s's columns
         int bo[BPC];
 #pragma unroll
         for (int r = 0; r < BPC; ++r) {
-            const int id = tid + NTHR * r, t = id / (NSW / 8), oc = id % (NSW / 8);
-            bo[r] = t * brow + oc * 16;
+            const int id = tid + NTHR * r, sh = id / SLICE_EL, i2 = id % SLICE_EL;
+            const int t = i2 / (NSW / 8), oc = i2 % (NSW / 8);
+            bo[r] = t * brow + oc * 16 + sh * NIT * NSW * 2;
         }
         bf16x8 bq[BPC];
         auto load_b = [&](int n0) {
@@ -860,26 +875,56 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
         for (int J = 0; J < NI; ++J) cb[J] = zero_acc();
         load_b(0);
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-            __syncthreads();   // previous slice consumed
+        for (int it = 0; it < NIT; ++it) {
+            __syncthreads();   // previous slices consumed
 #pragma unroll
             for (int r = 0; r < BPC; ++r) {
-                const int id = tid + NTHR * r, t = id / (NSW / 8), oc = id % (NSW / 8);
-                *reinterpret_cast<bf16x8 *>(&Un[t * BP + oc * 8]) = bq[r];
+                const int id = tid + NTHR * r, sh = id / SLICE_EL, i2 = id % SLICE_EL;
+                const int t = i2 / (NSW / 8), oc = i2 % (NSW / 8);
+                *reinterpret_cast<bf16x8 *>(&Un[sh * Q * BP + t * BP + oc * 8]) = bq[r];
             }
-            if (sl + 1 < NSL) load_b((sl + 1) * NSW);
+            if (it + 1 < NIT) load_b((it + 1) * NSW);
             __syncthreads();
 #pragma unroll
             for (int J = 0; J < NI; ++J) {
                 if (J <= I) {
-                    const bf16 *brw = Un + (J * 32 + (lane & 31)) * BP + kq;
+                    const bf16 *brw = Un + hf * Q * BP + (J * 32 + (lane & 31)) * BP + kq;
 #pragma unroll
                     for (int ks = 0; ks < NSW / 16; ++ks)
-                        mma(cb[J], *reinterpret_cast<const bf16x8 *>(brw + ks * 16), cfa[sl * (NSW / 16) + ks]);
+                        mma(cb[J], *reinterpret_cast<const bf16x8 *>(brw + ks * 16), cfa[it * (NSW / 16) + ks]);
                 }
             }
         }
         __syncthreads();   // the B slice area becomes the C B^T store
+        if constexpr (SPL == 2) {
+            // half 1 hands its partial C B^T (fp32) to half 0 through the S area
+            float *pcb = reinterpret_cast<float *>(Sf) + (I * (I + 1) / 2) * 1024 + 4 * lane;
+            if (hf == 1) {
+#pragma unroll
+                for (int J = 0; J < NI; ++J)
+                    if (J <= I)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            f32x4 v;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = cb[J][4 * k + e];
+                            *reinterpret_cast<f32x4 *>(pcb + J * 1024 + k * 256) = v;
+                        }
+            }
+            __syncthreads();
+            if (hf == 0) {
+#pragma unroll
+                for (int J = 0; J < NI; ++J)
+                    if (J <= I)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const f32x4 v = *reinterpret_cast<const f32x4 *>(pcb + J * 1024 + k * 256);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) cb[J][4 * k + e] += v[e];
+                        }
+            }
+        }
+        if (hf == 0) {
 #pragma unroll
         for (int J = 0; J < NI; ++J) {
             if (J <= I) {
@@ -893,10 +938,11 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
                 *reinterpret_cast<u32x4 *>(cbl + J * 1024 + 512) = hi;
             }
         }
+        }
     }
 
     // ================= per-head work =================
-    const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + (lane >> 3);
+    const int tg = (wi >> 1) * 8 + (lane & 7), cg = (wi & 1) * 8 + (lane >> 3);
     struct XRegs {
         u32x2 xv[8];
         float gt, ge, dt;
@@ -948,6 +994,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
         const int pos0 = (tg >> 1) * 16 + ((tg & 1) ? 4 : 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if (hf != 0) break;   // half 1 holds a copy of the same x pieces
             u32x2 lo, hi;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
@@ -1002,9 +1049,12 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
         for (int f = 0; f < NF; ++f)
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
-                mma(ya[pp], *reinterpret_cast<const bf16x8 *>(sfrow + pp * 32 * SFP + f * 16), cfa[f]);
+                mma(ya[pp], *reinterpret_cast<const bf16x8 *>(sfrow + pp * 32 * SFP + (hf * NF + f) * 16), cfa[f]);
 
-        load_s(RS, hl + 1);
+        // next head's chunk-start state: with one column half per wave its latency
+        // hides behind the decay-matrix products; with two (twice the registers per
+        // thread) it is issued after them
+        if constexpr (SPL == 1) load_s(RS, hl + 1);
         // Y^T = exp2(G_i) Y^T + M' x
         const float gi = Gs[i_loc];
         const float si = fast_exp2(gi);
@@ -1018,7 +1068,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
                 for (int pp = 0; pp < 2; ++pp) mma(ya[pp], ld16(xt + pp * 32 * XP), m[sub]);
             }
         };
-        for (int J = 0; J < I; ++J) {   // off the diagonal
+        for (int J = hf; J < I; J += SPL) {   // off the diagonal (this half's tiles)
             const int jrow = J * 32 + 4 * (lane >> 5);   // + 8q + r for element 4q + r
             const float ci = fast_exp2(gi - Gs[J * 32 + 31]);
             const u32x4 c0 = *reinterpret_cast<const u32x4 *>(cbl + J * 1024);
@@ -1037,7 +1087,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
             }
             mfma_tile(J, m);
         }
-        {   // the diagonal tile, selected on i >= j
+        if (SPL == 1 || (I & 1) == hf) {   // the diagonal tile, selected on i >= j
             const int jrow = I * 32 + 4 * (lane >> 5);
             const u32x4 c0 = *reinterpret_cast<const u32x4 *>(cbl + I * 1024);
             const u32x4 c1 = *reinterpret_cast<const u32x4 *>(cbl + I * 1024 + 512);
@@ -1058,18 +1108,42 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
             mfma_tile(I, m);
         }
 
+        if constexpr (SPL == 2) {
+            load_s(RS, hl + 1);
+            // swap partial Y^T with the other half of the row tile: this wave keeps
+            // rows pp = hf and sends rows 1 - hf
+            float *xc = reinterpret_cast<float *>(Un + CB_EL) + I * 2048 + 4 * lane;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = hf ? ya[0][4 * k + e] : ya[1][4 * k + e];
+                *reinterpret_cast<f32x4 *>(xc + (1 - hf) * 1024 + k * 256) = v;
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ya[0][e] = hf ? ya[1][e] : ya[0][e];
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(xc + hf * 1024 + k * 256);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ya[0][4 * k + e] += v[e];
+            }
+        }
+
         // y = Y + D x
         const float Dh = D[h];
         bf16 *yb = y + ((int64_t)b * L + t0 + i_loc) * xstride + (int64_t)h * P;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
+        for (int pq = 0; pq < 2 / SPL; ++pq) {
+            const int pp = SPL == 1 ? pq : hf;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
                 const bf16x4 xv = tr_read4(Xd + skip_off + (pp * 32 + 8 * q) * XP);
                 bf16x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pp][4 * q + r] + Dh * (float)xv[r]);
+                for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pq][4 * q + r] + Dh * (float)xv[r]);
                 *reinterpret_cast<bf16x4 *>(yb + p) = o;
             }
         }
@@ -1079,11 +1153,13 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_hb_kernel(
 // ===========================================================================
 // Launchers
 // ===========================================================================
-// Head-blocked kernel: chunks of 128 or 256 tokens with N of 64, 128 or 256; the
+// Head-blocked kernel: chunks of 128 or 256 tokens with N of 64, 128 or 256, and
+// 128-token chunks with N = 512 (column halves split over wave pairs); the
 // single-head kernel covers the rest.
 static bool head_blocked(const Shape &s)
 {
-    return (s.Q == 128 || s.Q == 256) && (s.N == 64 || s.N == 128 || s.N == 256);
+    return ((s.Q == 128 || s.Q == 256) && (s.N == 64 || s.N == 128 || s.N == 256)) ||
+           (s.Q == 128 && s.N == 512);
 }
 
 // register ring depth of the state pass (sub-steps in flight)
@@ -1211,16 +1287,17 @@ static hipError_t hb_launch(const Shape &s, const void *x, const void *B, const 
                             void *y, const void *Hb, const float *beta, int K, int ng, int nc_full,
                             hipStream_t st)
 {
+    constexpr int SPL = NN > 256 ? 2 : 1;
     const int HB = heads_per_block(s);
     const int xcd = (nc_full % 8 == 0) ? 1 : 0;
-    const dim3 grid((unsigned)(nc_full * s.b * s.G * (s.H / s.G / HB))), block(2 * Q);
+    const dim3 grid((unsigned)(nc_full * s.b * s.G * (s.H / s.G / HB))), block(2 * Q * SPL);
     if (Hb != nullptr)
-        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, true>), grid, block, 0, st, (const bf16 *)x,
+        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, true, SPL>), grid, block, 0, st, (const bf16 *)x,
                            (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
                            (const bf16 *)Hb, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
                            (int)s.Lp, K, ng, HB, nc_full, xcd);
     else
-        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, false>), grid, block, 0, st, (const bf16 *)x,
+        hipLaunchKernelGGL((chunk_out_hb_kernel<Q, NN, false, SPL>), grid, block, 0, st, (const bf16 *)x,
                            (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
                            (const bf16 *)nullptr, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
                            (int)s.Lp, K, ng, HB, nc_full, xcd);
@@ -1237,7 +1314,11 @@ static hipError_t hb_dispatch_q(const Shape &s, const void *x, const void *B, co
     switch (s.N) {
     case 64: return hb_launch<Q, 64>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
     case 128: return hb_launch<Q, 128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
-    default: return hb_launch<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    case 256: return hb_launch<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    default:
+        if constexpr (Q == 128)
+            return hb_launch<Q, 512>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+        return hipErrorInvalidValue;   // not head-blocked: never dispatched here
     }
 }
 

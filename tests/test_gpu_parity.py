@@ -122,6 +122,9 @@ SMALL_CASES = [
     _wl("bf16_groups_q256", "bf16", 2, 2900, 3, 64, 256, 3, 256),
     _wl("bf16_groups_q64", "bf16", 1, 1100, 1, 64, 64, 1, 64, h0=False),
     _wl("bf16_groups_odd", "bf16", 1, 1100, 43, 64, 256, 1, 128),   # 3 chunks per group
+    # N = 512 with 128-token chunks: column halves split over wave pairs
+    _wl("bf16_groups_n512", "bf16", 1, 2200, 4, 64, 512, 2, 128),    # grouped, ragged, G = 2
+    _wl("bf16_hb2_n512", "bf16", 1, 8192, 8, 64, 512, 1, 128),       # 2 heads per block
 ]
 
 
