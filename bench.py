@@ -24,8 +24,8 @@ HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of this
 script (FETCH_SIZE, then WRITE_SIZE), each with ``--copy-mib`` so that a plain
 device-to-device copy of known size calibrates the counter:
 
-    rocprofv3 --pmc FETCH_SIZE -f csv -d DIR_F -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-mib 1024
-    rocprofv3 --pmc WRITE_SIZE -f csv -d DIR_W -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-mib 1024
+    rocprofv3 --pmc FETCH_SIZE -f csv -d DIR_F -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --cold-reps 0 --copy-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -f csv -d DIR_W -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --cold-reps 0 --copy-mib 1024
     python bench.py --summarize-pmc DIR_F DIR_W --copy-mib 1024
 
 The last command writes profiles/traffic_<workload>.json, which later runs report
@@ -169,7 +169,7 @@ def summarize_pmc(w, fetch_dir, write_dir, copy_mib):
     w_scale = known_kib / max(wr["copy"])
     alg = algorithmic(w)
     cmd = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 3 --warmup 1 "
-           f"--no-cpu-baseline --copy-mib {copy_mib} --workload {w.name}")
+           f"--no-cpu-baseline --cold-reps 0 --copy-mib {copy_mib} --workload {w.name}")
     out = {"workload": w.name, "source_hash": source_hash(), "copy_mib": copy_mib,
            "commands": [cmd.format(c="FETCH_SIZE", d=fetch_dir), cmd.format(c="WRITE_SIZE", d=write_dir),
                         f"python bench.py --summarize-pmc {fetch_dir} {write_dir} --copy-mib {copy_mib}"
