@@ -125,6 +125,12 @@ SMALL_CASES = [
     # N = 512 with 128-token chunks: column halves split over wave pairs
     _wl("bf16_groups_n512", "bf16", 1, 2200, 4, 64, 512, 2, 128),    # grouped, ragged, G = 2
     _wl("bf16_hb2_n512", "bf16", 1, 8192, 8, 64, 512, 1, 128),       # 2 heads per block
+    # corners of the supported set on the single-head chunk output
+    _wl("bf16_q64_n512", "bf16", 1, 300, 2, 64, 512, 1, 64),
+    _wl("bf16_q256_n512", "bf16", 1, 600, 2, 64, 512, 2, 256, shift=-3.0),
+    _wl("bf16_q128_n448", "bf16", 2, 500, 3, 64, 448, 1, 128),
+    _wl("bf16_q256_n384", "bf16", 1, 700, 4, 64, 384, 4, 256, h0=False),
+    _wl("fp32_q128_n512", "fp32", 1, 260, 2, 64, 512, 1, 128),
 ]
 
 
