@@ -235,6 +235,35 @@ def test_stages_match_forward():
     check(f64(hTf), f64(hT), 1e-5, "hT forward vs stages (both fp32 states)")
 
 
+STAGE1_CASES = [
+    _wl("s1_groups_q128", "bf16", 1, 3000, 2, 64, 128, 1, 128),     # grouped, ragged
+    _wl("s1_n512_q128", "bf16", 1, 1000, 2, 64, 512, 2, 128),       # two state-pass column workgroups
+    _wl("s1_q64", "bf16", 2, 650, 3, 64, 64, 1, 64),
+    _wl("s1_q256", "bf16", 1, 2900, 3, 64, 256, 3, 256, shift=-2.0),
+    _wl("s1_fp32", "fp32", 1, 300, 2, 64, 64, 1, 64),
+]
+
+
+@pytest.mark.parametrize("w", STAGE1_CASES, ids=[c.name for c in STAGE1_CASES])
+def test_forward_stage1_outputs_match_stage1_bitwise(w):
+    """What ssd_forward leaves in its workspace as stage-1 output (G2, dtT, wT) equals the
+    stage-1 entry point's output bit for bit, on every element."""
+    dev = require_gpu()
+    inp = make_inputs(w, 21)
+    print(f"case {w}", flush=True)
+    d = to_dev(inp, dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    ws = ssd.workspace_for(prob, dev)
+    ws.fill_(0xFF)   # NaN patterns: every element must be written
+    ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                    workspace=ws)
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    torch.cuda.synchronize()
+    v = ssd.workspace_views(prob, ws)
+    for name, ref in (("G2", G2), ("dtT", dtT), ("wT", wT)):
+        assert torch.equal(v[name], ref), name
+
+
 def test_forward_timed_events():
     dev = require_gpu()
     w = _wl("timed", "bf16", 1, 1024, 2, 64, 128, 1, 128)
