@@ -15,8 +15,8 @@ each rep; and the fp64 CPU oracle timed on this host.
     python bench.py --step B     # the decode step (ssd_step) at batch B instead
     python bench.py --sweep      # the forward over 1K-256K tokens x state 64-512
 
-With ``--step B`` one step is one ``ssd_step`` call (one token for each of B
-sequences) on the heads of the workload (default: 32 heads, P=64, N=256, bf16),
+With ``--step B`` one step is one ``ssd_step`` call through a ``StepPlan`` (one
+token for each of B sequences) on the heads of the workload (default: 32 heads, P=64, N=256, bf16),
 its fp32 state resident in HBM; the line reports tokens/s and the step's HBM
 roofline (it reads and writes the whole state once).
 
@@ -207,8 +207,8 @@ def bench_step(args):
     y = torch.empty(b, H, P, device=dev, dtype=x.dtype)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        ssd.ssd_step(x, dt, d["A"], B, C, d["D"], h, y=y, stream=stream)
+    # the decode fast path: arguments checked once, each call only launches
+    step = ssd.StepPlan(x, dt, d["A"], B, C, d["D"], h, y=y, stream=stream).run
 
     for _ in range(args.warmup):
         step()

@@ -268,9 +268,8 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
         _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
     return y, hT
 
-def ssd_step(x, dt, A, B, C, D, h, *, y=None, stream=None):
-    """One decode step.  x [b,H,P], dt [b,H], B and C [b,G,N] (input dtype), A and D [H]
-    float32, h [b,H,P,N] float32 (updated in place).  Returns y [b,H,P]."""
+def _step_args(x, dt, A, B, C, D, h, y, stream):
+    """Checked ctypes arguments of ssd_step (and the output tensor y)."""
     if x.dim() != 3 or B.dim() != 3:
         raise ValueError("ssd_step takes x [b,H,P] and B [b,G,N]")
     b, H, P = x.shape
@@ -288,9 +287,36 @@ def ssd_step(x, dt, A, B, C, D, h, *, y=None, stream=None):
     if y is None:
         y = torch.empty(b, H, P, device=dev, dtype=io)
     _dev(y, "y", io, (b, H, P), dev)
-    _raise(lib().ssd_step(ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                          _ptr(D), _ptr(h), _ptr(y), _stream(stream, dev)), "ssd_step")
+    args = (ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(h), _ptr(y), _stream(stream, dev))
+    return problem, args, y
+
+
+def ssd_step(x, dt, A, B, C, D, h, *, y=None, stream=None):
+    """One decode step.  x [b,H,P], dt [b,H], B and C [b,G,N] (input dtype), A and D [H]
+    float32, h [b,H,P,N] float32 (updated in place).  Returns y [b,H,P]."""
+    _, args, y = _step_args(x, dt, A, B, C, D, h, y, stream)
+    _raise(lib().ssd_step(*args), "ssd_step")
     return y
+
+
+class StepPlan:
+    """ssd_step bound to fixed tensors, for decode loops: the arguments are checked once,
+    and run() only calls the C entry point (the caller refills x, dt, B and C in place
+    between calls; h is updated in place by each call).  The tensors are kept alive by
+    the plan; the stream is fixed when the plan is made (default: the current stream)."""
+
+    def __init__(self, x, dt, A, B, C, D, h, *, y=None, stream=None):
+        self._keep = (x, dt, A, B, C, D, h)
+        self._problem, self._args, self.y = _step_args(x, dt, A, B, C, D, h, y, stream)
+        self._fn = lib().ssd_step
+
+    def run(self):
+        """One step; returns y (the same tensor every call)."""
+        st = self._fn(*self._args)
+        if st != 0:
+            _raise(st, "ssd_step")
+        return self.y
 
 
 def workspace_views(problem: SsdProblem, workspace: torch.Tensor) -> dict:

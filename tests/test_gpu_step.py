@@ -132,3 +132,30 @@ def test_step_rejects_bad_arguments():
     with pytest.raises(ssd.SsdError) as ei:
         ssd.ssd_step(x, d["dt"].reshape(1, 4), d["A"], Bbad, Bbad, d["D"], hbad)
     assert ei.value.status == 3
+
+
+def test_step_plan_matches_step_calls():
+    """A StepPlan run with its inputs refilled in place gives, step after step, the same
+    bits as ssd_step called on the same values."""
+    dev = require_gpu()
+    w = Workload("plan", "bf16", 3, 6, 8, 64, 256, 2, 64, has_h0=True)
+    inp = make_inputs(w, 7)
+    d = to_dev(inp, dev)
+    b, H, P, G, N = 3, 8, 64, 2, 256
+    x = torch.empty(b, H, P, device=dev, dtype=torch.bfloat16)
+    dt = torch.empty(b, H, device=dev, dtype=torch.bfloat16)
+    B = torch.empty(b, G, N, device=dev, dtype=torch.bfloat16)
+    C = torch.empty_like(B)
+    h_plan = d["h0"].clone()
+    h_call = d["h0"].clone()
+    plan = ssd.StepPlan(x, dt, d["A"], B, C, d["D"], h_plan)
+    for t in range(w.seqlen):
+        x.copy_(d["x"][:, t]); dt.copy_(d["dt"][:, t]); B.copy_(d["B"][:, t]); C.copy_(d["C"][:, t])
+        y_plan = plan.run().clone()
+        y_call = ssd.ssd_step(d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"],
+                              d["B"][:, t].contiguous(), d["C"][:, t].contiguous(), d["D"], h_call)
+        torch.cuda.synchronize()
+        assert torch.equal(y_plan, y_call), t
+    assert torch.equal(h_plan, h_call)
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
+    check(f64(h_plan), ref["hT"], TOL["bf16"], "state after the plan's steps")
