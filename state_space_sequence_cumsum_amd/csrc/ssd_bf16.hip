@@ -6,10 +6,12 @@
 // "Kernel 3：compute_out" (decayed chunk output).
 //
 // Both kernels contract over tokens, which are the strided dimension of every
-// input tensor.  Tiles are copied into LDS in their natural token-major layout
-// with 16-byte writes and the token-packed MFMA operands are read back with
-// the gfx950 LDS transpose read (ds_read_b64_tr_b16), so no element-wise
-// transposition happens on the way in.
+// input tensor, and an MFMA operand packs 8 consecutive values of the
+// contraction index per lane.  The state pass copies its tiles into LDS in their
+// natural token-major layout with 16-byte writes and reads the token-packed
+// operands back with the gfx950 LDS transpose read (ds_read_b64_tr_b16); the
+// head-blocked chunk output transposes its x tile with byte permutes while
+// staging it, so that the many later reads of that tile are plain 16-byte reads.
 #include <algorithm>
 #include <type_traits>
 
