@@ -488,9 +488,9 @@ __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
 // the slice loads, the wait counts keep the next slice in flight while the
 // current one is multiplied.
 // ===========================================================================
-constexpr int kMaxN = 512;
-
-template <int Q, bool CORR>
+// NMX: the largest N this instance serves (128, 256 or 512); it sizes the S_eff
+// tile, so small states leave LDS for more workgroups per CU.
+template <int Q, bool CORR, int NMX>
 __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const bf16 *__restrict__ S,
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 Bs[Q * BP];
     // S_eff rows of N + 8 elements: an odd number of 16-byte units, so 16
     // consecutive rows read at the same column hit 16 distinct bank groups
-    __shared__ __attribute__((aligned(16))) bf16 Sf[P * (kMaxN + 8)];
+    __shared__ __attribute__((aligned(16))) bf16 Sf[P * (NMX + 8)];
     __shared__ __attribute__((aligned(16))) float Gs[Q];
     __shared__ __attribute__((aligned(16))) float We[Q];   // exp2(G_e - G_j), e = end of j's tile
 
@@ -1250,25 +1250,38 @@ hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const v
     return hipGetLastError();
 }
 
+template <int Q, int NMX>
+static hipError_t co_launch_n(const Shape &s, const void *x, const void *B, const void *C,
+                              const float *G2, const float *dtT, const void *S, const float *D,
+                              void *y, const float *Hg, const float *beta, int K, int ng,
+                              int c_first, int nc_grid, hipStream_t st)
+{
+    const int xcd = (nc_grid % 8 == 0) ? 1 : 0;
+    const dim3 grid((unsigned)(nc_grid * s.b * s.H)), block(2 * Q);
+    if (Hg != nullptr)
+        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, true, NMX>), grid, block, 0, st,
+                           (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
+                           (const bf16 *)S, D, (bf16 *)y, Hg, beta, (int)s.L, (int)s.H, (int)s.G,
+                           (int)s.N, (int)s.nc, (int)s.Lp, K, ng, c_first, nc_grid, xcd);
+    else
+        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, false, NMX>), grid, block, 0, st,
+                           (const bf16 *)x, (const bf16 *)B, (const bf16 *)C, G2, dtT,
+                           (const bf16 *)S, D, (bf16 *)y, Hg, beta, (int)s.L, (int)s.H, (int)s.G,
+                           (int)s.N, (int)s.nc, (int)s.Lp, K, ng, c_first, nc_grid, xcd);
+    return hipGetLastError();
+}
+
 template <int Q>
 static hipError_t co_launch(const Shape &s, const void *x, const void *B, const void *C,
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, const float *Hg, const float *beta, int K, int ng,
                             int c_first, int nc_grid, hipStream_t st)
 {
-    const int xcd = (nc_grid % 8 == 0) ? 1 : 0;
-    const dim3 grid((unsigned)(nc_grid * s.b * s.H)), block(2 * Q);
-    if (Hg != nullptr)
-        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, true>), grid, block, 0, st, (const bf16 *)x,
-                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
-                           Hg, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp,
-                           K, ng, c_first, nc_grid, xcd);
-    else
-        hipLaunchKernelGGL((chunk_out_bf16_kernel<Q, false>), grid, block, 0, st, (const bf16 *)x,
-                           (const bf16 *)B, (const bf16 *)C, G2, dtT, (const bf16 *)S, D, (bf16 *)y,
-                           Hg, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp,
-                           K, ng, c_first, nc_grid, xcd);
-    return hipGetLastError();
+    if (s.N <= 128)
+        return co_launch_n<Q, 128>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
+    if (s.N <= 256)
+        return co_launch_n<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
+    return co_launch_n<Q, 512>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
 }
 
 // heads per workgroup of the head-blocked chunk output: the largest divisor of

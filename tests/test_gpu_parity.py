@@ -264,6 +264,21 @@ def test_forward_stage1_outputs_match_stage1_bitwise(w):
         assert torch.equal(v[name], ref), name
 
 
+@pytest.mark.parametrize("w", [_wl("nofinal_groups", "bf16", 1, 3000, 2, 64, 128, 1, 128),
+                               _wl("nofinal_fp32", "fp32", 1, 300, 2, 64, 64, 1, 64)],
+                         ids=["bf16-grouped", "fp32"])
+def test_forward_without_final_state(w):
+    """hT = NULL (want_final=False): the same y, bit for bit, and nothing else written."""
+    dev = require_gpu()
+    inp = make_inputs(w, 31)
+    d = to_dev(inp, dev)
+    y1, h1 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk)
+    y2, h2 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                             want_final=False)
+    torch.cuda.synchronize()
+    assert h2 is None and torch.equal(y1, y2)
+
+
 def test_forward_timed_events():
     dev = require_gpu()
     w = _wl("timed", "bf16", 1, 1024, 2, 64, 128, 1, 128)
