@@ -157,6 +157,25 @@ ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, c
                     const void *B, const void *C, const float *D, float *h, void *y,
                     void *stream);
 
+/* How ssd_forward launches `problem` on this GPU: the per-shape choices of the state pass
+ * (chunks per group, groups, state columns per workgroup) and of the chunk output (the
+ * head-blocked kernel or the one-head kernel, heads per workgroup, column halves split over
+ * wave pairs), with the workgroup counts.  Host-only; for reports and tuning. */
+typedef struct {
+    int32_t sp_group_chunks;    /* chunks per state-pass group (K) */
+    int32_t sp_groups;          /* state-pass groups per (batch, head) chain (ng) */
+    int32_t sp_columns;         /* state columns per state-pass workgroup */
+    int32_t sp_workgroups;      /* state-pass workgroups */
+    int32_t scan;               /* 1 when the group scan runs (sp_groups > 1) */
+    int32_t co_head_blocked;    /* 1: full chunks on the head-blocked kernel */
+    int32_t co_heads_per_block; /* heads per chunk-output workgroup (1: one-head kernel) */
+    int32_t co_column_split;    /* 2: state columns split over wave pairs (N = 512) */
+    int32_t co_workgroups;      /* chunk-output workgroups (ragged last chunk included) */
+    int32_t co_threads;         /* threads per head-blocked (else one-head) workgroup */
+} ssd_launch_plan;
+
+ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan);
+
 /* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
                                 size_t *off_wT, size_t *off_S);

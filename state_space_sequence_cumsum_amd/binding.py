@@ -43,6 +43,12 @@ class SsdProblem(ctypes.Structure):
         return -(-self.seqlen // self.chunk)
 
 
+class SsdLaunchPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "sp_group_chunks", "sp_groups", "sp_columns", "sp_workgroups", "scan", "co_head_blocked",
+        "co_heads_per_block", "co_column_split", "co_workgroups", "co_threads")]
+
+
 _lib = None
 
 
@@ -67,6 +73,7 @@ def lib():
         L.ssd_forward_timed.argtypes = L.ssd_forward.argtypes + [ctypes.POINTER(vp)]
         L.ssd_forward_timed.restype = st
         L.ssd_step.argtypes, L.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
+        L.ssd_plan.argtypes, L.ssd_plan.restype = [P, ctypes.POINTER(SsdLaunchPlan)], st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
         L.ssd_last_hip_error.argtypes, L.ssd_last_hip_error.restype = [], ctypes.c_int
         _lib = L
@@ -118,6 +125,13 @@ def ssd_workspace_layout(problem: SsdProblem) -> tuple[int, int, int, int]:
     _raise(lib().ssd_workspace_layout(ctypes.byref(problem), *[ctypes.byref(o) for o in offs]),
            "ssd_workspace_layout")
     return tuple(o.value for o in offs)
+
+
+def ssd_plan(problem: SsdProblem) -> dict:
+    """How ssd_forward launches `problem` (host only): field name -> value."""
+    plan = SsdLaunchPlan()
+    _raise(lib().ssd_plan(ctypes.byref(problem), ctypes.byref(plan)), "ssd_plan")
+    return {n: getattr(plan, n) for n, _ in SsdLaunchPlan._fields_}
 
 
 def ssd_status_string(status: int) -> str:

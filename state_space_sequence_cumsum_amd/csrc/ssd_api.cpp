@@ -139,6 +139,25 @@ ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size
     return SSD_OK;
 }
 
+ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (plan == nullptr) return SSD_ERR_NULL_ARG;
+    const ssd::LaunchPlan lp = ssd::plan_of(make_shape(problem));
+    plan->sp_group_chunks = lp.sp_group_chunks;
+    plan->sp_groups = lp.sp_groups;
+    plan->sp_columns = lp.sp_columns;
+    plan->sp_workgroups = lp.sp_workgroups;
+    plan->scan = lp.scan;
+    plan->co_head_blocked = lp.co_head_blocked;
+    plan->co_heads_per_block = lp.co_heads_per_block;
+    plan->co_column_split = lp.co_column_split;
+    plan->co_workgroups = lp.co_workgroups;
+    plan->co_threads = lp.co_threads;
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A, float *G2,
                             float *dtT, float *wT, void *stream)
 {

@@ -1296,6 +1296,43 @@ static int heads_per_block(const Shape &s)
     return best;
 }
 
+LaunchPlan plan_of(const Shape &s)
+{
+    LaunchPlan lp;
+    const Grouping gp = state_pass_groups(s);
+    lp.sp_group_chunks = gp.K;
+    lp.sp_groups = gp.ng;
+    if (!s.bf16) {   // fp32 kernels: one serial chain per (b, h) and 64 columns, one (chunk, head) per workgroup
+        lp.sp_columns = 64;
+        lp.sp_workgroups = (int)(s.b * s.H * (s.N / 64));
+        lp.scan = 0;
+        lp.co_head_blocked = 0;
+        lp.co_heads_per_block = 1;
+        lp.co_column_split = 1;
+        lp.co_workgroups = (int)(s.nc * s.b * s.H);
+        lp.co_threads = (int)s.Q;
+        return lp;
+    }
+    lp.sp_columns = sp_cols(s);
+    lp.sp_workgroups = (int)(s.b * s.H * (s.N / lp.sp_columns) * gp.ng);
+    lp.scan = gp.ng > 1 ? 1 : 0;
+    lp.co_head_blocked = head_blocked(s) ? 1 : 0;
+    if (lp.co_head_blocked) {
+        const int64_t nc_full = s.L / s.Q;
+        lp.co_heads_per_block = heads_per_block(s);
+        lp.co_column_split = s.N > 256 ? 2 : 1;
+        lp.co_workgroups = (int)(nc_full * s.b * s.G * (s.H / s.G / lp.co_heads_per_block) +
+                                 (nc_full < s.nc ? s.b * s.H : 0));
+        lp.co_threads = (int)(2 * s.Q * lp.co_column_split);
+    } else {
+        lp.co_heads_per_block = 1;
+        lp.co_column_split = 1;
+        lp.co_workgroups = (int)(s.nc * s.b * s.H);
+        lp.co_threads = (int)(2 * s.Q);
+    }
+    return lp;
+}
+
 template <int Q, int NN>
 static hipError_t hb_launch(const Shape &s, const void *x, const void *B, const void *C,
                             const float *G2, const float *dtT, const void *S, const float *D,

@@ -48,6 +48,13 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const 
                                       const float *Hg, const void *Hb, const float *beta,
                                       hipStream_t st);
 
+// The launch configuration of the forward pass for shape s (host only).
+struct LaunchPlan {
+    int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
+    int co_head_blocked, co_heads_per_block, co_column_split, co_workgroups, co_threads;
+};
+LaunchPlan plan_of(const Shape &s);
+
 // One decode step per (batch, head), h updated in place (ssd_step.hip).
 hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, float *h, void *y,

@@ -152,3 +152,34 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         ssd.ssd_forward(x, torch.zeros(1, 64, 2, dtype=torch.bfloat16), torch.zeros(2), B, B,
                         torch.zeros(2), chunk=64)
+
+
+def test_launch_plan_per_shape():
+    """ssd_plan reports the per-shape launch choices (host only)."""
+    # headline: 8 groups of 8 chunks, one state-pass workgroup per CU, 8 heads per
+    # head-blocked chunk-output workgroup of 2 Q threads
+    assert ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256)) == dict(
+        sp_group_chunks=8, sp_groups=8, sp_columns=256, sp_workgroups=256, scan=1,
+        co_head_blocked=1, co_heads_per_block=8, co_column_split=1, co_workgroups=256,
+        co_threads=512)
+    # N = 512 with 128-token chunks: two 256-column state-pass workgroups per chain, the
+    # chunk output's columns split over wave pairs
+    p512 = ssd.ssd_plan(_p(seqlen=65536, dstate=512, chunk=128))
+    assert (p512["sp_columns"], p512["sp_groups"], p512["co_column_split"], p512["co_threads"]) == (256, 4, 2, 512)
+    assert p512["sp_workgroups"] == 32 * 2 * 4 and p512["co_workgroups"] == 512 * (32 // p512["co_heads_per_block"])
+    # ragged: 23 full chunks head-blocked (one head per block here) plus the last chunk of
+    # each (batch, head) on the one-head kernel
+    pr = ssd.ssd_plan(_p(seqlen=3000, nheads=2, dstate=128, chunk=128))
+    assert pr["co_head_blocked"] == 1 and pr["co_heads_per_block"] == 1
+    assert pr["co_workgroups"] == 23 * 2 + 2
+    # 64-token chunks and N = 384 use the one-head kernel
+    for kw in (dict(chunk=64), dict(dstate=384, chunk=128)):
+        q = ssd.ssd_plan(_p(**kw))
+        assert q["co_head_blocked"] == 0 and q["co_heads_per_block"] == 1
+    # fp32: one serial chain per (batch, head) and 64 columns
+    f = ssd.ssd_plan(_p(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"))
+    assert (f["sp_groups"], f["sp_columns"], f["sp_workgroups"], f["scan"], f["co_head_blocked"]) == (1, 64, 4, 0, 0)
+    # the plan refuses what the forward refuses
+    with pytest.raises(ssd.SsdError) as ei:
+        ssd.ssd_plan(_p(dstate=96))
+    assert ei.value.status == 3
