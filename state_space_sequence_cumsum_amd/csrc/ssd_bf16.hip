@@ -91,6 +91,17 @@ constexpr int lcm3(int a, int b, int c)
     return ab / gcd_(ab, c) * c;
 }
 
+// Row pitch (elements) of the token-major B tile: a multiple of 32 bytes that is
+// 64 or 192 mod 256, so the four rows one 32-lane pass of the MFMA operand's
+// transpose read touches (32 bytes each, at two column offsets 32 bytes apart)
+// fall on distinct banks.
+constexpr int b_pitch(int cols)
+{
+    int b = (cols * 2 + 31) / 32 * 32;
+    while ((b % 256) != 64 && (b % 256) != 192) b += 32;
+    return b / 2;
+}
+
 template <int Q, int N>   // N = NR, the columns of one workgroup
 struct SpCfg {
     static constexpr int P = 64;
@@ -100,7 +111,7 @@ struct SpCfg {
     static constexpr int NTHR = 64 * NWAVE;
     static constexpr int RTW = 1;                                // n tiles per wave
     static constexpr int CTW = (N == 256) ? 2 : 1;               // p tiles per wave
-    static constexpr int BP = tr_pitch(N);                       // token-major B rows
+    static constexpr int BP = b_pitch(N);                        // token-major B rows
     static constexpr int XRP = tr_pitch(P);                      // token-major x rows
     static constexpr int XKP = TS + 8;                           // k-packed x~ rows
     static constexpr int SSP = N + 8;                            // chunk-start state staging rows
@@ -191,9 +202,12 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
         bt_[r] = t;
         blo[r] = t * BP + c8 * 8;
     }
+    // x: piece id is 16 bytes (8 p) of one token row; the two 8-lane halves of each
+    // 16 lanes take rows t and t + 4, whose LDS rows are 128 bytes apart mod 256
 #pragma unroll
     for (int r = 0; r < XPT; ++r) {
-        const int id = min(tid + NTHR * r, XPIECES - 1), t = id >> 3, c8 = id & 7;
+        const int id = min(tid + NTHR * r, XPIECES - 1), c8 = id & 7, g = id >> 4;
+        const int t = (g >> 2) * 8 + (g & 3) + 4 * ((id >> 3) & 1);
         xo[r] = c8 * 16;
         xt_[r] = t;
         xlo[r] = t * XRP + c8 * 8;
