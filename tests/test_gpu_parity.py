@@ -139,6 +139,32 @@ def test_forward_parity_small(w):
     _check_forward(w, seed=0)
 
 
+def _random_cases(n, seed=2026):
+    """n shapes drawn from the supported set (any L, H divisible by G, N a multiple of 64 up
+    to 512, Q in {64, 128, 256}, bf16 or fp32, with or without h0), sized for the oracle."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        Q = int(rng.choice([64, 128, 256]))
+        N = int(64 * rng.integers(1, 9))
+        G = int(rng.choice([1, 2, 3]))
+        H = G * int(rng.integers(1, 4))
+        b = int(rng.integers(1, 3))
+        L = int(rng.integers(1, 1500))
+        dtype = "fp32" if rng.random() < 0.25 else "bf16"
+        cases.append(_wl(f"rand{k}_{dtype}_b{b}L{L}H{H}G{G}N{N}Q{Q}", dtype, b, L, H, 64, N, G, Q,
+                         h0=bool(rng.random() < 0.6), shift=float(rng.choice([-4.0, -2.0, 0.0]))))
+    return cases
+
+
+RANDOM_CASES = _random_cases(12)
+
+
+@pytest.mark.parametrize("w", RANDOM_CASES, ids=[c.name for c in RANDOM_CASES])
+def test_forward_parity_random_shapes(w):
+    _check_forward(w, seed=7)
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_forward_parity_seeds(seed):
     _check_forward(_wl("bf16_seeds", "bf16", 1, 512, 4, 64, 128, 1, 128), seed=seed)
