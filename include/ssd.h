@@ -40,8 +40,10 @@
  * h0 and hT may be the same buffer.
  *
  * Supported set: dtype SSD_F32 or SSD_BF16; headdim 64; dstate a multiple of 64
- * up to 512; chunk 64, 128 or 256; batch * nheads <= 65535; chunk * nheads *
- * headdim and chunk * ngroups * dstate below 2^31; any seqlen >= 1 (a partial last chunk is
+ * up to 512; chunk 64, 128 or 256; batch * nheads <= 65535; seqlen * nheads * headdim
+ * and seqlen * ngroups * dstate below 2^30; chunk * nheads * headdim and chunk *
+ * ngroups * dstate below 2^31; ceil(seqlen / chunk) * batch * nheads below 2^31 (the
+ * workgroup count of the one-head output kernel); any seqlen >= 1 (a partial last chunk is
  * zero-padded, which is exact: a token with dt = 0 and x = B = C = 0 changes
  * nothing).  Other shapes return SSD_ERR_UNSUPPORTED.
  *

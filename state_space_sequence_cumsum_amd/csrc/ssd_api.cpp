@@ -36,10 +36,13 @@ ssd_status check_shape(const ssd_problem *p)
     if (p->headdim != 64) return SSD_ERR_UNSUPPORTED;
     if (p->dstate % 64 != 0 || p->dstate > 512) return SSD_ERR_UNSUPPORTED;
     if (p->chunk != 64 && p->chunk != 128 && p->chunk != 256) return SSD_ERR_UNSUPPORTED;
-    // 32-bit grid and index limits of the kernels
+    // 32-bit grid and index limits of the kernels (each factor bounded before a product)
+    if (p->batch > 65535 || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->batch * p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->seqlen > (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
-    if (p->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    // one-head chunk output: one workgroup per (chunk, batch, head) in a 1-D grid
+    if ((p->seqlen + p->chunk - 1) / p->chunk * p->batch * p->nheads >= (int64_t(1) << 31))
+        return SSD_ERR_UNSUPPORTED;
     // in-chunk element offsets are 32-bit, and so are byte offsets within one batch
     // of x and of B / C
     if (p->chunk * p->nheads * p->headdim >= (int64_t(1) << 31)) return SSD_ERR_UNSUPPORTED;

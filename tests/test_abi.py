@@ -183,3 +183,22 @@ def test_launch_plan_per_shape():
     with pytest.raises(ssd.SsdError) as ei:
         ssd.ssd_plan(_p(dstate=96))
     assert ei.value.status == 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    # per-batch extents of x and of B / C: below 2^30 elements
+    (dict(seqlen=(1 << 30) // (32 * 64) - 1, nheads=32, dstate=64), 0),
+    (dict(seqlen=(1 << 30) // (32 * 64), nheads=32, dstate=64), 3),
+    (dict(seqlen=(1 << 30) // 512 - 1, nheads=1, dstate=512), 0),
+    (dict(seqlen=(1 << 30) // 512, nheads=1, dstate=512), 3),
+    # batch * heads
+    (dict(batch=65535, nheads=1, seqlen=64, dstate=64, chunk=64), 0),
+    (dict(batch=65536, nheads=1, seqlen=64, dstate=64, chunk=64), 3),
+    (dict(batch=1 << 40, nheads=4), 3),             # no overflow in the product
+    (dict(batch=4, nheads=1 << 40, ngroups=1), 3),
+    # the one-head output kernel's workgroup count
+    (dict(batch=9362, nheads=7, ngroups=7, seqlen=(1 << 21) + 192, dstate=64, chunk=64), 3),
+    (dict(batch=9362, nheads=7, ngroups=7, seqlen=1 << 15, dstate=64, chunk=64), 0),
+])
+def test_validate_size_limits(kw, status):
+    assert ssd.ssd_validate(_p(**kw)) == status
