@@ -516,7 +516,10 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     constexpr int XP = Q + 8, BP = frag_pitch(NS);
     constexpr int BPC = Q * (NS / 8) / NTHR;   // 16-byte B pieces per thread per slice
     constexpr int SPC = P * (NS / 8) / NTHR;   // 16-byte S pieces per thread per 64 columns
-    constexpr int SPART = 256;                 // S_eff columns staged per round
+    // S_eff columns staged per round: the pieces of a round (S in bf16, H_g in fp32)
+    // are in flight together, so with 64-token chunks (four pieces per thread per 64
+    // columns) and the correction a round is halved to stay within the registers
+    constexpr int SPART = (CORR && SPC >= 4) ? 128 : 256;
     static_assert(BPC >= 1 && SPC >= 1, "slice staging cover");
     // (dt x)^T [p][position]: within each 16-token group the token at offset o is
     // kept at position o with its middle two 4-token blocks swapped, so the
@@ -815,6 +818,9 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     constexpr int SLICE_EL = Q * (NSW / 8);     // 16-byte pieces of one B slice
     constexpr int BPC = SPL * SLICE_EL / NTHR;  // 16-byte B pieces per thread per step
     constexpr int SPT = P * (NN / 8) / NTHR;    // 16-byte S pieces per thread
+    // the next head's S (and H_g) pieces are requested before the decay products when
+    // they take at most 32 registers per thread, else after them
+    constexpr bool EARLY_S = SPL == 1 && SPT * (CORR ? 2 : 1) <= 8;
     static_assert(BPC >= 1 && SPT >= 1 && NN % 16 == 0 && NSL % SPL == 0, "staging cover");
     static_assert(SPL == 1 || SPL == 2, "one or two column halves");
     constexpr int NTILE = NI * (NI + 1) / 2;    // causal tiles
@@ -1067,10 +1073,11 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
             for (int pp = 0; pp < 2; ++pp)
                 mma(ya[pp], *reinterpret_cast<const bf16x8 *>(sfrow + pp * 32 * SFP + (hf * NF + f) * 16), cfa[f]);
 
-        // next head's chunk-start state: with one column half per wave its latency
-        // hides behind the decay-matrix products; with two (twice the registers per
-        // thread) it is issued after them
-        if constexpr (SPL == 1) load_s(RS, hl + 1);
+        // next head's chunk-start state: when its pieces fit in 32 registers per
+        // thread its latency hides behind the decay-matrix products; otherwise (two
+        // column halves, or a 256-column state over 256 threads) it is issued after
+        // them, which keeps the kernel within 256 registers (two waves per SIMD)
+        if constexpr (EARLY_S) load_s(RS, hl + 1);
         // Y^T = exp2(G_i) Y^T + M' x
         const float gi = Gs[i_loc];
         const float si = fast_exp2(gi);
@@ -1124,8 +1131,8 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
             mfma_tile(I, m);
         }
 
+        if constexpr (!EARLY_S) load_s(RS, hl + 1);
         if constexpr (SPL == 2) {
-            load_s(RS, hl + 1);
             // swap partial Y^T with the other half of the row tile: this wave keeps
             // rows pp = hf and sends rows 1 - hf
             float *xc = reinterpret_cast<float *>(Un + CB_EL) + I * 2048 + 4 * lane;

@@ -121,6 +121,7 @@ SMALL_CASES = [
     _wl("bf16_groups_q128", "bf16", 1, 3000, 2, 64, 128, 1, 128),
     _wl("bf16_groups_q256", "bf16", 2, 2900, 3, 64, 256, 3, 256),
     _wl("bf16_groups_q64", "bf16", 1, 1100, 1, 64, 64, 1, 64, h0=False),
+    _wl("bf16_groups_q64_n256", "bf16", 1, 1500, 2, 64, 256, 1, 64),   # S_eff staged in 2 rounds
     _wl("bf16_groups_odd", "bf16", 1, 1100, 43, 64, 256, 1, 128),   # 3 chunks per group
     # N = 512 with 128-token chunks: column halves split over wave pairs
     _wl("bf16_groups_n512", "bf16", 1, 2200, 4, 64, 512, 2, 128),    # grouped, ragged, G = 2
