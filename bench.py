@@ -3,7 +3,8 @@
 
 One step = one whole forward (chunk cumsum, state pass, chunk output) over the
 16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints one
-JSON line:  tokens/s of ``ssd_forward`` over K steps back to back; per-stage
+JSON line:  tokens/s of ``ssd_forward`` over K steps back to back (called through
+a ``ForwardPlan``, or with ``--graph`` replayed from a HIP graph); per-stage
 durations (mean, median, p10, p90) from HIP events that the library records on
 the launch stream between its stages, over K further steps run right after; the
 roofline of the dominant stage from its algorithmic bytes and flops; ``cold``:
@@ -12,6 +13,7 @@ each rep; and the fp64 CPU oracle timed on this host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--copy-mib M]
+    python bench.py --graph      # the timed forwards replayed from a HIP graph
     python bench.py --step B     # the decode step (ssd_step) at batch B instead
     python bench.py --sweep      # the forward over 1K-256K tokens x state 64-512
 
@@ -332,6 +334,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="forwards timed after a cache flush each (0: skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one forward recorded into a HIP graph")
     ap.add_argument("--sweep", action="store_true",
                     help="time the forward over the 1K-256K token x state 64-512 grid")
     ap.add_argument("--step", type=int, default=0, metavar="B",
@@ -380,6 +384,23 @@ def main():
         ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
                         y=y, hT=hT, workspace=ws, stream=stream, events=events)
 
+    # the timed loop calls the C entry point through a plan (arguments checked once), or
+    # with --graph replays one forward recorded into a HIP graph on a side stream
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        gplan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=side)
+        forward()                       # kernels loaded before the capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            gplan.run()
+        timed = graph.replay
+    else:
+        plan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                               chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream)
+        timed = plan.run
+
     if args.copy_mib > 0:   # a plain copy of known size, outside the timed region
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -389,14 +410,14 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        forward()
+        timed()
     torch.cuda.synchronize()
 
     # --- timed region: K whole forwards through the C ABI, nothing else on the stream ---
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        forward()
+        timed()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -474,6 +495,7 @@ def main():
         "kernels": {n: {k: round(v, 4) for k, v in kern[n].items()} for n in names},
         "stage_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
         "roofline": roof,
+        "launch": "graph" if args.graph else "plan",
     }
     if cold:
         out["cold"] = {"reps": len(cold), "flush_mib": FLUSH_MIB,

@@ -242,13 +242,9 @@ def workspace_for(problem: SsdProblem, device) -> torch.Tensor:
     return torch.empty(n, device=device, dtype=torch.uint8)
 
 
-def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want_final=True,
-                workspace=None, stream=None, events=None):
-    """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None).
-
-    ``events``: optional 4 recorded-once ``torch.cuda.Event`` objects; they are
-    re-recorded on the launch stream around the three stages (ssd_forward_timed).
-    """
+def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream):
+    """Checked ctypes arguments of ssd_forward, with the outputs and the workspace
+    (allocated here when not given)."""
     problem = problem_of(x, B, chunk)
     b, L, H, G, P, N, Q, nc = _dims(problem)
     io = _io_dtype(problem)
@@ -273,6 +269,18 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
     nbytes = workspace.numel() * workspace.element_size()
     args = (ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             _ptr(h0), _ptr(y), _ptr(hT), _ptr(workspace), nbytes, _stream(stream, dev))
+    return problem, args, y, hT, workspace
+
+
+def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want_final=True,
+                workspace=None, stream=None, events=None):
+    """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None).
+
+    ``events``: optional 4 recorded-once ``torch.cuda.Event`` objects; they are
+    re-recorded on the launch stream around the three stages (ssd_forward_timed).
+    """
+    _, args, y, hT, _ = _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace,
+                                      stream)
     if events is None:
         _raise(lib().ssd_forward(*args), "ssd_forward")
     else:
@@ -281,6 +289,30 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
         arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
         _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
     return y, hT
+
+
+class ForwardPlan:
+    """ssd_forward bound to fixed tensors: the arguments are checked and the outputs and
+    workspace allocated once, and run() only calls the C entry point (the caller refills
+    the inputs in place between calls).  The plan keeps its tensors alive; the stream is
+    fixed when the plan is made (default: the current stream), so a plan made for a
+    capture stream can be recorded into a HIP graph (the forward allocates, clears and
+    synchronises nothing)."""
+
+    def __init__(self, x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None,
+                 want_final=True, workspace=None, stream=None):
+        self._keep = (x, dt, A, B, C, D, h0)
+        self._problem, self._args, self.y, self.hT, self.workspace = _forward_args(
+            x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream)
+        self._fn = lib().ssd_forward
+
+    def run(self):
+        """One forward; returns (y, hT) (the same tensors every call)."""
+        st = self._fn(*self._args)
+        if st != 0:
+            _raise(st, "ssd_forward")
+        return self.y, self.hT
+
 
 def _step_args(x, dt, A, B, C, D, h, y, stream):
     """Checked ctypes arguments of ssd_step (and the output tensor y)."""
