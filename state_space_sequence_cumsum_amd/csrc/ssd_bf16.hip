@@ -287,7 +287,6 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     const int offA = tr_off_natural(lane, BP);
     const int offB = (lane & 31) * XKP + 8 * (lane >> 5);
 
-    // chunk start (sub-step u, u % NSUB == 0): store the chunk-start state, decay
     // chunk start (sub-step u, u % NSUB == 0): the chunk-start state goes to the
     // LDS staging tile as bf16 (row p, columns n), then the state decays
     auto chunk_start = [&](int ka) {
