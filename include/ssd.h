@@ -37,7 +37,9 @@
  * memory, never synchronises and keeps no global mutable state apart from the
  * thread-local HIP error code.  Work is asynchronous on `stream`; buffers must stay
  * valid until it completes.  Inputs and outputs must not overlap, except that
- * h0 and hT may be the same buffer.
+ * h0 and hT may be the same buffer.  Since a call issues only kernel launches (no
+ * allocation, memset, copy or synchronisation), ssd_forward, the three stages and
+ * ssd_step may be recorded into a HIP graph on a capturing stream and replayed.
  *
  * Supported set: dtype SSD_F32 or SSD_BF16; headdim 64; dstate a multiple of 64
  * up to 512; chunk 64, 128 or 256; batch * nheads <= 65535; seqlen * nheads * headdim
