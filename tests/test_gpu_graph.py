@@ -1,9 +1,11 @@
-"""Forward and decode step bound once (ForwardPlan, StepPlan) and recorded into HIP graphs.
+"""Forward and decode step bound once (ForwardPlan, StepPlan), and the forward, the decode
+step and the three stages recorded into HIP graphs.
 
-The library allocates, clears and synchronises nothing inside ssd_forward or ssd_step,
-so both can be captured on a side stream.  Every replay is compared bit for bit with
-the eager call on the same inputs, with eager work (output poisoning, input refills)
-and synchronisations between the replays; one case is also checked against the oracle.
+The library allocates, clears and synchronises nothing inside its entry points, so they
+can be captured on a side stream.  Every replay is compared bit for bit with the eager
+call on the same inputs, with eager work (output poisoning, input refills) and
+synchronisations between the replays; the refilled forward is also checked against the
+oracle.
 """
 import pytest
 import torch
@@ -129,3 +131,32 @@ def test_step_graph_replay():
     del y_warm
     ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
     check(f64(h_graph), ref["hT"], TOL["bf16"], "state after the replays")
+
+
+def test_stages_graph_replay():
+    """The three stage entry points recorded into one graph on a side stream, with every
+    intermediate preallocated, replay to the eager stages' outputs bit for bit."""
+    dev = require_gpu()
+    w = _wl("stages_graph", "bf16", 2, 1280, 4, 64, 128, 2, 64)
+    d = to_dev(make_inputs(w, 11), dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"])
+    y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
+    torch.cuda.synchronize()
+    outs = {"G2": G2, "dtT": dtT, "wT": wT, "S": S, "hT": hT, "y": y}
+    ref = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, wT, stream=side)
+        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"], S=S, hT=hT, stream=side)
+        ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"], y=y, stream=side)
+    for k in range(3):
+        for t in outs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(t, ref[name]), f"replay {k}: {name}"
