@@ -123,11 +123,11 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
 
 /* The whole forward pass: stage 1, 2 and 3 on `stream`, no host synchronisation.
  * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds the intermediates.
- * On return G2, dtT and wT hold the stage-1 outputs.  For bf16 problems the state pass
- * may split each (batch, head) chain of chunks into groups that run in parallel from a
- * zero state (the jump is linear), combine the group-final states with a short scan and
- * let stage 3 add the carried-in state; S then holds chunk-start states relative to
- * their group, and its contents are otherwise unspecified.  h0 may be NULL; hT may be
+ * On return G2, dtT and wT hold the stage-1 outputs.  The state pass may split each
+ * (batch, head) chain of chunks into groups that run in parallel from a zero state (the
+ * jump is linear), combine the group-final states with a short scan and let stage 3 add
+ * the carried-in state; S then holds chunk-start states relative to their group, and
+ * its contents are otherwise unspecified.  h0 may be NULL; hT may be
  * NULL (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
                        const float *A, const void *B, const void *C, const float *D,

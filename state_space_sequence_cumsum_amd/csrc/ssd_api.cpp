@@ -105,7 +105,7 @@ Layout layout_of(const ssd::Shape &s)
     l.gam = l.ug + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * sizeof(float)) : 0);
     l.beta = l.gam + (grouped ? align_up(bh * l.gp.ng * sizeof(float)) : 0);
     l.hb = l.beta + (grouped ? align_up(bh * s.nc * sizeof(float)) : 0);
-    l.total = l.hb + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * 2) : 0);
+    l.total = l.hb + ((grouped && s.bf16) ? align_up(bh * l.gp.ng * s.P * s.N * 2) : 0);
     return l;
 }
 

@@ -1237,14 +1237,11 @@ hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, 
 Grouping state_pass_groups(const Shape &s)
 {
     Grouping gp;
-    if (!s.bf16) {
-        gp.K = (int)s.nc;
-        gp.ng = 1;
-        return gp;
-    }
-    // about one state-pass workgroup per CU (each takes most of a CU's LDS)
-    const int64_t units = s.b * s.H * (s.N / sp_cols(s));
-    int64_t ng = (256 + units - 1) / units;
+    // bf16: about one state-pass workgroup per CU (each takes most of a CU's LDS);
+    // fp32 (64 columns per workgroup): as many as the LDS of its Q lets a CU hold
+    const int64_t units = s.b * s.H * (s.N / (s.bf16 ? sp_cols(s) : 64));
+    const int64_t target = s.bf16 ? 256 : 256 * (s.Q == 64 ? 4 : s.Q == 128 ? 2 : 1);
+    int64_t ng = (target + units - 1) / units;
     ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc));
     const int64_t K = (s.nc + ng - 1) / ng;
     gp.K = (int)K;
@@ -1257,16 +1254,18 @@ hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const v
                                      const float *h0, void *S, float *hT, float *Ug, void *Hb,
                                      float *gam, float *beta, hipStream_t st)
 {
-    if (!s.bf16 || gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
-    hipError_t e = sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st);
+    if (gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
+    hipError_t e = s.bf16 ? sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st)
+                          : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta,
+                                                          gp.K, gp.ng, st);
     if (e != hipSuccess) return e;
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
     // fp32 group-start states are read only by single-head chunk-output launches
     int g_f32 = 1;
-    if (head_blocked(s)) g_f32 = (s.L % s.Q != 0) ? (int)((s.nc - 1) / gp.K) : gp.ng;
-    hipLaunchKernelGGL(group_scan_kernel<8>, grid, dim3(256), 0, st, Ug, gam, hT, (bf16 *)Hb, PN,
-                       gp.ng, g_f32);
+    if (s.bf16 && head_blocked(s)) g_f32 = (s.L % s.Q != 0) ? (int)((s.nc - 1) / gp.K) : gp.ng;
+    hipLaunchKernelGGL(group_scan_kernel<8>, grid, dim3(256), 0, st, Ug, gam, hT,
+                       s.bf16 ? (bf16 *)Hb : (bf16 *)nullptr, PN, gp.ng, g_f32);
     return hipGetLastError();
 }
 
@@ -1322,10 +1321,10 @@ LaunchPlan plan_of(const Shape &s)
     const Grouping gp = state_pass_groups(s);
     lp.sp_group_chunks = gp.K;
     lp.sp_groups = gp.ng;
-    if (!s.bf16) {   // fp32 kernels: one serial chain per (b, h) and 64 columns, one (chunk, head) per workgroup
+    if (!s.bf16) {   // fp32 kernels: 64 columns per state-pass workgroup, one (chunk, head) per output workgroup
         lp.sp_columns = 64;
-        lp.sp_workgroups = (int)(s.b * s.H * (s.N / 64));
-        lp.scan = 0;
+        lp.sp_workgroups = (int)(s.b * s.H * (s.N / 64) * gp.ng);
+        lp.scan = gp.ng > 1 ? 1 : 0;
         lp.co_head_blocked = 0;
         lp.co_heads_per_block = 1;
         lp.co_column_split = 1;

@@ -86,17 +86,24 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
 }
 
 // ===========================================================================
-// Stage 2, fp32 inputs: chunk-start states.  One workgroup per (N tile of 64, batch*head),
-// four waves, each owning a 32x32 (P x N) quarter of the fp32 state in MFMA
-// accumulators.  Serially over chunks: stage X_c^T and W_c^T = (w * B_c)^T into
-// LDS (token-contiguous rows, so MFMA fragments are 8 consecutive tokens),
-// store the chunk-start state, scale it by exp2(G_last) and accumulate X^T W.
+// Stage 2, fp32 inputs: chunk-start states.  One workgroup per (N tile of 64,
+// batch*head, group of K consecutive chunks), four waves, each owning a 32x32
+// (P x N) quarter of the fp32 state in MFMA accumulators.  Serially over the
+// group's chunks: stage X_c^T and W_c^T = (w * B_c)^T into LDS (token-contiguous
+// rows, so MFMA fragments are 8 consecutive tokens), store the chunk-start
+// state, scale it by exp2(G_last) and accumulate X^T W.
+// Groups (the jump is linear, so a run of chunks can start from zero and be
+// corrected later): group g starts from h0 if g == 0 and from 0 otherwise; with
+// Ug it stores its final local state U_g there and, from one thread, the decays
+// beta_c (group start to chunk c) and gamma_g (the whole group) for the group
+// scan; without Ug (one group) the final state goes to hT.
 // ===========================================================================
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const T *__restrict__ x, const T *__restrict__ Bm, const float *__restrict__ G2,
     const float *__restrict__ wT, const float *__restrict__ h0, T *__restrict__ S,
-    float *__restrict__ hT, int L, int H, int G, int N, int nc, int Lp)
+    float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
+    float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng)
 {
     constexpr int P = 64, NT = 64;
     constexpr int PITCH = Q + 16 / (int)sizeof(T);  // row pitch in elements; rows 16 B aligned
@@ -109,10 +116,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const int n_base = blockIdx.x * NT;
     const int bh = blockIdx.y, b = bh / H, h = bh % H, g = h / (H / G);
     const int col = n_base + nh * 32 + (lane & 31);
+    const int grp = blockIdx.z, c0 = grp * K, c1 = min(c0 + K, nc);
 
     const int64_t st_off = (int64_t)bh * P * N;
     f32x16 acc = zero_acc();
-    if (h0 != nullptr) {
+    if (h0 != nullptr && grp == 0) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = h0[st_off + (int64_t)(ph * 32 + acc_row(v, lane)) * N + col];
     }
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const int64_t xrow = (int64_t)H * P;   // x token stride
     const int64_t brow = (int64_t)G * N;   // B token stride
 
-    for (int c = 0; c < nc; ++c) {
+    for (int c = c0; c < c1; ++c) {
         const int t0 = c * Q;
         const float glast = Gh[t0 + Q - 1];
         for (int t = tid; t < Q; t += 256) wsh[t] = wh[t0 + t];
@@ -180,9 +188,18 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         __syncthreads();
     }
 
-    if (hT != nullptr) {
+    if (Ug != nullptr && tid == 0 && blockIdx.x == 0) {
+        float run = 1.0f;
+        for (int c = c0; c < c1; ++c) {
+            beta[(int64_t)bh * nc + c] = run;
+            run *= fast_exp2(Gh[c * Q + Q - 1]);
+        }
+        gam[(int64_t)bh * ng + grp] = run;
+    }
+    float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : (hT ? hT + st_off : nullptr);
+    if (dst != nullptr) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) hT[st_off + (int64_t)(ph * 32 + acc_row(v, lane)) * N + col] = acc[v];
+        for (int v = 0; v < 16; ++v) dst[(int64_t)(ph * 32 + acc_row(v, lane)) * N + col] = acc[v];
     }
 }
 
@@ -197,12 +214,16 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 //              layout the next product wants for its B operand;
 //   * M (dt X): A = (dt X)^T from LDS (p rows, token-contiguous), B = M straight
 //              from registers after the decay, causal select and rounding.
+// CORR: S holds chunk-start states relative to the start of the chunk's state-pass
+// group, and the state used is S + beta_c H_g (H_g the true state at the group
+// start, fp32, from the group scan; beta is 0 in group 0, which adds nothing).
 // ===========================================================================
-template <typename T, int Q>
+template <typename T, int Q, bool CORR>
 __global__ __launch_bounds__(Q) void chunk_out_kernel(
     const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const T *__restrict__ S,
-    const float *__restrict__ D, T *__restrict__ y, int L, int H, int G, int N, int nc, int Lp)
+    const float *__restrict__ D, T *__restrict__ y, const float *__restrict__ Hg,
+    const float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng)
 {
     constexpr int P = 64, NI = Q / 32, NTHR = Q;  // Q/64 waves
     constexpr int PITCH = Q + 16 / (int)sizeof(T);
@@ -233,6 +254,19 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
     const T *Bc = Bm + ((int64_t)b * L + t0) * crow + (int64_t)g * N;
     const T *Sc = S + ((int64_t)bh * nc + c) * P * N;
     const int kq = 8 * (lane >> 5);
+    const int cgrp = CORR ? c / K : 0;
+    const float bc = (CORR && cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
+    const float *Hc = CORR ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr;
+    // state fragment of row r, columns k + kq .. k + kq + 7 (corrected when grouped)
+    auto state_frag = [&](int r, int k) {
+        typename Elem<T>::frag f = load_frag<T>(Sc + (int64_t)r * N + kq + k);
+        if constexpr (CORR) {
+            const f32x8 hv = load_frag<float>(Hc + (int64_t)r * N + kq + k);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = Elem<T>::from_f32((float)f[e] + bc * hv[e]);
+        }
+        return f;
+    };
 
     for (int pass = 0; pass < 2; ++pass) {
         const int I = pass == 0 ? wave : NI - 1 - wave;
@@ -244,8 +278,8 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
         f32x16 acc0 = zero_acc(), acc1 = zero_acc();
         for (int k = 0; k < N; k += 16) {
             const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
-            mma(acc0, load_frag<T>(Sc + (int64_t)(lane & 31) * N + kq + k), cf);
-            mma(acc1, load_frag<T>(Sc + (int64_t)(32 + (lane & 31)) * N + kq + k), cf);
+            mma(acc0, state_frag(lane & 31, k), cf);
+            mma(acc1, state_frag(32 + (lane & 31), k), cf);
         }
         const float gi = Gs[i_loc];
         const float si = fast_exp2(gi);
@@ -335,24 +369,25 @@ hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, f
 
 template <typename T, int Q>
 static hipError_t state_pass_tq(const Shape &s, const void *x, const void *B, const float *G2,
-                                const float *wT, const float *h0, void *S, float *hT,
-                                hipStream_t st)
+                                const float *wT, const float *h0, void *S, float *hT, float *Ug,
+                                float *gam, float *beta, int K, int ng, hipStream_t st)
 {
-    dim3 grid((unsigned)(s.N / 64), (unsigned)(s.b * s.H));
+    dim3 grid((unsigned)(s.N / 64), (unsigned)(s.b * s.H), (unsigned)ng);
     hipLaunchKernelGGL((state_pass_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)x, (const T *)B,
-                       G2, wT, h0, (T *)S, hT, (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc,
-                       (int)s.Lp);
+                       G2, wT, h0, (T *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G,
+                       (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t state_pass_t(const Shape &s, const void *x, const void *B, const float *G2,
-                               const float *wT, const float *h0, void *S, float *hT, hipStream_t st)
+                               const float *wT, const float *h0, void *S, float *hT, float *Ug,
+                               float *gam, float *beta, int K, int ng, hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return state_pass_tq<T, 64>(s, x, B, G2, wT, h0, S, hT, st);
-    case 128: return state_pass_tq<T, 128>(s, x, B, G2, wT, h0, S, hT, st);
-    default: return state_pass_tq<T, 256>(s, x, B, G2, wT, h0, S, hT, st);
+    case 64: return state_pass_tq<T, 64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return state_pass_tq<T, 128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return state_pass_tq<T, 256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
@@ -361,30 +396,47 @@ hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const
                              hipStream_t st)
 {
     return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, wT, h0, S, hT, st)
-                  : state_pass_t<float>(s, x, B, G2, wT, h0, S, hT, st);
+                  : state_pass_t<float>(s, x, B, G2, wT, h0, S, hT, nullptr, nullptr, nullptr,
+                                        (int)s.nc, 1, st);
+}
+
+hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const void *B,
+                                         const float *G2, const float *wT, const float *h0,
+                                         void *S, float *Ug, float *gam, float *beta, int K,
+                                         int ng, hipStream_t st)
+{
+    return state_pass_t<float>(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K, ng, st);
 }
 
 template <typename T, int Q>
 static hipError_t chunk_out_tq(const Shape &s, const void *x, const void *B, const void *C,
                                const float *G2, const float *dtT, const void *S, const float *D,
-                               void *y, hipStream_t st)
+                               void *y, const float *Hg, const float *beta, int K, int ng,
+                               hipStream_t st)
 {
     dim3 grid((unsigned)s.nc, (unsigned)(s.b * s.H));
-    hipLaunchKernelGGL((chunk_out_kernel<T, Q>), grid, dim3(Q), 0, st, (const T *)x, (const T *)B,
-                       (const T *)C, G2, dtT, (const T *)S, D, (T *)y, (int)s.L, (int)s.H,
-                       (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp);
+    if (Hg != nullptr)
+        hipLaunchKernelGGL((chunk_out_kernel<T, Q, true>), grid, dim3(Q), 0, st, (const T *)x,
+                           (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y, Hg, beta,
+                           (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
+    else
+        hipLaunchKernelGGL((chunk_out_kernel<T, Q, false>), grid, dim3(Q), 0, st, (const T *)x,
+                           (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y,
+                           (const float *)nullptr, (const float *)nullptr, (int)s.L, (int)s.H,
+                           (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, (int)s.nc, 1);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t chunk_out_t(const Shape &s, const void *x, const void *B, const void *C,
                               const float *G2, const float *dtT, const void *S, const float *D,
-                              void *y, hipStream_t st)
+                              void *y, const float *Hg, const float *beta, int K, int ng,
+                              hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return chunk_out_tq<T, 64>(s, x, B, C, G2, dtT, S, D, y, st);
-    case 128: return chunk_out_tq<T, 128>(s, x, B, C, G2, dtT, S, D, y, st);
-    default: return chunk_out_tq<T, 256>(s, x, B, C, G2, dtT, S, D, y, st);
+    case 64: return chunk_out_tq<T, 64>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    case 128: return chunk_out_tq<T, 128>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    default: return chunk_out_tq<T, 256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
     }
 }
 
@@ -394,7 +446,7 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
 {
     return s.bf16 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, nullptr,
                                           (int)s.nc, 1, st)
-                  : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, st);
+                  : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, (int)s.nc, 1, st);
 }
 
 hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const void *x,
@@ -403,7 +455,8 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const 
                                       const float *Hg, const void *Hb, const float *beta,
                                       hipStream_t st)
 {
-    if (!s.bf16 || gp.ng <= 1) return launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, st);
+    if (gp.ng <= 1) return launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, st);
+    if (!s.bf16) return chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, gp.K, gp.ng, st);
     return launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, Hg, Hb, beta, gp.K, gp.ng, st);
 }
 

@@ -33,8 +33,14 @@ Grouping state_pass_groups(const Shape &s);
 // chunk-start states relative to their group, Ug the true group-start states
 // H_g (after the group scan), beta the per-chunk decay since the group start;
 // hT is the true final state.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng],
-// beta [b*H, nc], all fp32, and Hb [b*H, ng, P, N] bf16 (H_g rounded, zeros for
-// group 0).  fp32 problems always use one group.
+// beta [b*H, nc], all fp32, and for bf16 problems Hb [b*H, ng, P, N] bf16 (H_g
+// rounded, zeros for group 0).
+// fp32 state pass over ng groups of K chunks (ssd_kernels.hip): local chunk-start
+// states into S, final local states into Ug, decays into gam and beta.
+hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const void *B,
+                                         const float *G2, const float *wT, const float *h0,
+                                         void *S, float *Ug, float *gam, float *beta, int K,
+                                         int ng, hipStream_t st);
 hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
                                      const void *B, const float *G2, const float *wT,
                                      const float *h0, void *S, float *hT, float *Ug, void *Hb,

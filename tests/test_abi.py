@@ -176,9 +176,13 @@ def test_launch_plan_per_shape():
     for kw in (dict(chunk=64), dict(dstate=384, chunk=128)):
         q = ssd.ssd_plan(_p(**kw))
         assert q["co_head_blocked"] == 0 and q["co_heads_per_block"] == 1
-    # fp32: one serial chain per (batch, head) and 64 columns
+    # fp32: 64 columns per state-pass workgroup, chains split into groups up to four
+    # workgroups per CU at 64-token chunks (here one chunk per group), then the scan
     f = ssd.ssd_plan(_p(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"))
-    assert (f["sp_groups"], f["sp_columns"], f["sp_workgroups"], f["scan"], f["co_head_blocked"]) == (1, 64, 4, 0, 0)
+    assert (f["sp_group_chunks"], f["sp_groups"], f["sp_columns"], f["sp_workgroups"], f["scan"],
+            f["co_head_blocked"]) == (1, 4, 64, 16, 1, 0)
+    f2 = ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256, dtype="fp32"))
+    assert (f2["sp_group_chunks"], f2["sp_groups"], f2["sp_workgroups"]) == (32, 2, 256)
     # the plan refuses what the forward refuses
     with pytest.raises(ssd.SsdError) as ei:
         ssd.ssd_plan(_p(dstate=96))

@@ -132,6 +132,10 @@ SMALL_CASES = [
     _wl("bf16_q128_n448", "bf16", 2, 500, 3, 64, 448, 1, 128),
     _wl("bf16_q256_n384", "bf16", 1, 700, 4, 64, 384, 4, 256, h0=False),
     _wl("fp32_q128_n512", "fp32", 1, 260, 2, 64, 512, 1, 128),
+    # fp32 state pass split into groups: one chunk per group with a ragged last chunk,
+    # and two chunks per group with G = 2 and h0
+    _wl("fp32_groups_k1", "fp32", 1, 3000, 2, 64, 128, 1, 128, h0=False),
+    _wl("fp32_groups_k2", "fp32", 2, 2000, 8, 64, 256, 2, 256),
 ]
 
 
@@ -244,11 +248,12 @@ def test_deterministic_bitwise():
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
-def test_stages_match_forward():
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_stages_match_forward(dtype):
     """The public stages (one serial chain) and ssd_forward (grouped state pass with the
     carried state added in stage 3) agree with each other and with the oracle."""
     dev = require_gpu()
-    w = _wl("stages", "bf16", 2, 1280, 4, 64, 128, 2, 64)
+    w = _wl("stages", dtype, 2, 1280, 4, 64, 128, 2, 64)
     inp = make_inputs(w, 10)
     d = to_dev(inp, dev)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
@@ -257,8 +262,9 @@ def test_stages_match_forward():
     y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
     yf, hTf, _, _ = _gpu_forward(inp, w, dev)
     ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"])
-    check(f64(y), ref["y"], TOL["bf16"], "y (stages)")
-    check(f64(yf), ref["y"], TOL["bf16"], "y (forward)")
+    assert ssd.ssd_plan(prob)["sp_groups"] > 1
+    check(f64(y), ref["y"], TOL[dtype], "y (stages)")
+    check(f64(yf), ref["y"], TOL[dtype], "y (forward)")
     check(f64(hTf), f64(hT), 1e-5, "hT forward vs stages (both fp32 states)")
 
 
