@@ -381,3 +381,38 @@ def test_full_workload_sampled(name, units):
     del S
     # every output element was written and is finite
     assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+
+
+@pytest.mark.slow
+def test_largest_sequence_sampled():
+    """The longest sequence the supported set allows for the headline model's heads
+    (seqlen * nheads * headdim just below 2^30, a ragged last chunk): the state pass
+    addresses x rows with 32-bit byte offsets that reach 2^31 - 4 KiB here.  Two
+    (batch, head) units against the oracle: y, hT and the chunk-start states."""
+    dev = require_gpu()
+    L = (1 << 30) // (32 * 64) - 1
+    w = Workload("largest", "bf16", 1, L, 32, 64, 256, 1, 256, has_h0=True)
+    assert ssd.ssd_validate(ssd.make_problem(1, L, 32, 1, 64, 256, 256, torch.bfloat16)) == 0
+    assert ssd.ssd_validate(ssd.make_problem(1, L + 1, 32, 1, 64, 256, 256, torch.bfloat16)) == 3
+    print(f"case {w}: drawing inputs", flush=True)
+    inp = make_inputs(w, 0)
+    units = [0, 31]
+    print("forward", flush=True)
+    y, hT, ws, prob = _gpu_forward(inp, w, dev)
+    del ws
+    y_s = np.stack([f64(y[0, :, h, :]) for h in units])
+    h_s = np.stack([f64(hT[0, h]) for h in units])
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+    del y, hT
+    print("stage states", flush=True)
+    S, _ = _stage_states(inp, w, dev)
+    S_s = np.stack([f64(S[0, h]) for h in units])
+    del S
+    torch.cuda.empty_cache()
+    print("oracle", flush=True)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                         units=units, chunk=w.chunk)
+    tol = TOL["bf16"]
+    check(y_s, ref["y"], tol, "y (sampled units)")
+    check(h_s, ref["hT"], tol, "hT (sampled units)")
+    check(S_s, ref["snaps"], tol, "chunk-start states (stage 2, sampled units)")
