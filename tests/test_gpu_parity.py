@@ -383,20 +383,27 @@ def test_full_workload_sampled(name, units):
     assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
 
 
+LARGEST = [
+    # name, b, L, H, G, N, Q, sampled heads: L*H*P just below 2^30 (x rows), and
+    # L*G*N just below 2^30 (B and C rows; one head per group, N = 512 column split)
+    ("x_rows", 1, (1 << 30) // (32 * 64) - 1, 32, 1, 256, 256, [0, 31]),
+    ("bc_rows", 1, (1 << 30) // (8 * 512) - 1, 8, 8, 512, 128, [0, 7]),
+]
+
+
 @pytest.mark.slow
-def test_largest_sequence_sampled():
-    """The longest sequence the supported set allows for the headline model's heads
-    (seqlen * nheads * headdim just below 2^30, a ragged last chunk): the state pass
-    addresses x rows with 32-bit byte offsets that reach 2^31 - 4 KiB here.  Two
-    (batch, head) units against the oracle: y, hT and the chunk-start states."""
+@pytest.mark.parametrize("name,b,L,H,G,N,Q,units", LARGEST, ids=[c[0] for c in LARGEST])
+def test_largest_sequence_sampled(name, b, L, H, G, N, Q, units):
+    """The longest sequences the supported set allows along its two per-batch extents:
+    the state pass addresses x and B rows with 32-bit byte offsets, which reach within a
+    few KiB of 2^31 here (a ragged last chunk in both).  Sampled (batch, head) units
+    against the oracle: y, hT and the chunk-start states."""
     dev = require_gpu()
-    L = (1 << 30) // (32 * 64) - 1
-    w = Workload("largest", "bf16", 1, L, 32, 64, 256, 1, 256, has_h0=True)
-    assert ssd.ssd_validate(ssd.make_problem(1, L, 32, 1, 64, 256, 256, torch.bfloat16)) == 0
-    assert ssd.ssd_validate(ssd.make_problem(1, L + 1, 32, 1, 64, 256, 256, torch.bfloat16)) == 3
+    w = Workload(name, "bf16", b, L, H, 64, N, G, Q, has_h0=True)
+    assert ssd.ssd_validate(ssd.make_problem(b, L, H, G, 64, N, Q, torch.bfloat16)) == 0
+    assert ssd.ssd_validate(ssd.make_problem(b, L + 1, H, G, 64, N, Q, torch.bfloat16)) == 3
     print(f"case {w}: drawing inputs", flush=True)
     inp = make_inputs(w, 0)
-    units = [0, 31]
     print("forward", flush=True)
     y, hT, ws, prob = _gpu_forward(inp, w, dev)
     del ws
