@@ -1237,15 +1237,43 @@ hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, 
 Grouping state_pass_groups(const Shape &s)
 {
     Grouping gp;
-    // bf16: about one state-pass workgroup per CU (each takes most of a CU's LDS);
-    // fp32 (64 columns per workgroup): as many as the LDS of its Q lets a CU hold
     const int64_t units = s.b * s.H * (s.N / (s.bf16 ? sp_cols(s) : 64));
-    const int64_t target = s.bf16 ? 256 : 256 * (s.Q == 64 ? 4 : s.Q == 128 ? 2 : 1);
-    int64_t ng = (target + units - 1) / units;
-    ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc));
-    const int64_t K = (s.nc + ng - 1) / ng;
-    gp.K = (int)K;
-    gp.ng = (int)((s.nc + K - 1) / K);
+    if (!s.bf16) {
+        // fp32 (64 columns per workgroup): as many workgroups as the LDS of its Q
+        // lets the CUs hold at once
+        const int64_t target = 256 * (s.Q == 64 ? 4 : s.Q == 128 ? 2 : 1);
+        int64_t ng = (target + units - 1) / units;
+        ng = std::max<int64_t>(1, std::min<int64_t>(ng, s.nc));
+        const int64_t K = (s.nc + ng - 1) / ng;
+        gp.K = (int)K;
+        gp.ng = (int)((s.nc + K - 1) / K);
+        return gp;
+    }
+    // bf16: a workgroup takes most of a CU's LDS (two fit at 64 columns), so `slots`
+    // run at once and units * ng workgroups take ceil(units * ng / slots) rounds of K
+    // chunks each.  The count minimises that makespan plus a fixed cost per
+    // workgroup (~0.6 chunk: prologue, last state store) and the group scan (it
+    // reads and writes every group's state, ~6 bytes per element at ~5 TB/s),
+    // in units of one chunk's time (~1.2 us per 64 tokens); ties keep fewer groups.
+    const int64_t slots = 256 * (sp_cols(s) == 64 ? 2 : 1);
+    const double tchunk = (double)s.Q / 64 * 1.2e-6;
+    const int64_t ng_max = std::min<int64_t>(s.nc, 8 * slots / units + 1);
+    double best = 1e300;
+    int64_t best_ng = 1, best_K = s.nc;
+    for (int64_t ng = 1; ng <= ng_max; ++ng) {
+        const int64_t K = (s.nc + ng - 1) / ng, g = (s.nc + K - 1) / K;
+        if (g != ng) continue;   // same K as a smaller count
+        const double rounds = (double)((units * g + slots - 1) / slots);
+        const double scan = g > 1 ? (double)(s.b * s.H) * g * s.P * s.N * 6.0 / 5e12 / tchunk : 0.0;
+        const double cost = rounds * (K + 0.6) + scan;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_ng = g;
+            best_K = K;
+        }
+    }
+    gp.K = (int)best_K;
+    gp.ng = (int)best_ng;
     return gp;
 }
 
