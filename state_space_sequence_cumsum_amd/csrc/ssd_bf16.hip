@@ -1331,15 +1331,25 @@ static hipError_t co_launch(const Shape &s, const void *x, const void *B, const 
     return co_launch_n<Q, 512>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
 }
 
-// heads per workgroup of the head-blocked chunk output: the largest divisor of
-// the heads per group that still gives at least one workgroup per CU
+// heads per workgroup of the head-blocked chunk output: the divisor HB of the heads
+// per group that minimises the makespan ceil(workgroups / 256) * (HB + c), c the
+// per-workgroup cost in units of one head's work (the C B^T phase, ~0.9 N / 256,
+// plus ~0.5 for the prologue and launch); ties keep fewer heads per workgroup
 static int heads_per_block(const Shape &s)
 {
     const int hpg = (int)(s.H / s.G);
     const int64_t units = s.nc * s.b * s.G;
+    const double c = 0.9 * (double)s.N / 256 + 0.5;
+    double best_cost = 1e300;
     int best = 1;
-    for (int hb = 1; hb <= hpg; ++hb)
-        if (hpg % hb == 0 && units * (hpg / hb) >= 256) best = hb;
+    for (int hb = 1; hb <= hpg; ++hb) {
+        if (hpg % hb) continue;
+        const double cost = (double)((units * (hpg / hb) + 255) / 256) * (hb + c);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = hb;
+        }
+    }
     return best;
 }
 
