@@ -152,6 +152,14 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         ssd.ssd_forward(x, torch.zeros(1, 64, 2, dtype=torch.bfloat16), torch.zeros(2), B, B,
                         torch.zeros(2), chunk=64)
+    # the plans check their tensors when they are made, before any call
+    with pytest.raises(ValueError):
+        ssd.ForwardPlan(x, torch.zeros(1, 64, 2, dtype=torch.bfloat16), torch.zeros(2), B, B,
+                        torch.zeros(2), chunk=64)
+    with pytest.raises(ValueError):
+        ssd.StepPlan(torch.zeros(1, 2, 64, dtype=torch.bfloat16), torch.zeros(1, 2, dtype=torch.bfloat16),
+                     torch.zeros(2), torch.zeros(1, 1, 64, dtype=torch.bfloat16),
+                     torch.zeros(1, 1, 64, dtype=torch.bfloat16), torch.zeros(2), torch.zeros(1, 2, 64, 64))
 
 
 def test_launch_plan_per_shape():
