@@ -1252,9 +1252,11 @@ Grouping state_pass_groups(const Shape &s)
     // bf16: a workgroup takes most of a CU's LDS (two fit at 64 columns), so `slots`
     // run at once and units * ng workgroups take ceil(units * ng / slots) rounds of K
     // chunks each.  The count minimises that makespan plus a fixed cost per
-    // workgroup (~0.6 chunk: prologue, last state store) and the group scan (it
-    // reads and writes every group's state, ~6 bytes per element at ~5 TB/s),
-    // in units of one chunk's time (~1.2 us per 64 tokens); ties keep fewer groups.
+    // workgroup (~0.6 chunk: prologue, last state store) and the group scan, in
+    // units of one chunk's time (~1.2 us per 64 tokens); ties keep fewer groups.
+    // The scan reads and writes every group's state (~6 bytes per element at
+    // ~5 TB/s) and walks the groups in order, eight loads in flight (~1.5 us per
+    // eight groups): whichever is longer.
     const int64_t slots = 256 * (sp_cols(s) == 64 ? 2 : 1);
     const double tchunk = (double)s.Q / 64 * 1.2e-6;
     const int64_t ng_max = std::min<int64_t>(s.nc, 8 * slots / units + 1);
@@ -1264,7 +1266,9 @@ Grouping state_pass_groups(const Shape &s)
         const int64_t K = (s.nc + ng - 1) / ng, g = (s.nc + K - 1) / K;
         if (g != ng) continue;   // same K as a smaller count
         const double rounds = (double)((units * g + slots - 1) / slots);
-        const double scan = g > 1 ? (double)(s.b * s.H) * g * s.P * s.N * 6.0 / 5e12 / tchunk : 0.0;
+        const double scan_bw = (double)(s.b * s.H) * g * s.P * s.N * 6.0 / 5e12;
+        const double scan_serial = (double)((g + 7) / 8) * 1.5e-6;
+        const double scan = g > 1 ? std::max(scan_bw, scan_serial) / tchunk : 0.0;
         const double cost = rounds * (K + 0.6) + scan;
         if (cost < best - 1e-9) {
             best = cost;
