@@ -39,17 +39,27 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
     const int t0 = c * Q;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    for (int idx = tid; idx < Q * HB; idx += 256) {
-        const int t = idx / HB, hh = idx % HB;
-        float v = 0.0f;
-        if (hh < nh && t0 + t < L) v = (float)dt[((int64_t)b * L + t0 + t) * H + hb + hh];
-        tile[t][hh] = v;
+    // every load is issued before the first is used (positions clamped into the
+    // problem, values outside it zeroed afterwards): a load under a branch would be
+    // waited for before the next one is issued
+    constexpr int NLD = Q * HB / 256;   // dt elements per thread
+    const float a = A[hb + min(wave, nh - 1)];
+    float v[NLD];
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+        const int idx = tid + 256 * r, t = idx / HB, hh = idx % HB;
+        v[r] = (float)dt[((int64_t)b * L + min(t0 + t, L - 1)) * H + hb + min(hh, nh - 1)];
     }
+#pragma unroll
+    for (int r = 0; r < NLD; ++r) {
+        const int idx = tid + 256 * r, t = idx / HB, hh = idx % HB;
+        tile[t][hh] = (hh < nh && t0 + t < L) ? v[r] : 0.0f;
+    }
+    asm volatile("" ::"v"(a));   // keeps A's load ahead of the barrier, in flight with dt's
     __syncthreads();
     if (wave >= nh) return;
 
     const int hh = wave;
-    const float a = A[hb + hh];
     float part[PER], run = 0.0f;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {

@@ -210,6 +210,26 @@ def test_masked_exponent_overflow(dtype):
     _check_forward(w, inp=inp)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("zero", ["B", "C"])
+def test_degenerate_zero_B_or_C(dtype, zero):
+    """B = 0: nothing enters the state, so hT = exp(sum of a) h0 and y_t = exp(G_t) C_t h0
+    + D x_t (the grouped state pass then carries only h0 through the group scan).  C = 0:
+    the state is never read out and y = D x; the chunk output rounds the fp32 product once,
+    so y equals round(D x) bit for bit.  With B = 0, A is scaled by 0.01 so that h0 is
+    still well above fp32's range at the end (with A down to -16 the exact hT is ~1e-50)."""
+    Q = 128 if dtype == "bf16" else 64
+    w = _wl(f"zero_{zero}", dtype, 1, 700, 3, 64, 128, 1, Q)
+    inp = make_inputs(w, 8)
+    inp[zero].zero_()
+    if zero == "B":
+        inp["A"].mul_(0.01)
+    y, hT, ref = _check_forward(w, inp=inp)
+    if zero == "C":
+        skip = (inp["D"][None, None, :, None] * inp["x"].float()).to(inp["x"].dtype)
+        assert torch.equal(y.cpu(), skip)
+
+
 def test_state_continuation():
     dev = require_gpu()
     w = _wl("cont", "fp32", 1, 448, 2, 64, 64, 1, 64)
