@@ -247,15 +247,25 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
     const float *Gh = G2 + (int64_t)bh * Lp + t0;
     const float *dh = dtT + (int64_t)bh * Lp + t0;
 
+    // Q <= 128: rows past L are clamped to row L-1 instead of zeroed, so no load sits
+    // under a per-lane branch (such a load is waited for before the next is issued):
+    // their dt is 0, so their (dt x) rows vanish, and their outputs are never stored.
+    // Q = 256 keeps the zero-filled loads, which measured faster there.
     for (int t = tid; t < Q; t += NTHR) Gs[t] = Gh[t];
-    for (int idx = tid; idx < Q * 8; idx += NTHR) {
+    const int last = L - 1 - t0;   // last row of the chunk inside the problem
+    auto stage_x = [&](int idx, bool clamp) {
         const int t = idx >> 3, oct = idx & 7;
-        typename Elem<T>::frag f =
-            (t0 + t < L) ? load_frag<T>(x + ((int64_t)b * L + t0 + t) * xrow + (int64_t)h * P + oct * 8)
-                         : zero_frag<T>();
+        const T *xr = x + ((int64_t)b * L + t0 + min(t, last)) * xrow + (int64_t)h * P + oct * 8;
+        const typename Elem<T>::frag f = (clamp || t <= last) ? load_frag<T>(xr) : zero_frag<T>();
         const float d = dh[t];
 #pragma unroll
         for (int e = 0; e < 8; ++e) XdT[(oct * 8 + e) * PITCH + t] = Elem<T>::from_f32((float)f[e] * d);
+    };
+    if constexpr (Q <= 128) {
+#pragma unroll
+        for (int r = 0; r < Q * 8 / NTHR; ++r) stage_x(tid + NTHR * r, true);
+    } else {
+        for (int idx = tid; idx < Q * 8; idx += NTHR) stage_x(idx, false);
     }
     __syncthreads();
 
@@ -282,14 +292,35 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
         const int I = pass == 0 ? wave : NI - 1 - wave;
         const int i_loc = I * 32 + (lane & 31);
         const bool ivalid = t0 + i_loc < L;
-        const T *crow_i = Cc + (int64_t)i_loc * crow + kq;
+        const T *crow_i = Cc + (int64_t)min(i_loc, last) * crow + kq;
 
         // inter-chunk term: Y^T = S C^T, then scale column i by exp2(G_i)
+        // Q <= 128: N is a multiple of 64, and the fragments of four 16-wide steps
+        // are loaded before their products so that their latencies overlap; at
+        // Q = 256 the registers this takes cost more occupancy than the overlap gains
         f32x16 acc0 = zero_acc(), acc1 = zero_acc();
-        for (int k = 0; k < N; k += 16) {
-            const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
-            mma(acc0, state_frag(lane & 31, k), cf);
-            mma(acc1, state_frag(32 + (lane & 31), k), cf);
+        if constexpr (Q <= 128) {
+            for (int k0 = 0; k0 < N; k0 += 64) {
+                typename Elem<T>::frag cf[4], s0[4], s1[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    cf[u] = load_frag<T>(crow_i + k0 + 16 * u);
+                    s0[u] = state_frag(lane & 31, k0 + 16 * u);
+                    s1[u] = state_frag(32 + (lane & 31), k0 + 16 * u);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keeps the loads ahead of the products
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    mma(acc0, s0[u], cf[u]);
+                    mma(acc1, s1[u], cf[u]);
+                }
+            }
+        } else {
+            for (int k = 0; k < N; k += 16) {
+                const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
+                mma(acc0, state_frag(lane & 31, k), cf);
+                mma(acc1, state_frag(32 + (lane & 31), k), cf);
+            }
         }
         const float gi = Gs[i_loc];
         const float si = fast_exp2(gi);
@@ -299,13 +330,27 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
         // intra-chunk term over causal tiles J <= I
         for (int J = 0; J <= I; ++J) {
             const int j_loc = J * 32 + (lane & 31);
-            const bool jvalid = t0 + j_loc < L;
-            const T *brow_j = Bc + (int64_t)j_loc * crow + kq;
+            const T *brow_j = Bc + (int64_t)min(j_loc, last) * crow + kq;
             f32x16 cb = zero_acc();
-            for (int k = 0; k < N; k += 16) {
-                const typename Elem<T>::frag bf = jvalid ? load_frag<T>(brow_j + k) : zero_frag<T>();
-                const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
-                mma(cb, bf, cf);
+            if constexpr (Q <= 128) {
+                for (int k0 = 0; k0 < N; k0 += 64) {
+                    typename Elem<T>::frag bf[4], cf[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        bf[u] = load_frag<T>(brow_j + k0 + 16 * u);
+                        cf[u] = load_frag<T>(crow_i + k0 + 16 * u);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) mma(cb, bf[u], cf[u]);
+                }
+            } else {
+                const bool jvalid = t0 + j_loc < L;
+                for (int k = 0; k < N; k += 16) {
+                    const typename Elem<T>::frag bf = jvalid ? load_frag<T>(brow_j + k) : zero_frag<T>();
+                    const typename Elem<T>::frag cf = ivalid ? load_frag<T>(crow_i + k) : zero_frag<T>();
+                    mma(cb, bf, cf);
+                }
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
