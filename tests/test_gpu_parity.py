@@ -144,6 +144,28 @@ def test_forward_parity_small(w):
     _check_forward(w, seed=0)
 
 
+# many heads over short sequences: the state pass runs as one group per (batch, head), and the
+# chunk output reads true chunk-start states (its uncorrected instances)
+SINGLE_GROUP_CASES = [
+    _wl("sg_hb_n64_q128", "bf16", 2, 320, 128, 64, 64, 1, 128),            # 4 heads per block, ragged
+    _wl("sg_hb_n256_q256", "bf16", 1, 640, 128, 64, 256, 1, 256, h0=False),
+    _wl("sg_hb_n256_q128", "bf16", 1, 320, 96, 64, 256, 2, 128),
+    _wl("sg_hb_n512_q128", "bf16", 1, 320, 48, 64, 512, 1, 128),          # column halves
+    _wl("sg_onehead_q64", "bf16", 1, 160, 96, 64, 128, 3, 64),
+    _wl("sg_fp32_q256", "fp32", 1, 640, 64, 64, 256, 1, 256),
+    _wl("sg_fp32_q128", "fp32", 1, 320, 128, 64, 256, 2, 128, h0=False),
+    _wl("sg_fp32_q64", "fp32", 4, 160, 128, 64, 128, 1, 64),
+]
+
+
+@pytest.mark.parametrize("w", SINGLE_GROUP_CASES, ids=[c.name for c in SINGLE_GROUP_CASES])
+def test_forward_parity_single_group(w):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    prob = ssd.make_problem(w.batch, w.seqlen, w.nheads, w.ngroups, w.headdim, w.dstate, w.chunk, dt)
+    assert ssd.ssd_plan(prob)["sp_groups"] == 1, "shape no longer runs as one group"
+    _check_forward(w, seed=3)
+
+
 def _random_cases(n, seed=2026):
     """n shapes drawn from the supported set (any L, H divisible by G, N a multiple of 64 up
     to 512, Q in {64, 128, 256}, bf16 or fp32, with or without h0), sized for the oracle."""
