@@ -425,6 +425,29 @@ def test_full_workload_sampled(name, units):
     assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
 
 
+@pytest.mark.slow
+def test_largest_batch_heads_sampled():
+    """batch * heads at the supported maximum (65535, a grid dimension of the group scan and
+    of the one-head chunk output): 4369 sequences of 15 heads in 3 groups, 200 tokens in
+    128-token chunks (one full, one ragged), so the state pass runs as one group and both
+    chunk-output kernels run their largest grids; sampled units against the oracle."""
+    dev = require_gpu()
+    w = _wl("max_bh", "bf16", 4369, 200, 15, 64, 64, 3, 128)
+    assert w.batch * w.nheads == 65535
+    inp = make_inputs(w, 5)
+    units = [0, 1, 7, 32767, 50000, 65534]
+    print(f"case {w}: units {units}", flush=True)
+    y, hT, ws, prob = _gpu_forward(inp, w, dev)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"],
+                         units=units, chunk=w.chunk)
+    u = ref["units"]
+    b_idx, h_idx = u // w.nheads, u % w.nheads
+    tol = TOL[w.dtype]
+    check(np.stack([f64(y[b, :, h, :]) for b, h in zip(b_idx, h_idx)]), ref["y"], tol, "y (sampled units)")
+    check(np.stack([f64(hT[b, h]) for b, h in zip(b_idx, h_idx)]), ref["hT"], tol, "hT (sampled units)")
+    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+
+
 LARGEST = [
     # name, b, L, H, G, N, Q, sampled heads: L*H*P just below 2^30 (x rows), and
     # L*G*N just below 2^30 (B and C rows; one head per group, N = 512 column split)
