@@ -161,7 +161,15 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
     const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + n0;
-    const bool keeper = tid == 0 && n0 == 0;   // writes beta / gamma of this group
+    // the chunk-end cumsum value of chunk c0 + lane (clamped to the group), for the decay
+    // products written at the end; loaded now, as a per-lane load in every wave (no branch
+    // around it), so that its latency hides behind the chunk loop
+    float gend0;
+    {
+        int gi = min(c0 + lane, c1 - 1) * Q + Q - 1;
+        asm volatile("" : "+v"(gi));
+        gend0 = G2[(int64_t)bh * Lp + gi];
+    }
 
     // accumulator element v of tile (i, j): row n = 32 (rt0 + i) + acc_row(v, lane),
     // column p = 32 (ct0 + j) + lane % 32
@@ -388,14 +396,29 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     // with one sub-step per chunk the last chunk's staged state is still in LDS
     if constexpr (NSUB == 1) state_out(c1 - 1);
 
-    // decay products of the group (beta_c before each chunk, gamma for the group)
-    if (keeper) {
+    // decay products of the group (beta_c before each chunk, gamma for the group): lane k of
+    // wave 0 holds chunk c0 + k0 + k's decay (the first 64 from the prologue's loads, so no
+    // memory wait here) and the running product is taken in chunk order, as a sequential
+    // loop over the chunks would
+    if (n0 == 0 && wave == 0 && (beta != nullptr || gam != nullptr)) {
         float run = 1.0f;
-        for (int c = c0; c < c1; ++c) {
-            if (beta != nullptr) beta[(int64_t)bh * nc + c] = run;
-            run *= fast_exp2(Gh[c * Q + Q - 1]);
+        auto products = [&](float g, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
+            const float e = fast_exp2(g);
+            const int cnt = min(64, c1 - c0 - k0);
+            float mine = 0.0f;
+            for (int k = 0; k < cnt; ++k) {
+                if (lane == k) mine = run;
+                run *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
+            }
+            if (beta != nullptr && lane < cnt) beta[(int64_t)bh * nc + c0 + k0 + lane] = mine;
+        };
+        products(gend0, 0);
+        for (int k0 = 64; k0 < c1 - c0; k0 += 64) {   // groups of more than 64 chunks
+            int gi = min(c0 + k0 + lane, c1 - 1) * Q + Q - 1;
+            asm volatile("" : "+v"(gi));
+            products(Gh[gi], k0);
         }
-        if (gam != nullptr) gam[(int64_t)bh * ng + grp] = run;
+        if (gam != nullptr && lane == 0) gam[(int64_t)bh * ng + grp] = run;
     }
 
     // the state after the group's last chunk
