@@ -139,7 +139,17 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const float *wh = wT + (int64_t)bh * Lp;
     const int64_t xrow = (int64_t)H * P;   // x token stride
     const int64_t brow = (int64_t)G * N;   // B token stride
+    // the chunk-end cumsum value of chunk c0 + lane (clamped to the group), for the decay
+    // products written at the end; a per-lane load issued now, without a branch around it
+    float gend0;
+    {
+        int gi = min(c0 + lane, c1 - 1) * Q + Q - 1;
+        asm volatile("" : "+v"(gi));
+        gend0 = Gh[gi];
+    }
 
+    // Rows past L are clamped to row L-1 (no load under a per-lane branch, which is waited
+    // for before the next is issued): their weight w is 0, so their W rows vanish.
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * Q;
         const float glast = Gh[t0 + Q - 1];
@@ -152,9 +162,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 #pragma unroll
             for (int r = 0; r < Q / 32; ++r) {
                 const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
-                f[r] = (t0 + t < L)
-                           ? load_frag<T>(x + ((int64_t)b * L + t0 + t) * xrow + (int64_t)h * P + oct * 8)
-                           : zero_frag<T>();
+                f[r] = load_frag<T>(x + ((int64_t)b * L + min(t0 + t, L - 1)) * xrow + (int64_t)h * P + oct * 8);
             }
 #pragma unroll
             for (int r = 0; r < Q / 32; ++r) {
@@ -169,9 +177,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 #pragma unroll
             for (int r = 0; r < Q / 32; ++r) {
                 const int idx = tid + 256 * r, t = idx >> 3, oct = idx & 7;
-                f[r] = (t0 + t < L)
-                           ? load_frag<T>(Bm + ((int64_t)b * L + t0 + t) * brow + (int64_t)g * N + n_base + oct * 8)
-                           : zero_frag<T>();
+                f[r] = load_frag<T>(Bm + ((int64_t)b * L + min(t0 + t, L - 1)) * brow + (int64_t)g * N + n_base + oct * 8);
             }
 #pragma unroll
             for (int r = 0; r < Q / 32; ++r) {
@@ -198,13 +204,28 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         __syncthreads();
     }
 
-    if (Ug != nullptr && tid == 0 && blockIdx.x == 0) {
+    // decay products of the group (beta_c before each chunk, gamma for the group): lane k of
+    // wave 0 holds chunk c0 + k0 + k's decay and the running product is taken in chunk order,
+    // as a sequential loop over the chunks would
+    if (Ug != nullptr && wave == 0 && blockIdx.x == 0) {
         float run = 1.0f;
-        for (int c = c0; c < c1; ++c) {
-            beta[(int64_t)bh * nc + c] = run;
-            run *= fast_exp2(Gh[c * Q + Q - 1]);
+        auto products = [&](float gend, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
+            const float e = fast_exp2(gend);
+            const int cnt = min(64, c1 - c0 - k0);
+            float mine = 0.0f;
+            for (int k = 0; k < cnt; ++k) {
+                if (lane == k) mine = run;
+                run *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
+            }
+            if (lane < cnt) beta[(int64_t)bh * nc + c0 + k0 + lane] = mine;
+        };
+        products(gend0, 0);
+        for (int k0 = 64; k0 < c1 - c0; k0 += 64) {   // groups of more than 64 chunks
+            int gi = min(c0 + k0 + lane, c1 - 1) * Q + Q - 1;
+            asm volatile("" : "+v"(gi));
+            products(Gh[gi], k0);
         }
-        gam[(int64_t)bh * ng + grp] = run;
+        if (lane == 0) gam[(int64_t)bh * ng + grp] = run;
     }
     float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : (hT ? hT + st_off : nullptr);
     if (dst != nullptr) {
