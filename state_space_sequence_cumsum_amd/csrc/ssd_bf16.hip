@@ -1394,7 +1394,7 @@ LaunchPlan plan_of(const Shape &s)
         lp.co_heads_per_block = 1;
         lp.co_column_split = 1;
         lp.co_workgroups = (int)(s.nc * s.b * s.H);
-        lp.co_threads = (int)s.Q;
+        lp.co_threads = chunk_out_f32_threads(s);
         return lp;
     }
     lp.sp_columns = sp_cols(s);

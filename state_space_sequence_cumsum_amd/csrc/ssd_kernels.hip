@@ -8,6 +8,8 @@
 // All products run on MFMA: bf16 operands with fp32 accumulation for bf16 inputs,
 // fp32 operands for fp32 inputs.  Decays use base-2 exponentials of the
 // log2(e)-scaled cumsum (same page, section "Kernel 1").
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -237,7 +239,8 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 // ===========================================================================
 // Stage 3, fp32 inputs: chunk output.  One workgroup per (chunk, batch*head) with Q/64 waves.
 // The chunk has Q/32 row tiles of 32 tokens; wave w takes tiles w and Q/32-1-w so
-// every wave does the same number of causal tile pairs.  The output is built
+// every wave does the same number of causal tile pairs (at Q = 64 with a small grid,
+// two waves take one tile each, so the chunk's two tiles run side by side).  The output is built
 // transposed, Y^T [P x 32 tokens], so that
 //   * C S^T:   A = S rows (p, n), B = C rows (i, n) -- both n-contiguous in HBM;
 //   * C B^T:   computed as (B C^T) with A = B rows (j, n), B = C rows (i, n); its
@@ -249,14 +252,18 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 // group, and the state used is S + beta_c H_g (H_g the true state at the group
 // start, fp32, from the group scan; beta is 0 in group 0, which adds nothing).
 // ===========================================================================
-template <typename T, int Q, bool CORR>
-__global__ __launch_bounds__(Q) void chunk_out_kernel(
+// NTH: threads per workgroup, Q/64 waves taking two row tiles each (NTH = Q) or, for a small
+// grid at Q = 64, two waves taking one each (NTH = 128: the chunk's two tiles side by side)
+template <typename T, int Q, bool CORR, int NTH>
+__global__ __launch_bounds__(NTH) void chunk_out_kernel(
     const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ G2, const float *__restrict__ dtT, const T *__restrict__ S,
     const float *__restrict__ D, T *__restrict__ y, const float *__restrict__ Hg,
     const float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng)
 {
-    constexpr int P = 64, NI = Q / 32, NTHR = Q;  // Q/64 waves
+    constexpr int P = 64, NI = Q / 32, NTHR = NTH;
+    constexpr int NPASS = 2 * Q / NTHR;   // row tiles per wave
+    static_assert(NPASS == 1 || NPASS == 2, "one or two row tiles per wave");
     constexpr int PITCH = Q + 16 / (int)sizeof(T);
     __shared__ __attribute__((aligned(16))) T XdT[P * PITCH];
     __shared__ float Gs[Q];
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(Q) void chunk_out_kernel(
         return f;
     };
 
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < NPASS; ++pass) {
         const int I = pass == 0 ? wave : NI - 1 - wave;
         const int i_loc = I * 32 + (lane & 31);
         const bool ivalid = t0 + i_loc < L;
@@ -484,6 +491,11 @@ hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const vo
     return state_pass_t<float>(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K, ng, st);
 }
 
+int chunk_out_f32_threads(const Shape &s)
+{
+    return (s.Q == 64 && s.nc * s.b * s.H < 1024) ? 128 : (int)s.Q;
+}
+
 template <typename T, int Q>
 static hipError_t chunk_out_tq(const Shape &s, const void *x, const void *B, const void *C,
                                const float *G2, const float *dtT, const void *S, const float *D,
@@ -491,15 +503,25 @@ static hipError_t chunk_out_tq(const Shape &s, const void *x, const void *B, con
                                hipStream_t st)
 {
     dim3 grid((unsigned)s.nc, (unsigned)(s.b * s.H));
-    if (Hg != nullptr)
-        hipLaunchKernelGGL((chunk_out_kernel<T, Q, true>), grid, dim3(Q), 0, st, (const T *)x,
-                           (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y, Hg, beta,
-                           (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
-    else
-        hipLaunchKernelGGL((chunk_out_kernel<T, Q, false>), grid, dim3(Q), 0, st, (const T *)x,
-                           (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y,
-                           (const float *)nullptr, (const float *)nullptr, (int)s.L, (int)s.H,
-                           (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, (int)s.nc, 1);
+    auto launch = [&](auto nth) {
+        constexpr int NTH = decltype(nth)::value;
+        if (Hg != nullptr)
+            hipLaunchKernelGGL((chunk_out_kernel<T, Q, true, NTH>), grid, dim3(NTH), 0, st, (const T *)x,
+                               (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y, Hg, beta,
+                               (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
+        else
+            hipLaunchKernelGGL((chunk_out_kernel<T, Q, false, NTH>), grid, dim3(NTH), 0, st, (const T *)x,
+                               (const T *)B, (const T *)C, G2, dtT, (const T *)S, D, (T *)y,
+                               (const float *)nullptr, (const float *)nullptr, (int)s.L, (int)s.H,
+                               (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, (int)s.nc, 1);
+    };
+    if constexpr (Q == 64) {
+        if (chunk_out_f32_threads(s) == 128) {
+            launch(std::integral_constant<int, 128>{});
+            return hipGetLastError();
+        }
+    }
+    launch(std::integral_constant<int, Q>{});
     return hipGetLastError();
 }
 

@@ -54,6 +54,11 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const 
                                       const float *Hg, const void *Hb, const float *beta,
                                       hipStream_t st);
 
+// Threads per fp32 chunk-output workgroup: two waves with one 32-token row tile each for
+// 64-token chunks when the grid has fewer than 1024 workgroups (the chunk's tiles side by
+// side), else Q (Q/64 waves with two row tiles each).
+int chunk_out_f32_threads(const Shape &s);
+
 // The launch configuration of the forward pass for shape s (host only).
 struct LaunchPlan {
     int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
