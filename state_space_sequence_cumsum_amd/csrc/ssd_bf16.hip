@@ -467,7 +467,11 @@ __global__ __launch_bounds__(256) void group_scan_kernel(float *__restrict__ Ug,
         for (int k = 0; k < NGMAX; ++k) {
             const int g = min(g0 + k, ng - 1);
             v[k] = *reinterpret_cast<const f32x4 *>(Ug + ((int64_t)bh * ng + g) * PN + e);
-            gm[k] = gam[(int64_t)bh * ng + g];
+            // per-lane load, in flight with the state loads (a scalar load is issued and
+            // waited for on its own)
+            int gi = bh * ng + g;
+            asm volatile("" : "+v"(gi));
+            gm[k] = gam[gi];
         }
 #pragma unroll
         for (int k = 0; k < NGMAX; ++k) {
