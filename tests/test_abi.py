@@ -191,6 +191,13 @@ def test_launch_plan_per_shape():
             f["co_head_blocked"]) == (1, 4, 64, 16, 1, 0)
     f2 = ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256, dtype="fp32"))
     assert (f2["sp_group_chunks"], f2["sp_groups"], f2["sp_workgroups"]) == (32, 2, 256)
+    # fp32 chunk output: two waves (one row tile each) for 64-token chunks below 1024
+    # workgroups, else Q threads (Q/64 waves with two row tiles each)
+    assert (f["co_workgroups"], f["co_threads"]) == (16, 128)
+    f3 = ssd.ssd_plan(_p(batch=2, seqlen=4096, nheads=16, dstate=128, chunk=64, dtype="fp32"))
+    assert (f3["co_workgroups"], f3["co_threads"]) == (2048, 64)
+    assert ssd.ssd_plan(_p(batch=2, seqlen=4096, nheads=7, dstate=128, chunk=64, dtype="fp32"))["co_threads"] == 128
+    assert f2["co_threads"] == 256
     # the plan refuses what the forward refuses
     with pytest.raises(ssd.SsdError) as ei:
         ssd.ssd_plan(_p(dstate=96))
