@@ -244,26 +244,31 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     };
     const int last_row = L - 1;
     auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
+    // Issue order: the values the x~ copy needs one step after this load (the chunk's
+    // last cumsum value, the weights, x) before the B tile, which is copied a step later:
+    // wait counts retire loads in issue order, so waiting for the first ones leaves the
+    // B loads in flight.
     auto load = [&](Regs &R, int u) {
         u = min(u, U - 1);
         const int t0 = tok0(u);
-#pragma unroll
-        for (int r = 0; r < BPT; ++r) {
-            const uint32_t off = (uint32_t)(min(t0 + bt_[r], last_row) * brow + bo[r]);
-            R.b[r] = *reinterpret_cast<const bf16x8 *>(Bbytes + off);
-        }
-#pragma unroll
-        for (int r = 0; r < XPT; ++r) {
-            const uint32_t off = (uint32_t)(min(t0 + xt_[r], last_row) * xrow + xo[r]);
-            R.x[r] = *reinterpret_cast<const bf16x8 *>(xbytes + off);
-        }
-#pragma unroll
-        for (int r = 0; r < XPT; ++r) R.w[r] = wh[t0 + xt_[r]];
         // the chunk's last cumsum value, as a per-lane load (a scalar load would
         // share the LDS wait counter and stall every LDS wait behind it)
         int gi = (c0 + u / NSUB) * Q + Q - 1;
         asm volatile("" : "+v"(gi));
         R.gl = Gh[gi];
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) R.w[r] = wh[t0 + xt_[r]];
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            const uint32_t off = (uint32_t)(min(t0 + xt_[r], last_row) * xrow + xo[r]);
+            R.x[r] = *reinterpret_cast<const bf16x8 *>(xbytes + off);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keeps this issue order
+#pragma unroll
+        for (int r = 0; r < BPT; ++r) {
+            const uint32_t off = (uint32_t)(min(t0 + bt_[r], last_row) * brow + bo[r]);
+            R.b[r] = *reinterpret_cast<const bf16x8 *>(Bbytes + off);
+        }
     };
     // LDS buffer indices are passed in as compile-time constants
     auto storeB = [&](const Regs &R, int kb) {
