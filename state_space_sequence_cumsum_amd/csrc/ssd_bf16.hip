@@ -1185,20 +1185,36 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
             }
         }
 
-        // y = Y + D x
+        // y = Y + D x.  Lanes l and l + 32 hold the same token; lane l has columns
+        // 8q .. 8q+3 of each 32-column half and lane l + 32 columns 8q+4 .. 8q+7.  One
+        // swap of the upper and lower 32 lanes per pair (q, q+1) gives lane l the 8
+        // columns of q and lane l + 32 those of q+1, so each store writes 16 bytes per lane
+        // and 32 contiguous bytes per token row (half as many store instructions)
         const float Dh = D[h];
         bf16 *yb = y + ((int64_t)b * L + t0 + i_loc) * xstride + (int64_t)h * P;
 #pragma unroll
         for (int pq = 0; pq < 2 / SPL; ++pq) {
             const int pp = SPL == 1 ? pq : hf;
+            u32x2 w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
                 const bf16x4 xv = tr_read4(Xd + skip_off + (pp * 32 + 8 * q) * XP);
                 bf16x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pq][4 * q + r] + Dh * (float)xv[r]);
-                *reinterpret_cast<bf16x4 *>(yb + p) = o;
+                w[q] = __builtin_bit_cast(u32x2, o);
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(w[2 * pr][d], w[2 * pr + 1][d], false, false);
+                    o[d] = sw[0];
+                    o[2 + d] = sw[1];
+                }
+                const int p = pp * 32 + 16 * pr + 8 * (lane >> 5);
+                *reinterpret_cast<u32x4 *>(yb + p) = o;
             }
         }
     }
