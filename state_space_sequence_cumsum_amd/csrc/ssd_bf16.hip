@@ -785,12 +785,15 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     }
 
     // ---------------- y = Y + D x ----------------
+    // Lanes l and l + 32 hold the same token (so both or neither pass the row check);
+    // the swap of their halves gives each lane 8 whole columns to store as 16 bytes
     if (iv) {
         const float Dh = D[h];
         const int yo = i_loc * (int)xstride;
         bf16 *yb = y + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
+            u32x2 w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int p = pp * 32 + 8 * q + 4 * (lane >> 5);
@@ -798,7 +801,19 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
                 bf16x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (bf16)(ya[pp][4 * q + r] + Dh * (float)xv[r]);
-                *reinterpret_cast<bf16x4 *>(yb + yo + p) = o;
+                w[q] = __builtin_bit_cast(u32x2, o);
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(w[2 * pr][d], w[2 * pr + 1][d], false, false);
+                    o[d] = sw[0];
+                    o[2 + d] = sw[1];
+                }
+                const int p = pp * 32 + 16 * pr + 8 * (lane >> 5);
+                *reinterpret_cast<u32x4 *>(yb + yo + p) = o;
             }
         }
     }
