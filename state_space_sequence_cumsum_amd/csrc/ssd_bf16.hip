@@ -1010,7 +1010,9 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     }
 
     // ================= per-head work =================
-    const int tg = (wi >> 1) * 8 + (lane & 7), cg = (wi & 1) * 8 + (lane >> 3);
+    // thread = 8 tokens (group tg) x 4 columns (group cg); lanes l and l + 32 take the
+    // two 4-column halves of one 8-column block
+    const int tg = (wi >> 1) * 8 + (lane & 7), cg = (wi & 1) * 8 + 2 * ((lane >> 3) & 3) + (lane >> 5);
     struct XRegs {
         u32x2 xv[8];
         float gt, ge, dt;
@@ -1025,9 +1027,21 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
         hl = min(hl, HB - 1);
         const int h = h_first + hl, bh = b * H + h;
         const char *xbb = reinterpret_cast<const char *>(x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P);
+        // 16-byte loads: lane l reads tokens 0..3 of the group, lane l + 32 tokens 4..7, both
+        // the whole 8-column block; swapping the upper and lower 32 lanes leaves lane l with
+        // columns 0..3 and lane l + 32 with columns 4..7 of all 8 tokens
+        const int c8 = (cg & ~1) * 4, tsel = 4 * (lane >> 5);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            R.xv[r] = *reinterpret_cast<const u32x2 *>(xbb + (uint32_t)(((tg * 8 + r) * (int)xstride + cg * 4) * 2));
+        for (int r = 0; r < 4; ++r) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                xbb + (uint32_t)(((tg * 8 + tsel + r) * (int)xstride + c8) * 2));
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(v[d], v[2 + d], false, false);
+                R.xv[r][d] = sw[0];
+                R.xv[4 + r][d] = sw[1];
+            }
+        }
         const float *Gh = G2 + (int64_t)bh * Lp + t0;
         R.gt = Gh[tq];
         R.ge = Gh[tq | 31];
