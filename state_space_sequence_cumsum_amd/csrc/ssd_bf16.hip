@@ -666,13 +666,25 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     // packed per p column.  A wave covers 8 token groups (lane % 8) x 8 column
     // groups (lane / 8).
     {
-        const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + (lane >> 3);
+        // lanes l and l + 32 take the two 4-column halves of one 8-column block: each
+        // loads four tokens of the block as 16-byte rows (lane l tokens 0..3, lane l + 32
+        // tokens 4..7) and a swap of the upper and lower 32 lanes leaves each with its
+        // 4 columns of all 8 tokens
+        const int tg = (w >> 1) * 8 + (lane & 7), cg = (w & 1) * 8 + 2 * ((lane >> 3) & 3) + (lane >> 5);
         const char *xbb = reinterpret_cast<const char *>(xb);
         u32x2 xv[8];
+        const int c8 = (cg & ~1) * 4, tsel = 4 * (lane >> 5);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            xv[r] = *reinterpret_cast<const u32x2 *>(
-                xbb + (uint32_t)((min(tg * 8 + r, nvalid - 1) * (int)xstride + cg * 4) * 2));
+        for (int r = 0; r < 4; ++r) {
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                xbb + (uint32_t)((min(tg * 8 + tsel + r, nvalid - 1) * (int)xstride + c8) * 2));
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(v[e], v[2 + e], false, false);
+                xv[r][e] = sw[0];
+                xv[4 + r][e] = sw[1];
+            }
+        }
         const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dh + tg * 8);
         const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dh + tg * 8 + 4);
         const int tq = tid & (Q - 1);
