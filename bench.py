@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """Throughput of the Mamba-2 SSD chunked forward pass on one MI355X.
 
-One step = one whole forward (chunk cumsum, state pass, chunk output) over the
-16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints one
-JSON line:  tokens/s of ``ssd_forward`` over K steps back to back (called through
-a ``ForwardPlan``, or with ``--graph`` replayed from a HIP graph); per-stage
-durations (mean, median, p10, p90) from HIP events that the library records on
-the launch stream between its stages, over K further steps run right after; the
-roofline of the dominant stage from its algorithmic bytes and flops; ``cold``:
+One step = one whole forward (chunk cumsum, state pass, group scan, chunk output)
+over the 16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints
+one JSON line:  tokens/s of ``ssd_forward`` over K steps back to back (called
+through a ``ForwardPlan``, or with ``--graph`` replayed from a HIP graph); then,
+after that timed region, per-kernel durations (mean, median, p10, p90) from HIP
+events that the library records on the launch stream right before and after each
+of the four launches, over max(K, --kernel-reps) further forwards; the roofline of
+the dominant kernel from its algorithmic bytes and that mean duration; ``cold``:
 the median forward when a 1 GiB write flushes L2 and the Infinity Cache before
 each rep; and the fp64 CPU oracle timed on this host.
 
@@ -32,7 +33,11 @@ device-to-device copy of known size calibrates the counter:
 
 The last command writes profiles/traffic_<workload>.json, which later runs report
 as ``roofline.traffic`` as long as the kernel sources hash to the same value (null
-otherwise).
+otherwise).  Kernel durations of the same command, for comparison with the line's
+roofline:
+
+    rocprofv3 --kernel-trace --stats -f csv -d DIR_T -o run -- python3 bench.py --gpus 1 --steps 20 --warmup 5
+    python bench.py --summarize-trace DIR_T
 """
 from __future__ import annotations
 
@@ -50,13 +55,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-KERNEL_SOURCES = ["state_space_sequence_cumsum_amd/csrc/ssd_bf16.hip",
-                  "state_space_sequence_cumsum_amd/csrc/ssd_kernels.hip",
-                  "state_space_sequence_cumsum_amd/csrc/ssd_device.h",
-                  "state_space_sequence_cumsum_amd/csrc/ssd_api.cpp",
-                  "state_space_sequence_cumsum_amd/build.py"]
+# what source_hash() covers: every file the library is built from, its public header
+# and the build script (which holds the compiler flags)
+KERNEL_SOURCE_GLOBS = ["state_space_sequence_cumsum_amd/csrc/*", "include/ssd.h",
+                       "state_space_sequence_cumsum_amd/build.py"]
 KERNEL_NAMES = {"chunk_cumsum": "chunk_cumsum_kernel", "state_pass": "state_pass",
                 "group_scan": "group_scan_kernel", "chunk_out": "chunk_out"}
+# the four launches of a forward, in order; ssd_forward_timed records an event before
+# the first and after each
+STAGES = ["chunk_cumsum", "state_pass", "group_scan", "chunk_out"]
 COPY_KERNEL = "copyBuffer"
 FLUSH_MIB = 1024                # written before each cold rep: > L2 + 256 MB Infinity Cache
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
@@ -129,19 +136,42 @@ def cpu_baseline(w, inp, budget_s=20.0):
     el = statistics.median(runs)
     tok = w.batch * w.seqlen * n_units / units_all
     return {"value": tok / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "usable_cores": nthr, "cpu_model": cpu_model(),
             "sample": f"{n_units} of {units_all} (batch, head) units over all {w.seqlen} tokens "
                       f"(fp64 sequential recurrence, y and hT); tokens/s = tokens x sampled "
                       f"fraction of heads / median wall time of {len(runs)} run(s), {el:.2f} s"}
 
 
+def kernel_sources():
+    """Sorted repository paths of everything the library is built from."""
+    files = set()
+    for g in KERNEL_SOURCE_GLOBS:
+        files.update(os.path.relpath(f, ROOT) for f in glob.glob(os.path.join(ROOT, g))
+                     if os.path.isfile(f))
+    return sorted(files)
+
+
 def source_hash():
-    """sha256 over the kernel sources and build flags: counter figures taken from another
-    version of the kernels are not reported."""
+    """sha256 over the kernel sources, the header and the build script (with its flags):
+    counter figures taken from another version of the kernels are not reported."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources():
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def traffic_file(w):
@@ -194,6 +224,69 @@ def summarize_pmc(w, fetch_dir, write_dir, copy_mib):
     with open(traffic_file(w), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def kernel_label(name):
+    """Short readable label of a kernel name as rocprofv3 reports it (mangled or not):
+    the function name with its template arguments, without the parameter list."""
+    import re
+    m = re.match(r"_ZN3ssd(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        base = name[m.end():m.end() + n]
+        rest = name[m.end() + n:]
+        args = []
+        if rest.startswith("I"):
+            for tok in re.findall(r"Li(\d+)E|Lb([01])E|(DF16b)|(?<=[IE])(f)(?=[LEDf])", rest[1:rest.find("EE") + 1]):
+                num, boolean, bf, fl = tok
+                args.append(num or ("true" if boolean == "1" else "false" if boolean else "")
+                            or ("bf16" if bf else "float"))
+        return base + (f"<{','.join(args)}>" if args else "")
+    name = re.sub(r"^void\s+", "", name)
+    name = name.replace("ssd::", "")
+    depth = 0
+    for i, ch in enumerate(name):   # cut at the parameter list (outside the template brackets)
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i].replace(" ", "")
+    return name
+
+
+def read_kernel_stats(d):
+    """Rows of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv): name, calls
+    and durations in microseconds, with the forward-pass stage each kernel belongs to."""
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Name"]
+                kind = next((k for k, key in KERNEL_NAMES.items() if key in name), None)
+                rows.append({"name": name, "kind": kind, "calls": int(r["Calls"]),
+                             "avg_us": float(r["AverageNs"]) / 1e3,
+                             "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                             "share": float(r["Percentage"])})
+    if not rows:
+        raise SystemExit(f"no *kernel_stats.csv under {d}")
+    return rows
+
+
+def summarize_trace(w, d):
+    """Markdown table of a kernel-trace run, with the algorithmic bandwidth of each
+    forward-pass kernel at its average duration (the figure the bench line's roofline
+    reports from HIP events)."""
+    alg = algorithmic(w)
+    lines = ["| kernel | calls | average (µs) | min (µs) | max (µs) | share | algorithmic GB/s "
+             "at the average | fraction of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
+    for r in sorted(read_kernel_stats(d), key=lambda r: -r["share"]):
+        gbs = frac = "—"
+        if r["kind"] in alg:
+            v = alg[r["kind"]]["bytes"] / (r["avg_us"] * 1e-6) / 1e9
+            gbs, frac = f"{v:.0f}", f"{v / HBM_PEAK_GBS:.3f}"
+        name = kernel_label(r["name"])
+        lines.append(f"| `{name}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
+                     f"{r['max_us']:.2f} | {r['share']:.1f} % | {gbs} | {frac} |")
+    print("\n".join(lines))
 
 
 def bench_step(args):
@@ -284,7 +377,7 @@ def bench_sweep(args):
             y = torch.empty_like(d["x"])
             prob = ssd.problem_of(d["x"], d["B"], w.chunk)
             ws = ssd.workspace_for(prob, dev)
-            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ssd.FORWARD_EVENTS)]
                    for _ in range(args.steps)]
             for row in evs:
                 for e in row:
@@ -308,13 +401,15 @@ def bench_sweep(args):
             torch.cuda.synchronize()
             st = {n: statistics.median(evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3
                                        for k in range(args.steps))
-                  for i, n in enumerate(["chunk_cumsum", "state_pass", "chunk_out"])}
+                  for i, n in enumerate(STAGES)}
             alg = algorithmic(w)
+            plan = ssd.ssd_plan(prob)
             print(json.dumps({"workload": w.name, "tokens_per_s": round(w.batch * L / el),
                               "us_per_forward": round(el * 1e6, 2),
-                              "stage_median_us": {n: round(v, 2) for n, v in st.items()},
+                              "kernel_median_us": {n: round(v, 2) for n, v in st.items()},
                               "frac_hbm": {n: round(alg[n]["bytes"] / (st[n] * 1e-6) / 1e9
-                                                    / HBM_PEAK_GBS, 4) for n in st}}),
+                                                    / HBM_PEAK_GBS, 4) for n in st if n in alg},
+                              "plan": plan}),
                   flush=True)
             del d, y, ws
 
@@ -326,12 +421,16 @@ def main():
     # idle state: with 10 warm-up forwards the timed loop still includes the ramp
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--kernel-reps", type=int, default=400,
+                    help="forwards with per-launch events after the timed region (at least --steps)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a rocprofv3 --kernel-trace --stats run as a markdown table")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="forwards timed after a cache flush each (0: skip)")
     ap.add_argument("--graph", action="store_true",
@@ -342,9 +441,13 @@ def main():
                     help="time the decode step at batch B instead of the forward pass")
     args = ap.parse_args()
 
-    if args.summarize_pmc:
+    if args.summarize_pmc or args.summarize_trace:
         from state_space_sequence_cumsum_amd.inputs import HEADLINE, WORKLOADS
-        summarize_pmc(WORKLOADS[args.workload or HEADLINE], *args.summarize_pmc, args.copy_mib)
+        w = WORKLOADS[args.workload or HEADLINE]
+        if args.summarize_pmc:
+            summarize_pmc(w, *args.summarize_pmc, args.copy_mib)
+        else:
+            summarize_trace(w, args.summarize_trace)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -373,8 +476,10 @@ def main():
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
     ws = ssd.workspace_for(prob, dev)
     stream = torch.cuda.current_stream(dev)
-    names = ["chunk_cumsum", "state_pass", "chunk_out"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    names = STAGES
+    reps = max(args.steps, args.kernel_reps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ssd.FORWARD_EVENTS)]
+           for _ in range(reps)]
     for row in evs:          # create the HIP events before they are handed to the library
         for e in row:
             e.record(stream)
@@ -421,14 +526,16 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # --- stage region: K more forwards through ssd_forward_timed, with HIP events
-    # recorded on the launch stream between the three stages (the event packets add a
-    # few microseconds per forward, so they stay out of the throughput region) ---
-    for k in range(args.steps):
+    # --- kernel region, after the timed region: `reps` more forwards through
+    # ssd_forward_timed, which records a HIP event on the launch stream right before and
+    # right after each of the four launches, so an event pair brackets exactly one kernel.
+    # The event packets add a little time per forward, so they stay out of the throughput
+    # region.  These per-launch times are the kernels' durations for the roofline. ---
+    for k in range(reps):
         forward(evs[k])
     torch.cuda.synchronize()
 
-    per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)]
+    per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(reps)]
            for i, n in enumerate(names)}   # microseconds
     kern = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
                 "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v)}
@@ -452,6 +559,8 @@ def main():
 
     alg = algorithmic(w)
     for n in names:
+        if n not in alg:      # the group scan is this design's own step: no algorithmic count
+            continue
         t = kern[n]["mean_us"] * 1e-6
         kern[n]["GB_s"] = alg[n]["bytes"] / t / 1e9
         kern[n]["TFLOP_s"] = alg[n]["flops"] / t / 1e12
@@ -472,7 +581,10 @@ def main():
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(alg[dom]["bytes"]),
-            "mean_launch_us": round(kern[dom]["mean_us"], 2)}
+            "mean_launch_us": round(kern[dom]["mean_us"], 2),
+            "timing": f"mean of {reps} HIP-event intervals, each bracketing only the {dom} "
+                      f"launch (events recorded on its launch stream right before and after it), "
+                      f"in {reps} whole forwards run after the timed region"}
 
     ms = elapsed / args.steps * 1e3
     tokens = w.batch * w.seqlen
@@ -493,7 +605,7 @@ def main():
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "initial_state": w.has_h0, "accumulate": "fp32"},
         "kernels": {n: {k: round(v, 4) for k, v in kern[n].items()} for n in names},
-        "stage_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
+        "kernel_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
         "roofline": roof,
         "launch": "graph" if args.graph else "plan",
     }

@@ -134,11 +134,14 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
                        const float *h0, void *y, float *hT, void *workspace,
                        size_t workspace_bytes, void *stream);
 
-/* ssd_forward with stage timing marks, for profiling the forward pass as it runs.
- * `events` holds 4 hipEvent_t handles created by the caller; they are recorded on
- * `stream` before stage 1, after stage 1, after stage 2 (including the group scan
- * when the state pass is split) and after stage 3.  events == NULL behaves exactly
- * like ssd_forward. */
+/* ssd_forward with timing marks, for profiling the forward pass as it runs.
+ * `events` holds SSD_FORWARD_EVENTS (5) hipEvent_t handles created by the caller;
+ * they are recorded on `stream` right before stage 1, after stage 1, after the
+ * state pass, after the group scan (recorded straight after the previous mark when
+ * the state pass runs as one serial chain and no scan is launched) and after stage
+ * 3, so each pair of consecutive marks brackets exactly one kernel launch (or
+ * none).  events == NULL behaves exactly like ssd_forward. */
+#define SSD_FORWARD_EVENTS 5
 ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
                              const float *A, const void *B, const void *C, const float *D,
                              const float *h0, void *y, float *hT, void *workspace,
@@ -154,7 +157,9 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
  * A, D [H] float32; h [b, H, P, N] float32, read and overwritten in place (the hT
  * layout of ssd_forward, so a forward's final state continues directly).
  * problem->seqlen must be 1 and problem->chunk is ignored; any headdim >= 1 and
- * dstate a multiple of 64 up to 512.  The exponential is exp2 of A dt log2(e) in
+ * dstate a multiple of 64 up to 512, with batch * nheads * ceil(headdim / 4) at most
+ * 2^26 - 4 (one 64-lane wave per 4 state rows; the dispatch grid counts work-items in
+ * 32 bits), else SSD_ERR_UNSUPPORTED before any launch.  The exponential is exp2 of A dt log2(e) in
  * fp32, the update and the dot product are fp32, y is rounded to `dtype`.  All
  * pointers are required. */
 ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, const float *A,

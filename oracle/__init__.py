@@ -29,7 +29,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "ssd_oracle.c")
-LIBRARY = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_LIBRARY points the pins at another build of the oracle (the planted-mistake
+# test builds deliberately wrong copies of ssd_oracle.c and checks that the pins fail)
+LIBRARY = os.environ.get("SSD_ORACLE_LIBRARY") or os.path.join(_HERE, "libssd_oracle.so")
 
 _F64, _F32, _BF16 = 0, 1, 2
 _lib = None
@@ -38,11 +40,16 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile ssd_oracle.c into libssd_oracle.so with gcc (-O2, no fast-math)."""
     if force or not os.path.exists(LIBRARY):
-        tmp = LIBRARY + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-shared", "-fPIC",
-                               "-pthread", SOURCE, "-o", tmp, "-lm"])
-        os.replace(tmp, LIBRARY)
+        compile_oracle(SOURCE, LIBRARY)
     return LIBRARY
+
+
+def compile_oracle(source: str, library: str) -> None:
+    """gcc -O2 (no fast-math) of an oracle source file into a shared library."""
+    tmp = library + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-shared", "-fPIC",
+                           "-pthread", source, "-o", tmp, "-lm"])
+    os.replace(tmp, library)
 
 
 def _load():

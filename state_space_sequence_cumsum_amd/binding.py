@@ -20,6 +20,7 @@ LIBRARY = os.path.join(_PKG, "libssd.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
 
 SSD_F32, SSD_BF16 = 0, 1
+FORWARD_EVENTS = 5      # SSD_FORWARD_EVENTS: marks around stage 1, state pass, group scan, stage 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED"}
 
@@ -276,17 +277,19 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
                 workspace=None, stream=None, events=None):
     """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None).
 
-    ``events``: optional 4 recorded-once ``torch.cuda.Event`` objects; they are
-    re-recorded on the launch stream around the three stages (ssd_forward_timed).
+    ``events``: optional ``FORWARD_EVENTS`` (5) recorded-once ``torch.cuda.Event``
+    objects; they are re-recorded on the launch stream around each of the four
+    launches (stage 1, state pass, group scan, stage 3; ssd_forward_timed).
     """
     _, args, y, hT, _ = _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace,
                                       stream)
     if events is None:
         _raise(lib().ssd_forward(*args), "ssd_forward")
     else:
-        if len(events) != 4 or not all(getattr(e, "cuda_event", 0) for e in events):
-            raise ValueError("events must be 4 torch.cuda.Event objects recorded at least once")
-        arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        if len(events) != FORWARD_EVENTS or not all(getattr(e, "cuda_event", 0) for e in events):
+            raise ValueError(f"events must be {FORWARD_EVENTS} torch.cuda.Event objects "
+                             "recorded at least once")
+        arr = (ctypes.c_void_p * FORWARD_EVENTS)(*[e.cuda_event for e in events])
         _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
     return y, hT
 

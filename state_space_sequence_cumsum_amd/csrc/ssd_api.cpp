@@ -62,11 +62,15 @@ ssd_status check_step_shape(const ssd_problem *p)
     if (p->seqlen != 1 || p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
     if (p->dtype != SSD_F32 && p->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (p->dstate % 64 != 0 || p->dstate > 512) return SSD_ERR_UNSUPPORTED;
-    // 32-bit head and row indices, and a grid of at most 2^31 workgroups
+    // 32-bit head and row indices
     if (p->batch > (int64_t(1) << 31) || p->nheads > (int64_t(1) << 30) ||
         p->headdim > (int64_t(1) << 30))
         return SSD_ERR_UNSUPPORTED;
     if (p->batch * p->nheads > (int64_t(1) << 31) / p->headdim) return SSD_ERR_UNSUPPORTED;
+    // the dispatch grid counts work-items in 32 bits: one wave of 64 per ceil(P/4) rows of
+    // each (batch, head), in workgroups of 4 waves, so at most 2^24 - 1 workgroups
+    const int64_t waves = p->batch * p->nheads * ((p->headdim + 3) / 4);
+    if ((waves + 3) / 4 > (int64_t(1) << 24) - 1) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -204,8 +208,9 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
-    if (events != nullptr && (!events[0] || !events[1] || !events[2] || !events[3]))
-        return SSD_ERR_NULL_ARG;
+    if (events != nullptr)
+        for (int i = 0; i < SSD_FORWARD_EVENTS; ++i)
+            if (!events[i]) return SSD_ERR_NULL_ARG;
     const ssd::Shape s = make_shape(problem);
     const Layout l = layout_of(s);
     if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
@@ -228,13 +233,15 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     if (r == SSD_OK) r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
     if (r == SSD_OK) r = mark(1);
     if (r == SSD_OK)
-        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, Hb,
-                                                      gam, beta, hs));
+        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam,
+                                                      beta, hs));
     if (r == SSD_OK) r = mark(2);
+    if (r == SSD_OK) r = hip_status(ssd::launch_group_scan(s, l.gp, hT, Ug, Hb, gam, hs));
+    if (r == SSD_OK) r = mark(3);
     if (r == SSD_OK)
         r = hip_status(
             ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, Hb, beta, hs));
-    if (r == SSD_OK) r = mark(3);
+    if (r == SSD_OK) r = mark(4);
     return r;
 }
 

@@ -1372,14 +1372,19 @@ Grouping state_pass_groups(const Shape &s)
 
 hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
                                      const void *B, const float *G2, const float *wT,
-                                     const float *h0, void *S, float *hT, float *Ug, void *Hb,
-                                     float *gam, float *beta, hipStream_t st)
+                                     const float *h0, void *S, float *hT, float *Ug, float *gam,
+                                     float *beta, hipStream_t st)
 {
     if (gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
-    hipError_t e = s.bf16 ? sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st)
-                          : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta,
-                                                          gp.K, gp.ng, st);
-    if (e != hipSuccess) return e;
+    return s.bf16 ? sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st)
+                  : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta, gp.K,
+                                                  gp.ng, st);
+}
+
+hipError_t launch_group_scan(const Shape &s, const Grouping &gp, float *hT, float *Ug, void *Hb,
+                             const float *gam, hipStream_t st)
+{
+    if (gp.ng <= 1) return hipSuccess;   // one serial chain: the state pass wrote hT itself
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
     // fp32 group-start states are read only by single-head chunk-output launches

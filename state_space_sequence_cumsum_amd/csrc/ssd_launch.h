@@ -30,11 +30,13 @@ struct Grouping {
 Grouping state_pass_groups(const Shape &s);
 
 // Grouped state pass as used by the forward pass: with ng > 1, S receives
-// chunk-start states relative to their group, Ug the true group-start states
-// H_g (after the group scan), beta the per-chunk decay since the group start;
-// hT is the true final state.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng],
-// beta [b*H, nc], all fp32, and for bf16 problems Hb [b*H, ng, P, N] bf16 (H_g
-// rounded, zeros for group 0).
+// chunk-start states relative to their group, Ug the final local state of each
+// group, gam each group's decay and beta the per-chunk decay since the group
+// start; with ng == 1 it is the plain state pass (true states, hT written).
+// launch_group_scan then (ng > 1 only) turns Ug into the true group-start states
+// H_g and writes hT.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng], beta [b*H, nc],
+// all fp32, and for bf16 problems Hb [b*H, ng, P, N] bf16 (H_g rounded, zeros for
+// group 0).
 // fp32 state pass over ng groups of K chunks (ssd_kernels.hip): local chunk-start
 // states into S, final local states into Ug, decays into gam and beta.
 hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const void *B,
@@ -43,8 +45,10 @@ hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const vo
                                          int ng, hipStream_t st);
 hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
                                      const void *B, const float *G2, const float *wT,
-                                     const float *h0, void *S, float *hT, float *Ug, void *Hb,
-                                     float *gam, float *beta, hipStream_t st);
+                                     const float *h0, void *S, float *hT, float *Ug, float *gam,
+                                     float *beta, hipStream_t st);
+hipError_t launch_group_scan(const Shape &s, const Grouping &gp, float *hT, float *Ug, void *Hb,
+                             const float *gam, hipStream_t st);
 
 // Chunk output that adds beta_c H_g to the handed-over chunk-start states
 // (Hg == NULL: S already holds true states).  Hg is fp32, Hb its bf16 copy.

@@ -1,4 +1,7 @@
 """Helpers shared by the GPU parity tests: tolerances and device transfer."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -29,8 +32,30 @@ def rel_err(out, ref):
     return np.abs(out - ref).max() / (den if den > 0 else 1.0)
 
 
+def log_margin(what, err, tol):
+    """Append one parity margin to the JSON-lines file named by SSD_PARITY_LOG (if set)."""
+    path = os.environ.get("SSD_PARITY_LOG")
+    if path:
+        case = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"case": case, "what": what, "err": float(err), "tol": tol}) + "\n")
+
+
 def check(out, ref, tol, what):
     e = rel_err(out, ref)
     print(f"  {what}: max|err|/max|ref| = {e:.3e} (bound {tol:.0e})", flush=True)
+    log_margin(what, e, tol)
     assert e <= tol, f"{what}: relative error {e:.3e} exceeds {tol:.0e}"
+    return e
+
+
+def check_dev(out, ref, tol, what):
+    """check() for two device tensors of any size, reduced on the device."""
+    o, r = out.float(), ref.float()
+    assert bool(torch.isfinite(o).all()), f"{what}: non-finite values"
+    den = r.abs().max().item()
+    e = (o - r).abs().max().item() / (den if den > 0 else 1.0)
+    print(f"  {what}: max|diff|/max|ref| = {e:.3e} (bound {tol:.0e})", flush=True)
+    log_margin(what, e, tol)
+    assert e <= tol, f"{what}: relative difference {e:.3e} exceeds {tol:.0e}"
     return e

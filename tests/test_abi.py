@@ -88,7 +88,8 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.ssd_forward(ctypes.byref(bad), None, None, None, None, None, None, None, None,
                            None, None, 0, None) == 2
     # timed forward: events array with a NULL handle
-    ev = (ctypes.c_void_p * 4)(fake.value, fake.value, None, fake.value)
+    ev = (ctypes.c_void_p * binding.FORWARD_EVENTS)(fake.value, fake.value, fake.value, None,
+                                                     fake.value)
     assert lib.ssd_forward_timed(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
                                  None, fake, 10**12, None, ev) == 1
     assert lib.ssd_last_hip_error() == 0
@@ -130,6 +131,12 @@ def _sp(**kw):
     (dict(dstate=576), 3),
     (dict(dtype=9), 3),
     (dict(batch=1 << 20, nheads=1 << 12, headdim=64), 3),
+    # the dispatch grid: b * H * ceil(P / 4) waves in workgroups of 4 waves, at most
+    # 2^24 - 1 workgroups (2^32 work-items); within the 2^31 row-index limit
+    (dict(batch=1 << 24, nheads=4, headdim=1, dstate=64), 3),          # 2^26 waves
+    (dict(batch=(1 << 24) - 1, nheads=4, headdim=1, dstate=64), 1),    # 2^26 - 4 waves
+    (dict(batch=1 << 22, nheads=4, headdim=13, dstate=64), 3),         # ceil(13/4) = 4 rows
+    (dict(batch=(1 << 22) - 1, nheads=4, headdim=13, dstate=64), 1),
 ])
 def test_step_validates_before_launching(kw, status):
     lib = binding.lib()

@@ -14,7 +14,7 @@ import torch
 import oracle
 import state_space_sequence_cumsum_amd as ssd
 from state_space_sequence_cumsum_amd.inputs import WORKLOADS, Workload, make_inputs
-from gpu_util import TOL, check, f64, require_gpu, to_dev
+from gpu_util import TOL, check, check_dev, f64, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -359,7 +359,7 @@ def test_forward_timed_events():
     w = _wl("timed", "bf16", 1, 1024, 2, 64, 128, 1, 128)
     inp = make_inputs(w, 12)
     d = to_dev(inp, dev)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(ssd.FORWARD_EVENTS)]
     for e in evs:
         e.record()
     y1, h1 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
@@ -367,8 +367,11 @@ def test_forward_timed_events():
     y2, h2 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
-    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(ssd.FORWARD_EVENTS - 1)]
     assert all(t >= 0 for t in times), times
+    with pytest.raises(ValueError):
+        ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                        events=evs[:4])
 
 
 def test_errors_before_launch():
@@ -417,12 +420,20 @@ def test_full_workload_sampled(name, units):
     tol = TOL[w.dtype]
     check(y_s, ref["y"], tol, "y (sampled units)")
     check(np.stack([f64(hT[b, h]) for b, h in zip(b_idx, h_idx)]), ref["hT"], tol, "hT (sampled units)")
-    S, _ = _stage_states(inp, w, dev)
+    # every (batch, head) of the forward (grouped state pass, group scan, head-blocked
+    # chunk output) against the plain stage path (one serial state chain per head, the
+    # ungrouped chunk output), which runs other kernel instances: both sides are within
+    # the bound of the oracle, so their difference is bounded by it too
+    d = to_dev(inp, dev)
+    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S, hT2 = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"])
     check(np.stack([f64(S[b, h]) for b, h in zip(b_idx, h_idx)]), ref["snaps"], tol,
           "chunk-start states (stage 2, sampled units)")
-    del S
-    # every output element was written and is finite
-    assert torch.isfinite(y.float()).all() and torch.isfinite(hT).all()
+    y2 = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
+    torch.cuda.synchronize()
+    check_dev(y, y2, tol, "y, every unit: forward against the stage path")
+    check_dev(hT, hT2, tol, "hT, every unit: forward against the stage path")
+    del S, y2, G2, dtT, wT
 
 
 @pytest.mark.slow
