@@ -5,10 +5,12 @@ One step = one whole forward (chunk cumsum, state pass, group scan, chunk output
 over the 16K-token, 32-head, N=256 bf16 workload, inputs resident in HBM.  Prints
 one JSON line:  tokens/s of ``ssd_forward`` over K steps back to back (called
 through a ``ForwardPlan``, or with ``--graph`` replayed from a HIP graph); then,
-after that timed region, per-kernel durations (mean, median, p10, p90) from HIP
-events that the library records on the launch stream right before and after each
-of the four launches, over max(K, --kernel-reps) further forwards; the roofline of
-the dominant kernel from its algorithmic bytes and that mean duration; ``cold``:
+after that timed region, per-kernel durations (mean, median, p10, p90): for the
+chunk cumsum, state pass and chunk output, max(K, --kernel-reps) launches of each
+kernel alone, back to back, in batches between HIP-event pairs; for the group scan
+(and, as ``kernels_in_forward``, for all four) event pairs that the library records
+right before and after each launch inside whole forwards; the roofline of the
+dominant kernel from its algorithmic bytes and its mean duration alone; ``cold``:
 the median forward when a 1 GiB write flushes L2 and the Infinity Cache before
 each rep; and the fp64 CPU oracle timed on this host.
 
@@ -505,6 +507,9 @@ def main():
         plan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                                chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream)
         timed = plan.run
+    # stage launches for the kernel-alone timing, on the launch stream
+    aplan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                            chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream)
 
     if args.copy_mib > 0:   # a plain copy of known size, outside the timed region
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -526,20 +531,49 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # --- kernel region, after the timed region: `reps` more forwards through
+    # --- in-forward region, after the timed region: `reps` more forwards through
     # ssd_forward_timed, which records a HIP event on the launch stream right before and
-    # right after each of the four launches, so an event pair brackets exactly one kernel.
-    # The event packets add a little time per forward, so they stay out of the throughput
-    # region.  These per-launch times are the kernels' durations for the roofline. ---
+    # right after each of the four launches, so an event pair brackets exactly one kernel
+    # (and the event packet's own time).  The packets add a few microseconds per launch,
+    # so they stay out of the throughput region. ---
     for k in range(reps):
         forward(evs[k])
     torch.cuda.synchronize()
 
     per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(reps)]
            for i, n in enumerate(names)}   # microseconds
-    kern = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
-                "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v)}
-            for n, v in per.items()}
+    in_fwd = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
+                  "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v)}
+              for n, v in per.items()}
+
+    # --- kernel-alone region: each of the three method kernels launched `reps` times back
+    # to back by itself (ssd_forward_stage on the workspace the last forward filled), in
+    # batches bracketed by one HIP-event pair each, so event packets never sit between two
+    # launches; a batch's interval / its launches is the kernel's duration.  The chunk
+    # output runs first (the workspace then holds a whole forward), the state pass last.
+    # The group scan, which is not idempotent, keeps its in-forward event timing. ---
+    aplan.run()
+    torch.cuda.synchronize()
+    nb = 10
+    rb = max(1, reps // nb)
+    kern = {}
+    for n, stage in (("chunk_out", 3), ("chunk_cumsum", 0), ("state_pass", 1)):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(nb)]
+        for a, z in pairs:
+            a.record(stream)
+            for _ in range(rb):
+                aplan.run_stage(stage)
+            z.record(stream)
+        torch.cuda.synchronize()
+        v = [a.elapsed_time(z) * 1e3 / rb for a, z in pairs]
+        kern[n] = {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
+                   "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v),
+                   "launches": nb * rb}
+    aplan.run()       # the workspace as a whole forward leaves it
+    torch.cuda.synchronize()
+    kern["group_scan"] = dict(in_fwd["group_scan"], timing="in-forward event pair")
+    kern = {n: kern[n] for n in names}
 
     # --- cold region: each forward after a write of FLUSH_MIB through the caches, so
     # that inputs come from HBM rather than L2 or the Infinity Cache ---
@@ -582,9 +616,10 @@ def main():
             "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(alg[dom]["bytes"]),
             "mean_launch_us": round(kern[dom]["mean_us"], 2),
-            "timing": f"mean of {reps} HIP-event intervals, each bracketing only the {dom} "
-                      f"launch (events recorded on its launch stream right before and after it), "
-                      f"in {reps} whole forwards run after the timed region"}
+            "timing": f"{kern[dom]['launches']} launches of {dom} alone, back to back on its "
+                      f"launch stream after the timed region (ssd_forward_stage on the workspace "
+                      f"of the last forward), in {nb} batches each bracketed by one HIP-event "
+                      f"pair; mean = total event time / launches"}
 
     ms = elapsed / args.steps * 1e3
     tokens = w.batch * w.seqlen
@@ -604,8 +639,12 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "initial_state": w.has_h0, "accumulate": "fp32"},
-        "kernels": {n: {k: round(v, 4) for k, v in kern[n].items()} for n in names},
+        "kernels": {n: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in kern[n].items()}
+                    for n in names},
         "kernel_sum_us": round(sum(kern[n]["mean_us"] for n in names), 2),
+        # event pairs around each launch inside whole forwards (each pair adds the event
+        # packet's own ~2-3 us to the interval)
+        "kernels_in_forward": {n: {k: round(v, 3) for k, v in in_fwd[n].items()} for n in names},
         "roofline": roof,
         "launch": "graph" if args.graph else "plan",
     }

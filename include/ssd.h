@@ -142,6 +142,22 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
  * 3, so each pair of consecutive marks brackets exactly one kernel launch (or
  * none).  events == NULL behaves exactly like ssd_forward. */
 #define SSD_FORWARD_EVENTS 5
+
+/* One of the four launches of ssd_forward, alone: stage 0 the chunk cumsum, 1 the state
+ * pass, 2 the group scan (no launch when the state pass runs as one serial chain), 3 the
+ * chunk output; ssd_forward issues stages 0, 1, 2, 3 in this order on one workspace.
+ * For timing one kernel by itself: a stage reads the inputs and what the earlier stages
+ * left in `workspace` (filled by a previous ssd_forward or by the earlier stages of the
+ * same problem and inputs) and recomputes its own results, so stages 0, 1 and 3 may be
+ * repeated back to back (stage 1 writes hT when it runs as one chain: h0 and hT must not
+ * be the same buffer then).  Stage 2 rewrites part of the workspace in place and belongs
+ * once after each stage 1; after a repeated stage 1, run stage 2 before stage 3.  A stage
+ * outside 0..3 returns SSD_ERR_UNSUPPORTED.  Other arguments and errors as for
+ * ssd_forward. */
+ssd_status ssd_forward_stage(const ssd_problem *problem, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *h0, void *y, float *hT, void *workspace,
+                             size_t workspace_bytes, int stage, void *stream);
 ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
                              const float *A, const void *B, const void *C, const float *D,
                              const float *h0, void *y, float *hT, void *workspace,

@@ -73,6 +73,9 @@ def lib():
         L.ssd_forward.restype = st
         L.ssd_forward_timed.argtypes = L.ssd_forward.argtypes + [ctypes.POINTER(vp)]
         L.ssd_forward_timed.restype = st
+        L.ssd_forward_stage.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_size_t, ctypes.c_int, vp]
+        L.ssd_forward_stage.restype = st
         L.ssd_step.argtypes, L.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_plan.argtypes, L.ssd_plan.restype = [P, ctypes.POINTER(SsdLaunchPlan)], st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
@@ -243,9 +246,9 @@ def workspace_for(problem: SsdProblem, device) -> torch.Tensor:
     return torch.empty(n, device=device, dtype=torch.uint8)
 
 
-def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream):
-    """Checked ctypes arguments of ssd_forward, with the outputs and the workspace
-    (allocated here when not given)."""
+def _io_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final):
+    """Checked problem, inputs and outputs of a forward call (outputs allocated here
+    when not given)."""
     problem = problem_of(x, B, chunk)
     b, L, H, G, P, N, Q, nc = _dims(problem)
     io = _io_dtype(problem)
@@ -263,6 +266,13 @@ def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, st
         hT = torch.empty(b, H, P, N, device=dev, dtype=torch.float32)
     _dev(y, "y", io, (b, L, H, P), dev)
     _dev(hT, "hT", torch.float32, (b, H, P, N), dev)
+    return problem, dev, y, hT
+
+
+def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream):
+    """Checked ctypes arguments of ssd_forward, with the outputs and the workspace
+    (allocated here when not given)."""
+    problem, dev, y, hT = _io_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final)
     if workspace is None:
         workspace = workspace_for(problem, dev)
     if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
@@ -315,6 +325,13 @@ class ForwardPlan:
         if st != 0:
             _raise(st, "ssd_forward")
         return self.y, self.hT
+
+    def run_stage(self, stage: int):
+        """Launch one stage of the forward alone (ssd_forward_stage: 0 chunk cumsum, 1 state
+        pass, 2 group scan, 3 chunk output) on the plan's workspace, for timing one kernel."""
+        st = lib().ssd_forward_stage(*self._args[:-1], int(stage), self._args[-1])
+        if st != 0:
+            _raise(st, "ssd_forward_stage")
 
 
 def _step_args(x, dt, A, B, C, D, h, y, stream):

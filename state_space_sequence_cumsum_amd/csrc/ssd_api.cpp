@@ -200,16 +200,24 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
                                             (hipStream_t)stream));
 }
 
-ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
-                             const float *A, const void *B, const void *C, const float *D,
-                             const float *h0, void *y, float *hT, void *workspace,
-                             size_t workspace_bytes, void *stream, void *const *events)
+}  // extern "C"
+
+namespace {
+
+// Launches first..last (0 chunk cumsum, 1 state pass, 2 group scan, 3 chunk output) of
+// the forward on `stream`, with events[i] recorded right before launch i and
+// events[last + 1] after the last (events NULL: no marks).
+ssd_status forward_launches(const ssd_problem *problem, const void *x, const void *dt,
+                            const float *A, const void *B, const void *C, const float *D,
+                            const float *h0, void *y, float *hT, void *workspace,
+                            size_t workspace_bytes, void *stream, void *const *events, int first,
+                            int last)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
     if (events != nullptr)
-        for (int i = 0; i < SSD_FORWARD_EVENTS; ++i)
+        for (int i = first; i <= last + 1; ++i)
             if (!events[i]) return SSD_ERR_NULL_ARG;
     const ssd::Shape s = make_shape(problem);
     const Layout l = layout_of(s);
@@ -228,29 +236,59 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
     auto mark = [&](int i) -> ssd_status {
         return events ? hip_status(hipEventRecord((hipEvent_t)events[i], hs)) : SSD_OK;
     };
-
-    ssd_status r = mark(0);
-    if (r == SSD_OK) r = hip_status(ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs));
-    if (r == SSD_OK) r = mark(1);
-    if (r == SSD_OK)
-        r = hip_status(ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam,
-                                                      beta, hs));
-    if (r == SSD_OK) r = mark(2);
-    if (r == SSD_OK) r = hip_status(ssd::launch_group_scan(s, l.gp, hT, Ug, Hb, gam, hs));
-    if (r == SSD_OK) r = mark(3);
-    if (r == SSD_OK)
-        r = hip_status(
-            ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, Hb, beta, hs));
-    if (r == SSD_OK) r = mark(4);
+    auto launch = [&](int i) -> hipError_t {
+        switch (i) {
+        case 0: return ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs);
+        case 1:
+            return ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam, beta,
+                                                  hs);
+        case 2: return ssd::launch_group_scan(s, l.gp, hT, Ug, Hb, gam, hs);
+        default:
+            return ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, Hb,
+                                                   beta, hs);
+        }
+    };
+    ssd_status r = SSD_OK;
+    for (int i = first; i <= last && r == SSD_OK; ++i) {
+        r = mark(i);
+        if (r == SSD_OK) r = hip_status(launch(i));
+    }
+    if (r == SSD_OK) r = mark(last + 1);
     return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *h0, void *y, float *hT, void *workspace,
+                             size_t workspace_bytes, void *stream, void *const *events)
+{
+    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
+                            stream, events, 0, SSD_FORWARD_EVENTS - 2);
 }
 
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt, const float *A,
                        const void *B, const void *C, const float *D, const float *h0, void *y,
                        float *hT, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return ssd_forward_timed(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
-                             stream, nullptr);
+    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
+                            stream, nullptr, 0, SSD_FORWARD_EVENTS - 2);
+}
+
+ssd_status ssd_forward_stage(const ssd_problem *problem, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *h0, void *y, float *hT, void *workspace,
+                             size_t workspace_bytes, int stage, void *stream)
+{
+    if (stage < 0 || stage > SSD_FORWARD_EVENTS - 2) {
+        const ssd_status st = check_shape(problem);
+        return st != SSD_OK ? st : SSD_ERR_UNSUPPORTED;
+    }
+    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
+                            stream, nullptr, stage, stage);
 }
 
 ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, const float *A,

@@ -95,6 +95,21 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lib.ssd_last_hip_error() == 0
 
 
+def test_forward_stage_validates_before_launching():
+    lib = binding.lib()
+    p = _p()
+    fake = ctypes.c_void_p(256)
+    args = [fake] * 6 + [None, fake, None, fake]   # x dt A B C D h0 y hT workspace
+    for stage in (-1, 4):
+        assert lib.ssd_forward_stage(ctypes.byref(p), *args, 10**12, stage, None) == 3
+    assert lib.ssd_forward_stage(ctypes.byref(p), *args, 100, 3, None) == 4
+    no_y = [fake] * 6 + [None, None, None, fake]
+    assert lib.ssd_forward_stage(ctypes.byref(p), *no_y, 10**12, 0, None) == 1
+    bad = _p(nheads=6, ngroups=4)
+    assert lib.ssd_forward_stage(ctypes.byref(bad), *args, 10**12, 7, None) == 2
+    assert lib.ssd_last_hip_error() == 0
+
+
 def test_misaligned_pointers_are_rejected_without_launching():
     lib = binding.lib()
     p = _p()

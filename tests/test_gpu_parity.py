@@ -374,6 +374,31 @@ def test_forward_timed_events():
                         events=evs[:4])
 
 
+@pytest.mark.parametrize("w", [_wl("stages_grouped", "bf16", 1, 4096, 4, 64, 128, 1, 256),
+                               _wl("stages_ragged", "bf16", 2, 1000, 4, 64, 64, 2, 128),
+                               _wl("stages_fp32", "fp32", 1, 1024, 2, 64, 64, 1, 64)],
+                         ids=lambda w: w.name)
+def test_forward_stages_one_at_a_time(w):
+    """ssd_forward_stage 0, 1, 2, 3 in order reproduces ssd_forward bit for bit; repeating
+    stage 3 (and stage 0) on the filled workspace recomputes the same outputs."""
+    dev = require_gpu()
+    d = to_dev(make_inputs(w, 4), dev)
+    y_ref, h_ref = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                   chunk=w.chunk)
+    plan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk)
+    plan.y.fill_(float("nan"))
+    plan.hT.fill_(float("nan"))
+    for stage in range(4):
+        plan.run_stage(stage)
+    torch.cuda.synchronize()
+    assert torch.equal(plan.y, y_ref) and torch.equal(plan.hT, h_ref)
+    plan.y.fill_(float("nan"))
+    for stage in (3, 0, 3):
+        plan.run_stage(stage)
+    torch.cuda.synchronize()
+    assert torch.equal(plan.y, y_ref)
+
+
 def test_errors_before_launch():
     dev = require_gpu()
     w = _wl("err", "bf16", 1, 128, 2, 64, 64, 1, 64)
