@@ -35,7 +35,8 @@
  * Every call validates its arguments on the host before any launch and returns a
  * status; nothing is launched when it is not SSD_OK.  The library never allocates
  * memory, never synchronises and keeps no global mutable state apart from the
- * thread-local HIP error code.  Work is asynchronous on `stream`; buffers must stay
+ * thread-local HIP error code and the static scratch of ssd_forward_noalloc (a
+ * device array that the code object holds on each GPU, plus its per-device address).  Work is asynchronous on `stream`; buffers must stay
  * valid until it completes.  Inputs and outputs must not overlap, except that
  * h0 and hT may be the same buffer.  Since a call issues only kernel launches (no
  * allocation, memset, copy or synchronisation), ssd_forward, the three stages and
@@ -71,7 +72,9 @@ typedef enum {
     SSD_ERR_UNSUPPORTED = 3,  /* outside the supported dtype / headdim / dstate / chunk set */
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than ssd_workspace_bytes() */
     SSD_ERR_HIP = 5,          /* a HIP launch failed; see ssd_last_hip_error()        */
-    SSD_ERR_MISALIGNED = 6    /* a vector-accessed array does not start on 16 bytes  */
+    SSD_ERR_MISALIGNED = 6,   /* a vector-accessed array does not start on 16 bytes  */
+    SSD_ERR_SCRATCH = 7       /* ssd_forward_noalloc: the problem needs more than
+                                 SSD_SCRATCH_BYTES of workspace                         */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -162,6 +165,25 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
                              const float *A, const void *B, const void *C, const float *D,
                              const float *h0, void *y, float *hT, void *workspace,
                              size_t workspace_bytes, void *stream, void *const *events);
+
+/* ssd_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * and results as ssd_forward, with the workspace taken from a static device array of
+ * SSD_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends.  It calls no allocating routine; the caller still provides every input and
+ * output.  The array is the one of the stream's device (the current device for the
+ * NULL stream); its address is looked up on the first call for that device.
+ * Problems with ssd_workspace_bytes() > SSD_SCRATCH_BYTES return SSD_ERR_SCRATCH before
+ * any launch (128 MiB covers, e.g., b1 L16384 H32 P64 N256 Q256, which needs about
+ * 99 MB).  Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing: the forward writes every intermediate before
+ * reading it): calls that overlap on one GPU -- on two streams, or from two threads
+ * without ordering -- race and must not be issued.  Other arguments and errors as for
+ * ssd_forward. */
+#define SSD_SCRATCH_BYTES (128u << 20)
+ssd_status ssd_forward_noalloc(const ssd_problem *problem, const void *x, const void *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *h0, void *y, float *hT, void *stream);
 
 /* One decode step (the recurrence of section "Mamba-2 架构" applied to a single token
  * per sequence; section "Kernel 2: fwd_pass_state" notes that at inference the final

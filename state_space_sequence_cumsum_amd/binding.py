@@ -22,7 +22,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
 SSD_F32, SSD_BF16 = 0, 1
 FORWARD_EVENTS = 5      # SSD_FORWARD_EVENTS: marks around stage 1, state pass, group scan, stage 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED"}
+          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED", 7: "SSD_ERR_SCRATCH"}
+SCRATCH_BYTES = 128 << 20   # SSD_SCRATCH_BYTES: the static workspace of ssd_forward_noalloc
 
 
 class SsdError(RuntimeError):
@@ -76,6 +77,8 @@ def lib():
         L.ssd_forward_stage.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_size_t, ctypes.c_int, vp]
         L.ssd_forward_stage.restype = st
+        L.ssd_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ssd_forward_noalloc.restype = st
         L.ssd_step.argtypes, L.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_plan.argtypes, L.ssd_plan.restype = [P, ctypes.POINTER(SsdLaunchPlan)], st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
@@ -301,6 +304,19 @@ def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want
                              "recorded at least once")
         arr = (ctypes.c_void_p * FORWARD_EVENTS)(*[e.cuda_event for e in events])
         _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
+    return y, hT
+
+
+def ssd_forward_noalloc(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None,
+                        want_final=True, stream=None):
+    """ssd_forward with the library's static device scratch as the workspace: the C call
+    allocates nothing (pass y, and hT unless want_final is False, to keep this wrapper
+    from allocating them).  Returns (y, hT).  Raises SsdError with SSD_ERR_SCRATCH when
+    the problem needs more than SCRATCH_BYTES of workspace."""
+    problem, dev, y, hT = _io_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final)
+    _raise(lib().ssd_forward_noalloc(ctypes.byref(problem), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hT),
+                                     _stream(stream, dev)), "ssd_forward_noalloc")
     return y, hT
 
 

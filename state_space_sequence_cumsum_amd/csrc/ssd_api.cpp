@@ -122,6 +122,8 @@ ssd_status hip_status(hipError_t e)
 
 }  // namespace
 
+int ssd::hip_status(hipError_t e) { return ::hip_status(e); }
+
 extern "C" {
 
 ssd_status ssd_validate(const ssd_problem *problem) { return check_shape(problem); }
@@ -315,6 +317,9 @@ const char *ssd_status_string(ssd_status status)
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_HIP: return "HIP launch failed";
     case SSD_ERR_MISALIGNED: return "a vector-accessed array does not start on a 16-byte boundary";
+    case SSD_ERR_SCRATCH:
+        return "the problem needs more workspace than the static scratch of ssd_forward_noalloc "
+               "holds (SSD_SCRATCH_BYTES); use ssd_forward with a workspace";
     }
     return "unknown status";
 }

@@ -7,6 +7,10 @@
 
 namespace ssd {
 
+// SSD_OK for hipSuccess; otherwise SSD_ERR_HIP, with the code kept for
+// ssd_last_hip_error() on this thread (ssd_api.cpp).
+int hip_status(hipError_t e);
+
 struct Shape {
     int64_t b, L, H, G, P, N, Q, nc, Lp;
     bool bf16;

@@ -163,9 +163,31 @@ def test_step_validates_before_launching(kw, status):
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert ssd.ssd_status_string(s)
     assert "unknown" in ssd.ssd_status_string(42)
+
+
+def test_noalloc_scratch_limit_checked_before_launching():
+    """ssd_forward_noalloc refuses shapes whose workspace exceeds its static scratch, and bad
+    shapes, on the host (no pointer is touched, no GPU is needed)."""
+    lib = binding.lib()
+    text = open(binding.HEADER).read()
+    assert "#define SSD_SCRATCH_BYTES (128u << 20)" in text
+    assert binding.SCRATCH_BYTES == 128 << 20
+    fake = ctypes.c_void_p(4096)
+    big = _p(seqlen=65536, dstate=512, chunk=128)
+    assert ssd.ssd_workspace_bytes(big) > binding.SCRATCH_BYTES
+    assert lib.ssd_forward_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None,
+                                   fake, None, None) == 7
+    bad = _p(nheads=6, ngroups=4)
+    assert lib.ssd_forward_noalloc(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None,
+                                   fake, None, None) == 2
+    assert lib.ssd_forward_noalloc(None, fake, fake, fake, fake, fake, fake, None, fake, None,
+                                   None) == 1
+    # the headline forward fits
+    assert 0 < ssd.ssd_workspace_bytes(_p(seqlen=16384, dstate=256, chunk=256)) <= binding.SCRATCH_BYTES
+    assert lib.ssd_last_hip_error() == 0
 
 
 def test_binding_refuses_host_tensors():
