@@ -205,7 +205,7 @@ ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, c
                     void *stream);
 
 /* How ssd_forward launches `problem` on this GPU: the per-shape choices of the state pass
- * (chunks per group, groups, state columns per workgroup) and of the chunk output (the
+ * (kernel, chunks per group, groups, state columns per workgroup) and of the chunk output (the
  * head-blocked kernel or the one-head kernel, heads per workgroup, column halves split over
  * wave pairs), with the workgroup counts.  Host-only; for reports and tuning. */
 typedef struct {
@@ -219,6 +219,9 @@ typedef struct {
     int32_t co_column_split;    /* 2: state columns split over wave pairs (N = 512) */
     int32_t co_workgroups;      /* chunk-output workgroups (ragged last chunk included) */
     int32_t co_threads;         /* threads per head-blocked (else one-head) workgroup */
+    int32_t sp_register_transposed; /* 1: the state pass transposes B in registers (N >= 512),
+                                       0: through LDS */
+    int32_t sp_threads;         /* threads per state-pass workgroup */
 } ssd_launch_plan;
 
 ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan);

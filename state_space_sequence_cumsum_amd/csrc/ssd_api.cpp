@@ -164,6 +164,8 @@ ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan)
     plan->co_column_split = lp.co_column_split;
     plan->co_workgroups = lp.co_workgroups;
     plan->co_threads = lp.co_threads;
+    plan->sp_register_transposed = lp.sp_register_transposed;
+    plan->sp_threads = lp.sp_threads;
     return SSD_OK;
 }
 

@@ -446,6 +446,265 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
 }
 
 // ===========================================================================
+// State pass, register-transposed operands.  Workgroup = one (batch*head, range
+// of NR state columns, group of up to K consecutive chunks), NR/64 waves; wave w
+// keeps h[p][n] for all 64 p and its 64 columns n0 + 64 w .. + 64 in four fp32
+// MFMA accumulators (v_mfma_f32_32x32x16_bf16, row = p, column = n).
+//
+// The jump h <- a_c h + sum_t w_t x_t (outer) B_t contracts over tokens, the
+// strided dimension of both inputs, and an MFMA operand lane holds 8 consecutive
+// values of the contraction index.  So:
+//   * B (the N-wide operand, read once per workgroup): every lane loads its own
+//     two columns for 8 tokens as 4-byte words (lanes 0-31 tokens 0-7, lanes 32-63
+//     tokens 8-15 of a 16-token step; one 128-byte row segment per 32 lanes) and
+//     byte-permutes them into two k-packed operands, columns 2l and 2l + 1 of the
+//     wave's range.  B never goes through LDS.
+//   * x~ = round_bf16(w_t x_t) (64 wide, shared by all waves): each thread loads 8
+//     tokens x 2 columns of x, scales them by the tokens' weights and writes the two
+//     k-packed rows straight into a double-buffered LDS tile, which the waves read
+//     with 16-byte reads.  One barrier per 64-token sub-step.
+// The chunk-start state goes to HBM straight from the accumulators: lane l holds
+// columns 2l and 2l + 1 of a row, so a 4-byte store per lane writes 128 contiguous
+// bytes per 32 lanes.  Loads run D sub-steps ahead in a register ring; rows past
+// L are clamped to row L-1 (their weight is 0) and indices past the group's end
+// to its last sub-step, so the loop has no branches around memory operations.
+// Groups and the decay products for the group scan as in the kernel above.
+// ===========================================================================
+template <int Q, int NR, int D>
+__global__ __launch_bounds__(NR) void state_pass_rt_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
+    const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
+    float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
+    float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng, int xcd)
+{
+    constexpr int P = 64, TS = 64, NSUB = Q / TS, NTHR = NR, KS = TS / 16;
+    constexpr int XPT = 256 / NTHR;   // x pieces (8 tokens x 2 columns) per thread per sub-step
+    constexpr int XKP = 72;           // k-packed x~ row pitch: 144 bytes (16 more than 128)
+    static_assert(NR % 64 == 0 && NR <= 256 && Q % TS == 0, "state-pass tiling");
+    __shared__ __attribute__((aligned(16))) bf16 Xk[2][P * XKP];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    int grp, minor;
+    xcd_split(blockIdx.x, (int)(gridDim.x / ng), xcd != 0, grp, minor);
+    const int ntiles = N / NR, bh = minor / ntiles, n0 = (minor % ntiles) * NR;
+    const int c0 = grp * K, c1 = min(c0 + K, nc);
+    const int U = (c1 - c0) * NSUB;                               // sub-steps of this group
+    const int b = bh / H, h = bh % H, g = h / (H / G);
+    const int64_t st_off = (int64_t)bh * P * N;
+    const float *Gh = G2 + (int64_t)bh * Lp;
+    const float *wh = wT + (int64_t)bh * Lp;
+    const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
+    // x and B are read through buffer resources based at the first row of each tile and
+    // ending at row L, so rows past the sequence read as zero (their weight is 0 too);
+    // per-lane offsets are 32-bit (the host checks that one batch of x and of B spans
+    // less than 2^31 bytes)
+    const char *xbytes = reinterpret_cast<const char *>(x + (int64_t)b * L * xstride + (int64_t)h * P);
+    const char *Bbytes = reinterpret_cast<const char *>(Bm + (int64_t)b * L * bstride + (int64_t)g * N +
+                                                        n0 + 64 * wave);
+    const int xrow = (int)xstride * 2, brow = (int)bstride * 2;
+    const int ncol = n0 + 64 * wave + 2 * l32;                   // this lane's two columns
+    // the chunk-end cumsum value of chunk c0 + lane (clamped to the group), for the decay
+    // products written at the end; a per-lane load issued now, hidden by the chunk loop
+    float gend0;
+    {
+        int gi = min(c0 + lane, c1 - 1) * Q + Q - 1;
+        asm volatile("" : "+v"(gi));
+        gend0 = G2[(int64_t)bh * Lp + gi];
+    }
+
+    // acc[pt][e] element v: p = 32 pt + acc_row(v, lane), n = ncol + e
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) acc[pt][e] = zero_acc();
+    if (h0 != nullptr && grp == 0) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int p = 32 * pt + acc_row(v, lane);
+                const f32x2 hv = *reinterpret_cast<const f32x2 *>(h0 + st_off + (int64_t)p * N + ncol);
+                acc[pt][0][v] = hv[0];
+                acc[pt][1][v] = hv[1];
+            }
+    }
+
+    // x piece r of a sub-step: columns 2 pp, 2 pp + 1 of tokens 8 to .. 8 to + 7, read at
+    // byte offsets xoff[r] + k * xrow from the sub-step's first row; B word k of a 16-token
+    // step at boffk + k * brow from that step's first row
+    int ppv[XPT], tov[XPT];
+    uint32_t xoff[XPT];
+#pragma unroll
+    for (int r = 0; r < XPT; ++r) {
+        const int id = tid + NTHR * r;
+        ppv[r] = id & 31;
+        tov[r] = id >> 5;
+        xoff[r] = (uint32_t)(8 * tov[r] * xrow + 4 * ppv[r]);
+    }
+    const uint32_t boff = (uint32_t)(8 * half * brow + 4 * l32);
+    struct Regs {
+        uint32_t b[KS][8];      // B words of k-step ks: token 16 ks + 8 half + k, columns ncol, ncol + 1
+        uint32_t xv[XPT][8];    // x words of piece r: token 8 to + k, columns 2 pp, 2 pp + 1
+        f32x4 w[XPT][2];        // the weights of those 8 tokens
+        float gl;               // cumsum value at the end of the sub-step's chunk
+    };
+    auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
+    // x, weights and the chunk-end value first (used a step earlier), then B
+    auto load = [&](Regs &R, int u) {
+        u = min(u, U - 1);
+        const int t0 = tok0(u);
+        int gi = (c0 + u / NSUB) * Q + Q - 1;
+        asm volatile("" : "+v"(gi));   // per-lane load: a scalar one would share the LDS wait counter
+        R.gl = Gh[gi];
+        const rsrc_t xr = make_rsrc(xbytes + (int64_t)t0 * xrow, (L - t0) * xrow);
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            const float *wb = wh + t0 + 8 * tov[r];
+            R.w[r][0] = *reinterpret_cast<const f32x4 *>(wb);
+            R.w[r][1] = *reinterpret_cast<const f32x4 *>(wb + 4);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) R.xv[r][k] = buf_load_b32(xr, xoff[r] + k * xrow);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keeps this issue order
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int tk = t0 + 16 * ks;
+            const rsrc_t br = make_rsrc(Bbytes + (int64_t)tk * brow, (L - tk) * brow);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) R.b[ks][k] = buf_load_b32(br, boff + k * brow);
+        }
+    };
+    // k-packed x~ row p at 16-byte unit u is stored at unit u ^ ((p >> 4) & 1): with the
+    // 144-byte pitch both the staging writes (16 rows of one parity) and the operand reads
+    // (16 consecutive rows) touch 16 distinct 16-byte bank groups
+    auto xk_off = [](int p, int u) { return p * XKP + 8 * (u ^ ((p >> 4) & 1)); };
+    auto stageX = [&](const Regs &R, int kb) {
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            u32x4 f0, f1;
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const float w0 = R.w[r][k2 >> 1][2 * (k2 & 1)], w1 = R.w[r][k2 >> 1][2 * (k2 & 1) + 1];
+                const uint32_t a = R.xv[r][2 * k2], c = R.xv[r][2 * k2 + 1];
+                f0[k2] = pack_bf16(bf_lo(a) * w0, bf_lo(c) * w1);
+                f1[k2] = pack_bf16(bf_hi(a) * w0, bf_hi(c) * w1);
+            }
+            const int p = 2 * ppv[r];
+            *reinterpret_cast<u32x4 *>(&Xk[kb][xk_off(p, tov[r])]) = f0;
+            *reinterpret_cast<u32x4 *>(&Xk[kb][xk_off(p + 1, tov[r])]) = f1;
+        }
+    };
+    auto mma_sub = [&](const Regs &R, int kb) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 bf[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                u32x4 q;
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) q[k2] = pack_halves(R.b[ks][2 * k2], R.b[ks][2 * k2 + 1], e);
+                bf[e] = __builtin_bit_cast(bf16x8, q);
+            }
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const bf16x8 af = ld16(&Xk[kb][xk_off(32 * pt + l32, 2 * ks + half)]);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) mma(acc[pt][e], af, bf[e]);
+            }
+        }
+    };
+    // chunk start: the state goes to S[c] (bf16, straight from the accumulators), then decays
+    const uint32_t srow_off = (uint32_t)((4 * half * N + ncol) * 2);   // lane part of the S offsets
+    auto chunk_start = [&](float gl, int c) {
+        char *Sc = reinterpret_cast<char *>(S + ((int64_t)bh * nc + c) * P * N);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int prow = 32 * pt + 8 * (v >> 2) + (v & 3);   // acc_row without the lane part
+                *reinterpret_cast<uint32_t *>(Sc + (int64_t)prow * N * 2 + srow_off) =
+                    pack_bf16(acc[pt][0][v], acc[pt][1][v]);
+            }
+        const float a = fast_exp2(gl);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[pt][e][v] *= a;
+    };
+
+    // Register ring of D sub-steps: slot u % D holds sub-step u from its load (step u - D)
+    // until its B operands are used (step u); its x~ is staged one step earlier.
+    static_assert(D >= 2, "a slot holds one sub-step from the x~ staging to its products");
+    Regs R[D];
+    auto step = [&](int s, int j) {
+        if (j % NSUB == 0) chunk_start(R[j % D].gl, c0 + s / NSUB);
+        mma_sub(R[j % D], j & 1);
+        stageX(R[(j + 1) % D], (j + 1) & 1);
+        load(R[j % D], s + D);
+        __syncthreads();
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(R[u], u);
+    stageX(R[0], 0);
+    __syncthreads();
+    // the body covers UNR = lcm(NSUB, D, 2) sub-steps so that ring slots, LDS buffers and
+    // chunk-start positions are compile-time constants
+    constexpr int UNR = lcm3(NSUB, D, 2);
+    int s = 0;
+    for (; s + UNR <= U; s += UNR) {
+#pragma unroll
+        for (int j = 0; j < UNR; ++j) step(s + j, j);
+    }
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+        if (s + j < U) step(s + j, j);
+
+    // decay products of the group (beta_c before each chunk, gamma for the group), as in
+    // the kernel above
+    if (n0 == 0 && wave == 0 && (beta != nullptr || gam != nullptr)) {
+        float run = 1.0f;
+        auto products = [&](float gv, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
+            const float e = fast_exp2(gv);
+            const int cnt = min(64, c1 - c0 - k0);
+            float mine = 0.0f;
+            for (int k = 0; k < cnt; ++k) {
+                if (lane == k) mine = run;
+                run *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), k));
+            }
+            if (beta != nullptr && lane < cnt) beta[(int64_t)bh * nc + c0 + k0 + lane] = mine;
+        };
+        products(gend0, 0);
+        for (int k0 = 64; k0 < c1 - c0; k0 += 64) {   // groups of more than 64 chunks
+            int gi = min(c0 + k0 + lane, c1 - 1) * Q + Q - 1;
+            asm volatile("" : "+v"(gi));
+            products(Gh[gi], k0);
+        }
+        if (gam != nullptr && lane == 0) gam[(int64_t)bh * ng + grp] = run;
+    }
+
+    // the state after the group's last chunk (fp32): 8 bytes per lane, 256 contiguous bytes
+    // per 32 lanes
+    float *dst = (Ug != nullptr) ? Ug + ((int64_t)bh * ng + grp) * P * N : (hT ? hT + st_off : nullptr);
+    if (dst != nullptr) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int p = 32 * pt + acc_row(v, lane);
+                f32x2 o;
+                o[0] = acc[pt][0][v];
+                o[1] = acc[pt][1][v];
+                *reinterpret_cast<f32x2 *>(dst + (int64_t)p * N + ncol) = o;
+            }
+    }
+}
+
+// ===========================================================================
 // Group scan.  For each (batch*head, state element): walk the groups in order,
 // H_1 = U_0 and H_{g+1} = gamma_g H_g + U_g; H_g (the true state at group g's
 // start) replaces U_g in place for the groups g >= g_f32 (the chunk outputs that
@@ -1275,6 +1534,17 @@ static bool head_blocked(const Shape &s)
 
 // register ring depth of the state pass (sub-steps in flight)
 constexpr int kSpDepth = 2;
+constexpr int kSpRtDepth = 2;
+
+// Which state pass runs: the register-transposed kernel for N a multiple of 256 from
+// 512 up (256-column workgroups of 4 waves, two per CU), the LDS-transposed kernel
+// otherwise.  Measured on MI355X (bf16, one box, µs per state pass): b1 L65536 H32 N512
+// Q128 486 -> 433; at N = 256 (b1 L16384 H32 Q256) 38.7 -> 37.5 with one workgroup per
+// CU and 35.0 with two (then 16 groups, whose scan costs 4 µs more); at N = 128
+// 28.8 -> 30.3-38.0 (b4 L16384 H8 Q128) and 9.9 -> 10.3-11.5 (b2 L2048 H24 Q256).
+// Its 4-byte loads (two columns per lane for the in-register transpose) take four
+// times the address-unit issue of 16-byte loads per byte.
+static bool sp_register_transposed(const Shape &s) { return s.N >= 512 && s.N % 256 == 0; }
 
 template <int Q, int NR>
 static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
@@ -1283,6 +1553,15 @@ static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const 
 {
     const int units = (int)(s.b * s.H * (s.N / NR));
     const int xcd = (ng % 8 == 0) ? 1 : 0;
+    if constexpr (NR == 256) {
+        if (sp_register_transposed(s)) {
+            hipLaunchKernelGGL((state_pass_rt_kernel<Q, 256, kSpRtDepth>), dim3((unsigned)(units * ng)),
+                               dim3(256), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT, h0,
+                               (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
+                               (int)s.nc, (int)s.Lp, K, ng, xcd);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NR, kSpDepth>), dim3((unsigned)(units * ng)),
                        dim3(SpCfg<Q, NR>::NTHR), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT,
                        h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
@@ -1338,15 +1617,15 @@ Grouping state_pass_groups(const Shape &s)
         gp.ng = (int)((s.nc + K - 1) / K);
         return gp;
     }
-    // bf16: a workgroup takes most of a CU's LDS (two fit at 64 columns), so `slots`
-    // run at once and units * ng workgroups take ceil(units * ng / slots) rounds of K
-    // chunks each.  The count minimises that makespan plus a fixed cost per
+    // bf16: an LDS-transposed workgroup takes most of a CU's LDS (two fit at 64 columns),
+    // a register-transposed one half of a CU's registers, so `slots` run at once and
+    // units * ng workgroups take ceil(units * ng / slots) rounds of K chunks each.  The count minimises that makespan plus a fixed cost per
     // workgroup (~0.6 chunk: prologue, last state store) and the group scan, in
     // units of one chunk's time (~1.2 us per 64 tokens); ties keep fewer groups.
     // The scan reads and writes every group's state (~6 bytes per element at
     // ~5 TB/s) and walks the groups in order, eight loads in flight (~1.5 us per
     // eight groups): whichever is longer.
-    const int64_t slots = 256 * (sp_cols(s) == 64 ? 2 : 1);
+    const int64_t slots = (sp_register_transposed(s) || sp_cols(s) == 64) ? 512 : 256;
     const double tchunk = (double)s.Q / 64 * 1.2e-6;
     const int64_t ng_max = std::min<int64_t>(s.nc, 8 * slots / units + 1);
     double best = 1e300;
@@ -1460,6 +1739,8 @@ LaunchPlan plan_of(const Shape &s)
     if (!s.bf16) {   // fp32 kernels: 64 columns per state-pass workgroup, one (chunk, head) per output workgroup
         lp.sp_columns = 64;
         lp.sp_workgroups = (int)(s.b * s.H * (s.N / 64) * gp.ng);
+        lp.sp_register_transposed = 0;
+        lp.sp_threads = 256;
         lp.scan = gp.ng > 1 ? 1 : 0;
         lp.co_head_blocked = 0;
         lp.co_heads_per_block = 1;
@@ -1470,6 +1751,8 @@ LaunchPlan plan_of(const Shape &s)
     }
     lp.sp_columns = sp_cols(s);
     lp.sp_workgroups = (int)(s.b * s.H * (s.N / lp.sp_columns) * gp.ng);
+    lp.sp_register_transposed = sp_register_transposed(s) ? 1 : 0;
+    lp.sp_threads = lp.sp_register_transposed ? 256 : (lp.sp_columns == 64 ? 256 : 512);
     lp.scan = gp.ng > 1 ? 1 : 0;
     lp.co_head_blocked = head_blocked(s) ? 1 : 0;
     if (lp.co_head_blocked) {

@@ -13,6 +13,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -96,6 +97,26 @@ __device__ __forceinline__ f32x16 zero_acc()
 #pragma unroll
     for (int v = 0; v < 16; ++v) a[v] = 0.0f;
     return a;
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads (MUBUF).  A resource covers `bytes` bytes from `base`; a load at
+// a per-lane byte offset at or past the end returns zero (the hardware range check
+// of a raw buffer, which sees the per-lane offset), so a tile that runs past the end
+// of a sequence needs no clamping.  Word 3 is the gfx9 buffer configuration (32-bit
+// data format, no swizzle).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes < 0 ? 0 : bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -71,6 +71,7 @@ int chunk_out_f32_threads(const Shape &s);
 struct LaunchPlan {
     int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
     int co_head_blocked, co_heads_per_block, co_column_split, co_workgroups, co_threads;
+    int sp_register_transposed, sp_threads;
 };
 LaunchPlan plan_of(const Shape &s);
 

@@ -213,12 +213,17 @@ def test_launch_plan_per_shape():
     assert ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256)) == dict(
         sp_group_chunks=8, sp_groups=8, sp_columns=256, sp_workgroups=256, scan=1,
         co_head_blocked=1, co_heads_per_block=8, co_column_split=1, co_workgroups=256,
-        co_threads=512)
-    # N = 512 with 128-token chunks: two 256-column state-pass workgroups per chain, the
-    # chunk output's columns split over wave pairs
+        co_threads=512, sp_register_transposed=0, sp_threads=512)
+    # N = 512 with 128-token chunks: the register-transposed state pass, two 256-column
+    # workgroups of 4 waves per chain and two per CU (8 groups of 64 chunks), the chunk
+    # output's columns split over wave pairs
     p512 = ssd.ssd_plan(_p(seqlen=65536, dstate=512, chunk=128))
-    assert (p512["sp_columns"], p512["sp_groups"], p512["co_column_split"], p512["co_threads"]) == (256, 4, 2, 512)
-    assert p512["sp_workgroups"] == 32 * 2 * 4 and p512["co_workgroups"] == 512 * (32 // p512["co_heads_per_block"])
+    assert (p512["sp_columns"], p512["sp_groups"], p512["co_column_split"], p512["co_threads"]) == (256, 8, 2, 512)
+    assert (p512["sp_register_transposed"], p512["sp_threads"]) == (1, 256)
+    assert p512["sp_workgroups"] == 32 * 2 * 8 and p512["co_workgroups"] == 512 * (32 // p512["co_heads_per_block"])
+    # below 512 state columns the LDS-transposed state pass
+    for n in (64, 128, 256, 384, 448):
+        assert ssd.ssd_plan(_p(dstate=n, chunk=128))["sp_register_transposed"] == 0
     # ragged: 23 full chunks head-blocked (one head per block here) plus the last chunk of
     # each (batch, head) on the one-head kernel
     pr = ssd.ssd_plan(_p(seqlen=3000, nheads=2, dstate=128, chunk=128))

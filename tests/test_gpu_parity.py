@@ -128,6 +128,10 @@ SMALL_CASES = [
     _wl("bf16_hb2_n512", "bf16", 1, 8192, 8, 64, 512, 1, 128),       # 2 heads per block
     # corners of the supported set on the single-head chunk output
     _wl("bf16_q64_n512", "bf16", 1, 300, 2, 64, 512, 1, 64),
+    # the register-transposed state pass (N = 512): one sub-step per chunk over many groups,
+    # and a sequence shorter than one sub-step
+    _wl("bf16_rt_q64_groups", "bf16", 1, 2050, 2, 64, 512, 1, 64),
+    _wl("bf16_rt_short", "bf16", 2, 45, 2, 64, 512, 2, 256),
     _wl("bf16_q256_n512", "bf16", 1, 600, 2, 64, 512, 2, 256, shift=-3.0),
     _wl("bf16_q128_n448", "bf16", 2, 500, 3, 64, 448, 1, 128),
     _wl("bf16_q256_n384", "bf16", 1, 700, 4, 64, 384, 4, 256, h0=False),
@@ -150,7 +154,7 @@ SINGLE_GROUP_CASES = [
     _wl("sg_hb_n64_q128", "bf16", 2, 320, 128, 64, 64, 1, 128),            # 4 heads per block, ragged
     _wl("sg_hb_n256_q256", "bf16", 1, 640, 128, 64, 256, 1, 256, h0=False),
     _wl("sg_hb_n256_q128", "bf16", 1, 320, 96, 64, 256, 2, 128),
-    _wl("sg_hb_n512_q128", "bf16", 1, 320, 48, 64, 512, 1, 128),          # column halves
+    _wl("sg_hb_n512_q128", "bf16", 1, 256, 256, 64, 512, 1, 128),         # column halves
     _wl("sg_onehead_q64", "bf16", 1, 160, 96, 64, 128, 3, 64),
     _wl("sg_fp32_q256", "fp32", 1, 640, 64, 64, 256, 1, 256),
     _wl("sg_fp32_q128", "fp32", 1, 320, 128, 64, 256, 2, 128, h0=False),
