@@ -14,6 +14,7 @@
 // staging it, so that the many later reads of that tile are plain 16-byte reads.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -55,25 +56,26 @@ __device__ __forceinline__ void xcd_split(int id, int n_minor, bool xcd, int &ma
 // the x side: the contraction operand is x~ = round_bf16(w_t x_t), 64 wide, so
 // the N-wide B tile is used exactly as loaded.
 //
-// Each chunk is processed in sub-steps of TS tokens.  Step s of the loop:
-//   * copies B of sub-step s+1 into LDS token-major (16-byte rows) and x~ of
-//     sub-step s+2 (scaled on the way), both from registers loaded D sub-steps
-//     earlier, then reloads the freed registers;
-//   * k-packs x~ of s+1, Xk[p][t], by transpose-reading its token-major tile
-//     (4 consecutive tokens of one p per lane) and writing 8 bytes;
-//   * at a chunk start, writes the chunk-start state (bf16) into an LDS tile,
-//     which the next step stores to HBM as whole 16-byte-per-lane rows, and
-//     decays the state;
-//   * MFMA over sub-step s: A = B^T rows n, transpose-read from the token-major
-//     B tile (each B element is read once), B operand = Xk rows p (16-byte
-//     reads; every wave reads all of x~, the cheap operand);
-//   * one barrier.
-// Every LDS buffer is written one step before it is read and rewritten only
-// after the barrier that follows its last read, so two copies of each suffice.
-// Indices past the group's last sub-step are clamped (the extra copies are
-// never read) and rows past L are clamped to row L-1 (their weight is 0), so
-// the loop body has no branches around memory operations and the wait counts
-// leave later sub-steps in flight.
+// Both inputs are token-major and the MFMA operands hold 8 consecutive tokens per
+// lane.  Each chunk is processed in sub-steps of TS = 64 tokens:
+//   * B reaches LDS by 16-byte global->LDS loads (each lane of a load instruction
+//     writes its 16 bytes at base + 16 lane, so a wave fills 1 KB of consecutive
+//     rows), two sub-steps ahead into three unpadded buffers.  Unit u of row r is
+//     stored at unit u ^ swz(r), chosen on the global-address side, so that the
+//     operand's transpose reads (ds_read_b64_tr_b16, 4 rows x 64 bytes per 32
+//     lanes) touch 16 distinct bank groups.  No registers, no LDS writes by the
+//     waves, no wait before a copy.
+//   * x~: each thread loads its tokens of two columns of x as 4-byte words
+//     (buffer loads; rows past L read as zero), scales them by the tokens' weights
+//     and writes the two k-packed rows straight into a double-buffered LDS tile,
+//     which the waves read with 16-byte reads.
+//   * at a chunk start the state goes to an LDS staging tile (bf16), which is
+//     stored to HBM as whole 16-byte-per-lane rows, and then decays.
+// One barrier per sub-step; each waits (vmcnt) only for the B tile used next, the
+// count of memory instructions issued after it being a compile-time constant of the
+// unrolled step.  Rows past L are clamped out of the loads (zeros) and indices past
+// the group's end to its last sub-step, so the loop has no branches around memory
+// operations.
 //
 // Groups.  The jump is linear, so a run of chunks can start from a zero state
 // and be corrected afterwards: group g (chunks [gK, gK+K)) starts from h0 if
@@ -91,17 +93,6 @@ constexpr int lcm3(int a, int b, int c)
     return ab / gcd_(ab, c) * c;
 }
 
-// Row pitch (elements) of the token-major B tile: a multiple of 32 bytes that is
-// 64 or 192 mod 256, so the four rows one 32-lane pass of the MFMA operand's
-// transpose read touches (32 bytes each, at two column offsets 32 bytes apart)
-// fall on distinct banks.
-constexpr int b_pitch(int cols)
-{
-    int b = (cols * 2 + 31) / 32 * 32;
-    while ((b % 256) != 64 && (b % 256) != 192) b += 32;
-    return b / 2;
-}
-
 template <int Q, int N>   // N = NR, the columns of one workgroup
 struct SpCfg {
     static constexpr int P = 64;
@@ -111,43 +102,54 @@ struct SpCfg {
     static constexpr int NTHR = 64 * NWAVE;
     static constexpr int RTW = 1;                                // n tiles per wave
     static constexpr int CTW = (N == 256) ? 2 : 1;               // p tiles per wave
-    static constexpr int BP = b_pitch(N);                        // token-major B rows
-    static constexpr int XRP = tr_pitch(P);                      // token-major x rows
-    static constexpr int XKP = TS + 8;                           // k-packed x~ rows
     static constexpr int SSP = N + 8;                            // chunk-start state staging rows
     static constexpr int SPT = P * N / 8 / NTHR;                 // 16-byte state pieces per thread
-    static constexpr int BPT = TS * N / 8 / NTHR;                // 16-byte B pieces per thread
-    static constexpr int XPIECES = TS * P / 8;                   // 16-byte x pieces per sub-step
-    static constexpr int XPT = (XPIECES + NTHR - 1) / NTHR;      // per thread (last may idle)
-    static constexpr int TRG = TS * P / (4 * 16);                // 16-lane transpose reads per sub-step
-    static constexpr int TRL = TRG / (4 * NWAVE);                // ... per lane
-    static_assert(BPT >= 1 && TS * N / 8 % NTHR == 0, "B staging cover");
-    static_assert(TRL >= 1 && TRG % (4 * NWAVE) == 0, "x~ build cover");
     static_assert((N / 32 / RTW) * (2 / CTW) == NWAVE, "wave tiling");
     static_assert(Q % TS == 0, "sub-steps per chunk");
 };
 
-template <int Q, int NR, int D>
-__global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
+// s_waitcnt immediate with vmcnt = n and expcnt, lgkmcnt at their maxima (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// f(std::integral_constant<int, i>) for i = 0 .. n - 1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int Q, int NR>
+__global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
     const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
     float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
     float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng, int xcd)
 {
-    using C = SpCfg<Q, NR>;
-    constexpr int P = C::P, TS = C::TS, NSUB = C::NSUB, NTHR = C::NTHR, RTW = C::RTW,
-                  CTW = C::CTW, BP = C::BP, XRP = C::XRP, XKP = C::XKP, BPT = C::BPT,
-                  XPT = C::XPT, XPIECES = C::XPIECES, TRL = C::TRL;
-    constexpr int SSP = C::SSP, SPT = C::SPT;
-    __shared__ __attribute__((aligned(16))) bf16 Bs[2][TS * BP];
-    __shared__ __attribute__((aligned(16))) bf16 Xr[2][TS * XRP];
+    using Cf = SpCfg<Q, NR>;
+    constexpr int P = 64, TS = 64, NSUB = Q / TS, NTHR = Cf::NTHR, NWAVE = Cf::NWAVE;
+    constexpr int RTW = Cf::RTW, CTW = Cf::CTW, SSP = Cf::SSP, SPT = Cf::SPT;
+    constexpr int XKP = 72;                 // k-packed x~ row pitch: 144 bytes
+    constexpr int UPR = NR / 8;             // 16-byte units per B row
+    constexpr int RPI = 64 / UPR;           // B rows per DMA instruction (one wave, 1 KB)
+    constexpr int IPW = TS / RPI / NWAVE;   // DMA instructions per wave per sub-step
+    constexpr int TPP = 2048 / NTHR;        // tokens per x piece (two columns)
+    static_assert(IPW >= 1 && TS % (RPI * NWAVE) == 0, "B DMA cover");
+    static_assert(TPP == 4 || TPP == 8, "x piece");
+    __shared__ __attribute__((aligned(16))) bf16 Bs0[TS * NR];
+    __shared__ __attribute__((aligned(16))) bf16 Bs1[TS * NR];
+    __shared__ __attribute__((aligned(16))) bf16 Bs2[TS * NR];
     __shared__ __attribute__((aligned(16))) bf16 Xk[2][P * XKP];
     __shared__ __attribute__((aligned(16))) bf16 Ss[P * SSP];
-    __shared__ float Al[4];
+    auto bsel = [&](int k) -> bf16 * { return k == 0 ? Bs0 : (k == 1 ? Bs1 : Bs2); };
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // workgroup -> (group, batch*head, column range); with `xcd` all heads of one
-    // group share an XCD, so the group's B tiles are fetched into one L2
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int grp, minor;
     xcd_split(blockIdx.x, (int)(gridDim.x / ng), xcd != 0, grp, minor);
     const int ntiles = N / NR, bh = minor / ntiles, n0 = (minor % ntiles) * NR;
@@ -159,11 +161,9 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
     const float *Gh = G2 + (int64_t)bh * Lp;
     const float *wh = wT + (int64_t)bh * Lp;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
-    const bf16 *xb = x + (int64_t)b * L * xstride + (int64_t)h * P;
-    const bf16 *Bb = Bm + (int64_t)b * L * bstride + (int64_t)g * N + n0;
-    // the chunk-end cumsum value of chunk c0 + lane (clamped to the group), for the decay
-    // products written at the end; loaded now, as a per-lane load in every wave (no branch
-    // around it), so that its latency hides behind the chunk loop
+    const char *xbytes = reinterpret_cast<const char *>(x + (int64_t)b * L * xstride + (int64_t)h * P);
+    const char *Bbytes = reinterpret_cast<const char *>(Bm + (int64_t)b * L * bstride + (int64_t)g * N + n0);
+    const int xrow = (int)xstride * 2, brow = (int)bstride * 2;
     float gend0;
     {
         int gi = min(c0 + lane, c1 - 1) * Q + Q - 1;
@@ -171,8 +171,6 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
         gend0 = G2[(int64_t)bh * Lp + gi];
     }
 
-    // accumulator element v of tile (i, j): row n = 32 (rt0 + i) + acc_row(v, lane),
-    // column p = 32 (ct0 + j) + lane % 32
     f32x16 acc[RTW][CTW];
 #pragma unroll
     for (int i = 0; i < RTW; ++i)
@@ -193,116 +191,78 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
             }
     }
 
-    // ---- staging: sub-step u covers tokens t0(u) .. t0(u) + TS of chunk c0 + u / NSUB.
-    // Rows past L are clamped to row L-1 instead of zeroed: their weight w is 0 (stage
-    // 1 writes zeros there), so their x~ rows are 0 and they add nothing.  Every
-    // load is issued unconditionally, which keeps the loop body free of branches
-    // around memory operations and lets the wait counts leave later sub-steps in
-    // flight.
-    // Global offsets are 32-bit byte offsets from the batch's base pointer (the
-    // host checks that one batch of x and of B spans less than 2^31 bytes), so
-    // the loads use a scalar base plus one vector register.
-    int bo[BPT], blo[BPT], bt_[BPT], xo[XPT], xlo[XPT], xt_[XPT];
+    // B tile unit swizzle: XOR of bits 2-3 of the unit index with the row, so the four
+    // rows of a 32-lane transpose read land in four different 64-byte bank ranges
+    auto swz = [](int r) { return (NR >= 128) ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+    // DMA instruction k of this wave covers rows R0 .. R0 + RPI - 1; lane: row R0 + lane / UPR,
+    // physical unit lane % UPR, which holds logical unit (lane % UPR) ^ swz(row)
+    uint32_t bdoff[IPW];
 #pragma unroll
-    for (int r = 0; r < BPT; ++r) {
-        const int id = tid + NTHR * r, t = id / (NR / 8), c8 = id % (NR / 8);
-        bo[r] = c8 * 16;
-        bt_[r] = t;
-        blo[r] = t * BP + c8 * 8;
+    for (int k = 0; k < IPW; ++k) {
+        const int row = (wave * IPW + k) * RPI + lane / UPR;
+        bdoff[k] = (uint32_t)(row * brow + 16 * ((lane % UPR) ^ swz(row)));
     }
-    // x: piece id is 16 bytes (8 p) of one token row; the two 8-lane halves of each
-    // 16 lanes take rows t and t + 4, whose LDS rows are 128 bytes apart mod 256
-#pragma unroll
-    for (int r = 0; r < XPT; ++r) {
-        const int id = min(tid + NTHR * r, XPIECES - 1), c8 = id & 7, g = id >> 4;
-        const int t = (g >> 2) * 8 + (g & 3) + 4 * ((id >> 3) & 1);
-        xo[r] = c8 * 16;
-        xt_[r] = t;
-        xlo[r] = t * XRP + c8 * 8;
-    }
-    const char *Bbytes = reinterpret_cast<const char *>(Bb);
-    const char *xbytes = reinterpret_cast<const char *>(xb);
-    const int brow = (int)bstride * 2, xrow = (int)xstride * 2;
-    // x~ k-packing: 16-lane group j transpose-reads tokens 4 tb .. 4 tb + 3 of p
-    // block pb (16 p) of the scaled token-major tile; lane m of the group gets
-    // those 4 tokens of p = 16 pb + m and writes them k-packed.  The groups of one
-    // wave take consecutive token blocks so their 8-byte writes land in distinct
-    // banks.
-    const int m16 = lane & 15;
-    int tbv[TRL], pbv[TRL];
-#pragma unroll
-    for (int r = 0; r < TRL; ++r) {
-        const int gr = (lane >> 4) + 4 * wave + 4 * C::NWAVE * r;
-        tbv[r] = gr % (TS / 4);
-        pbv[r] = gr / (TS / 4);
-    }
+    // x piece: columns 2 pp, 2 pp + 1 of tokens TPP tq .. TPP tq + TPP - 1
+    const int pp = tid & 31, tq = tid >> 5;
+    const uint32_t xoff = (uint32_t)(TPP * tq * xrow + 4 * pp);
     struct Regs {
-        bf16x8 b[BPT];
-        bf16x8 x[XPT];
-        float w[XPT];   // weight of the token of x piece r
+        uint32_t xv[TPP];
+        f32x4 w[TPP / 4];
         float gl;
     };
-    const int last_row = L - 1;
+    const int last_sub = U - 1;
     auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
-    // Issue order: the values the x~ copy needs one step after this load (the chunk's
-    // last cumsum value, the weights, x) before the B tile, which is copied a step later:
-    // wait counts retire loads in issue order, so waiting for the first ones leaves the
-    // B loads in flight.
-    auto load = [&](Regs &R, int u) {
-        u = min(u, U - 1);
+    auto dma_b = [&](int kb, int u) {
+        u = min(u, last_sub);
         const int t0 = tok0(u);
-        // the chunk's last cumsum value, as a per-lane load (a scalar load would
-        // share the LDS wait counter and stall every LDS wait behind it)
-        int gi = (c0 + u / NSUB) * Q + Q - 1;
-        asm volatile("" : "+v"(gi));
-        R.gl = Gh[gi];
+        const rsrc_t br = make_rsrc(Bbytes + (int64_t)t0 * brow, (L - t0) * brow);
+        bf16 *dst = bsel(kb);
 #pragma unroll
-        for (int r = 0; r < XPT; ++r) R.w[r] = wh[t0 + xt_[r]];
-#pragma unroll
-        for (int r = 0; r < XPT; ++r) {
-            const uint32_t off = (uint32_t)(min(t0 + xt_[r], last_row) * xrow + xo[r]);
-            R.x[r] = *reinterpret_cast<const bf16x8 *>(xbytes + off);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keeps this issue order
-#pragma unroll
-        for (int r = 0; r < BPT; ++r) {
-            const uint32_t off = (uint32_t)(min(t0 + bt_[r], last_row) * brow + bo[r]);
-            R.b[r] = *reinterpret_cast<const bf16x8 *>(Bbytes + off);
-        }
+        for (int k = 0; k < IPW; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(dst + (wave * IPW + k) * RPI * NR),
+                                                     16, (int)bdoff[k], 0, 0, 0);
     };
-    // LDS buffer indices are passed in as compile-time constants
-    auto storeB = [&](const Regs &R, int kb) {
-#pragma unroll
-        for (int r = 0; r < BPT; ++r) *reinterpret_cast<bf16x8 *>(&Bs[kb][blo[r]]) = R.b[r];
-    };
-    auto storeX = [&](const Regs &R, int kx, int ka) {
-        // x~ = round(w_t x_t), token-major
-#pragma unroll
-        for (int r = 0; r < XPT; ++r) {
-            const u32x4 xv = __builtin_bit_cast(u32x4, R.x[r]);
-            u32x4 o;
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) o[k2] = pack_bf16(bf_lo(xv[k2]) * R.w[r], bf_hi(xv[k2]) * R.w[r]);
-            if (XPT * NTHR == XPIECES || tid + NTHR * r < XPIECES)
-                *reinterpret_cast<u32x4 *>(&Xr[kx][xlo[r]]) = o;
+    // x, weights and (for the first sub-step of a chunk, the only one that uses it) the
+    // chunk-end cumsum value of sub-step u; `with_gl` is a compile-time constant, so the
+    // number of memory instructions a call issues is known
+    auto load = [&](Regs &R, int u, auto with_gl) {
+        u = min(u, last_sub);
+        const int t0 = tok0(u);
+        if constexpr (decltype(with_gl)::value) {
+            int gi = (c0 + u / NSUB) * Q + Q - 1;
+            asm volatile("" : "+v"(gi));   // per-lane load: a scalar one would share the LDS wait counter
+            R.gl = Gh[gi];
         }
-        Al[ka] = fast_exp2(R.gl);   // same value from every thread
-    };
-    auto build = [&](int k, int kx) {
+        const float *wb = wh + t0 + TPP * tq;
 #pragma unroll
-        for (int r = 0; r < TRL; ++r) {
-            const int tb = tbv[r], pb = pbv[r];
-            const bf16x4 v = tr_read4(&Xr[k][(4 * tb + (m16 >> 2)) * XRP + 16 * pb + 4 * (m16 & 3)]);
-            *reinterpret_cast<bf16x4 *>(&Xk[kx][(16 * pb + m16) * XKP + 4 * tb]) = v;
+        for (int k = 0; k < TPP / 4; ++k) R.w[k] = *reinterpret_cast<const f32x4 *>(wb + 4 * k);
+        const rsrc_t xr = make_rsrc(xbytes + (int64_t)t0 * xrow, (L - t0) * xrow);
+#pragma unroll
+        for (int k = 0; k < TPP; ++k) R.xv[k] = buf_load_b32(xr, xoff + k * xrow);
+    };
+    // k-packed x~ row p: 16-byte unit u (8 tokens) stored at unit u ^ ((p >> 4) & 1)
+    auto xk_off = [](int p, int u) { return p * XKP + 8 * (u ^ ((p >> 4) & 1)); };
+    auto stageX = [&](const Regs &R, int kx) {
+        uint32_t f0[TPP / 2], f1[TPP / 2];
+#pragma unroll
+        for (int k2 = 0; k2 < TPP / 2; ++k2) {
+            const float w0 = R.w[k2 >> 1][2 * (k2 & 1)], w1 = R.w[k2 >> 1][2 * (k2 & 1) + 1];
+            const uint32_t a = R.xv[2 * k2], c = R.xv[2 * k2 + 1];
+            f0[k2] = pack_bf16(bf_lo(a) * w0, bf_lo(c) * w1);
+            f1[k2] = pack_bf16(bf_hi(a) * w0, bf_hi(c) * w1);
+        }
+        if constexpr (TPP == 8) {
+            *reinterpret_cast<u32x4 *>(&Xk[kx][xk_off(2 * pp, tq)]) = u32x4{f0[0], f0[1], f0[2], f0[3]};
+            *reinterpret_cast<u32x4 *>(&Xk[kx][xk_off(2 * pp + 1, tq)]) = u32x4{f1[0], f1[1], f1[2], f1[3]};
+        } else {
+            *reinterpret_cast<u32x2 *>(&Xk[kx][xk_off(2 * pp, tq >> 1) + 4 * (tq & 1)]) = u32x2{f0[0], f0[1]};
+            *reinterpret_cast<u32x2 *>(&Xk[kx][xk_off(2 * pp + 1, tq >> 1) + 4 * (tq & 1)]) = u32x2{f1[0], f1[1]};
         }
     };
 
-    const int offA = tr_off_natural(lane, BP);
-    const int offB = (lane & 31) * XKP + 8 * (lane >> 5);
-
-    // chunk start (sub-step u, u % NSUB == 0): the chunk-start state goes to the
-    // LDS staging tile as bf16 (row p, columns n), then the state decays
-    auto chunk_start = [&](int ka) {
+    // chunk start: the chunk-start state to the staging tile (bf16, row p, columns n), then
+    // the state decays
+    auto chunk_start = [&](float gl) {
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
 #pragma unroll
@@ -316,7 +276,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
                     *reinterpret_cast<bf16x4 *>(&Ss[p * SSP + n + 8 * q]) = o;
                 }
             }
-        const float a = Al[ka];
+        const float a = fast_exp2(gl);
 #pragma unroll
         for (int i = 0; i < RTW; ++i)
 #pragma unroll
@@ -324,8 +284,6 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] *= a;
     };
-    // the staged state of chunk c to HBM: thread piece r is row p, 8 columns;
-    // consecutive lanes cover consecutive 16 bytes of a row
     auto state_out = [&](int c) {
         char *Sc = reinterpret_cast<char *>(S + ((int64_t)bh * nc + c) * P * N + n0);
 #pragma unroll
@@ -335,80 +293,116 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
             *reinterpret_cast<bf16x8 *>(Sc + (uint32_t)((p * N + 8 * c8) * 2)) = v;
         }
     };
+    // transpose-read operand: lane l reads 4 tokens (rows) of 4 columns; rows
+    // 8 (l / 32) + (l % 16) / 4 (+ 4 for the second read), columns 32 tile + 16 ((l / 16) & 1) + 4 (l % 4)
+    const int arow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    int aoff[RTW];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i) {
+        const int u = 4 * (rt0 + i) + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        aoff[i] = arow * NR + 8 * (u ^ swz(arow)) + 4 * (lane & 1);
+    }
+    const int l32 = lane & 31, half = lane >> 5;
     auto mma_sub = [&](int kb, int kx) {
-        const bf16 *bt = &Bs[kb][offA];
-        const bf16 *xt = &Xk[kx][offB];
+        const bf16 *bt = bsel(kb);
 #pragma unroll
         for (int ks = 0; ks < TS / 16; ++ks) {
             bf16x8 bfr[CTW];
 #pragma unroll
-            for (int j = 0; j < CTW; ++j) bfr[j] = ld16(xt + 32 * (ct0 + j) * XKP + 16 * ks);
+            for (int j = 0; j < CTW; ++j) bfr[j] = ld16(&Xk[kx][xk_off(32 * (ct0 + j) + l32, 2 * ks + half)]);
 #pragma unroll
             for (int i = 0; i < RTW; ++i) {
-                const bf16 *a0 = bt + 16 * ks * BP + 32 * (rt0 + i);
-                const bf16x8 af = cat8(tr_read4(a0), tr_read4(a0 + 4 * BP));
+                const bf16 *a0 = bt + 16 * ks * NR + aoff[i];
+                const bf16x8 af = cat8(tr_read4(a0), tr_read4(a0 + 4 * NR));
 #pragma unroll
                 for (int j = 0; j < CTW; ++j) mma(acc[i][j], af, bfr[j]);
             }
         }
     };
+    // memory instructions issued after the B DMA of step j - 1 and before the barrier of step j
+    // (a lower bound, so the wait never falls short): step j - 1's x loads and late state
+    // stores, step j's DMA, x loads and late state stores
+    // (nx: the x loads a step issues, with the chunk-end value when sub-step s + 2 starts a
+    // chunk; the step before position 0 is the prologue or the previous block's last step,
+    // which issue the same x loads)
+    constexpr auto wait_n = [](int j) {
+        const auto so_late = [](int i) { return (NSUB > 1 && i % NSUB == 1) ? SPT : 0; };
+        const auto nx = [](int i) { return TPP + TPP / 4 + (((i + 2) % NSUB == 0) ? 1 : 0); };
+        return nx(j > 0 ? j - 1 : lcm3(NSUB, 3, 2) - 1) + (j > 0 ? so_late(j - 1) : 0) + IPW + nx(j) +
+               so_late(j);
+    };
+// (sched_barrier keeps the scheduler from moving any instruction across: otherwise it
+// pulls the next step's register work up, and its wait for this step's x loads drains
+// the B loads in flight with them)
+#define SP_BARRIER(n)                                                                           \
+    do {                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        asm volatile("" ::: "memory");                                                          \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(n));                                               \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                         \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+#define LDS_BARRIER()                                                                           \
+    do {                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                         \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
 
-    // Register ring of D sub-steps: sub-step u sits in R[u % D] from its load
-    // (step u - 1 - D) until its B tile is copied (step u - 1); its x~ is copied
-    // one step earlier (step u - 2).
-    static_assert(D >= 2, "a ring slot holds one sub-step from x~ copy to B copy");
-    Regs R[D];
-    // step s, with j = s mod UNR a compile-time constant
-    // The products of sub-step s come first so that the copies for later
-    // sub-steps (independent buffers) can issue while the MFMAs run.
-    auto step = [&](int s, int j) {
+    Regs R[2];
+    // step s: B of sub-step s + 2 and x of sub-step s + 2 go out, products of sub-step s,
+    // x~ of sub-step s + 1 into LDS, then wait for B of sub-step s + 1 and synchronise
+    auto step = [&](int s, auto jc) {
+        constexpr int j = decltype(jc)::value;
         if (j % NSUB == 0) {
             if constexpr (NSUB == 1) {   // the previous chunk's staged state leaves first
                 if (s > 0) state_out(c0 + s - 1);
-                __syncthreads();
+                LDS_BARRIER();
             }
-            chunk_start(j & 3);
+            chunk_start(R[j & 1].gl);
         }
-        mma_sub(j & 1, j & 1);
-        storeB(R[(j + 1) % D], (j + 1) & 1);
-        storeX(R[(j + 2) % D], (j + 2) & 1, (j + 2) & 3);
-        load(R[(j + 1) % D], s + 1 + D);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        dma_b((j + 2) % 3, s + 2);
+        asm volatile("" ::: "memory");
+        load(R[j & 1], s + 2, std::integral_constant<bool, (j + 2) % NSUB == 0>{});
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);   // the loads go out before anything waits
+        mma_sub(j % 3, j & 1);
+        stageX(R[(j + 1) & 1], (j + 1) & 1);
         if (NSUB > 1 && j % NSUB == 1) state_out(c0 + s / NSUB);
-        build((j + 1) & 1, (j + 1) & 1);
-        __syncthreads();
+        constexpr int nwait = wait_n(j);
+        SP_BARRIER(nwait);
     };
 
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(R[u], u);
-    storeX(R[0], 0, 0);
-    storeB(R[0], 0);
-    load(R[0], D);
-    storeX(R[1 % D], 1, 1);
-    __syncthreads();
-    build(0, 0);
-    __syncthreads();
-    // The body covers UNR = lcm(NSUB, D, 4) sub-steps so that ring slots, LDS
-    // buffers and chunk-start positions are compile-time constants.
-    constexpr int UNR = lcm3(NSUB, D, 4);
+    dma_b(0, 0);
+    asm volatile("" ::: "memory");
+    load(R[0], 0, std::true_type{});
+    asm volatile("" ::: "memory");
+    dma_b(1, 1);
+    asm volatile("" ::: "memory");
+    load(R[1], 1, std::integral_constant<bool, NSUB == 1>{});
+    asm volatile("" ::: "memory");
+    stageX(R[0], 0);
+    constexpr int nwait0 = (TPP + TPP / 4 + 1) + IPW + (TPP + TPP / 4 + (NSUB == 1 ? 1 : 0));
+    SP_BARRIER(nwait0);   // B of sub-step 0
+    constexpr int UNR = lcm3(NSUB, 3, 2);
     int s = 0;
-    for (; s + UNR <= U; s += UNR) {
-#pragma unroll
-        for (int j = 0; j < UNR; ++j) step(s + j, j);
-    }
-#pragma unroll
-    for (int j = 0; j < UNR; ++j)
-        if (s + j < U) step(s + j, j);
-    // with one sub-step per chunk the last chunk's staged state is still in LDS
+    for (; s + UNR <= U; s += UNR) static_for<UNR>([&](auto jc) { step(s + decltype(jc)::value, jc); });
+    static_for<UNR>([&](auto jc) {
+        if (s + decltype(jc)::value < U) step(s + decltype(jc)::value, jc);
+    });
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no LDS load still in flight past this point
     if constexpr (NSUB == 1) state_out(c1 - 1);
+#undef SP_BARRIER
+#undef LDS_BARRIER
 
-    // decay products of the group (beta_c before each chunk, gamma for the group): lane k of
-    // wave 0 holds chunk c0 + k0 + k's decay (the first 64 from the prologue's loads, so no
-    // memory wait here) and the running product is taken in chunk order, as a sequential
-    // loop over the chunks would
+    // decay products of the group (beta_c before each chunk, gamma for the group), as in
+    // the kernel above
     if (n0 == 0 && wave == 0 && (beta != nullptr || gam != nullptr)) {
         float run = 1.0f;
-        auto products = [&](float g, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
-            const float e = fast_exp2(g);
+        auto products = [&](float gv, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
+            const float e = fast_exp2(gv);
             const int cnt = min(64, c1 - c0 - k0);
             float mine = 0.0f;
             for (int k = 0; k < cnt; ++k) {
@@ -468,7 +462,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_bf16_kernel(
 // bytes per 32 lanes.  Loads run D sub-steps ahead in a register ring; rows past
 // L are clamped to row L-1 (their weight is 0) and indices past the group's end
 // to its last sub-step, so the loop has no branches around memory operations.
-// Groups and the decay products for the group scan as in the kernel above.
+// Groups and the decay products for the group scan as in the LDS-transposed kernel.
 // ===========================================================================
 template <int Q, int NR, int D>
 __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
@@ -1532,13 +1526,12 @@ static bool head_blocked(const Shape &s)
            (s.Q == 128 && s.N == 512);
 }
 
-// register ring depth of the state pass (sub-steps in flight)
-constexpr int kSpDepth = 2;
+// register ring depth of the register-transposed state pass (sub-steps in flight)
 constexpr int kSpRtDepth = 2;
 
 // Which state pass runs: the register-transposed kernel for N a multiple of 256 from
 // 512 up (256-column workgroups of 4 waves, two per CU), the LDS-transposed kernel
-// otherwise.  Measured on MI355X (bf16, one box, µs per state pass): b1 L65536 H32 N512
+// with DMA staging otherwise.  Measured on MI355X (bf16, one box, µs per state pass): b1 L65536 H32 N512
 // Q128 486 -> 433; at N = 256 (b1 L16384 H32 Q256) 38.7 -> 37.5 with one workgroup per
 // CU and 35.0 with two (then 16 groups, whose scan costs 4 µs more); at N = 128
 // 28.8 -> 30.3-38.0 (b4 L16384 H8 Q128) and 9.9 -> 10.3-11.5 (b2 L2048 H24 Q256).
@@ -1562,7 +1555,7 @@ static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const 
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((state_pass_bf16_kernel<Q, NR, kSpDepth>), dim3((unsigned)(units * ng)),
+    hipLaunchKernelGGL((state_pass_dma_kernel<Q, NR>), dim3((unsigned)(units * ng)),
                        dim3(SpCfg<Q, NR>::NTHR), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT,
                        h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
                        (int)s.nc, (int)s.Lp, K, ng, xcd);
