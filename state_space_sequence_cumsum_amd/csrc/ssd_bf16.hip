@@ -397,8 +397,10 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
 #undef SP_BARRIER
 #undef LDS_BARRIER
 
-    // decay products of the group (beta_c before each chunk, gamma for the group), as in
-    // the kernel above
+    // decay products of the group (beta_c before each chunk, gamma for the group): lane k of
+    // wave 0 holds chunk c0 + k0 + k's decay (the first 64 from the prologue's loads, so no
+    // memory wait here) and the running product is taken in chunk order, as a sequential
+    // loop over the chunks would
     if (n0 == 0 && wave == 0 && (beta != nullptr || gam != nullptr)) {
         float run = 1.0f;
         auto products = [&](float gv, int k0) {   // chunks c0 + k0 .. c0 + k0 + 63
