@@ -209,7 +209,7 @@ def summarize_pmc(w, fetch_dir, write_dir, copy_mib):
     w_scale = known_kib / max(wr["copy"])
     alg = algorithmic(w)
     cmd = ("rocprofv3 --pmc {c} -f csv -d {d} -o run -- python3 bench.py --steps 3 --warmup 1 "
-           f"--no-cpu-baseline --cold-reps 0 --copy-mib {copy_mib} --workload {w.name}")
+           f"--kernel-reps 3 --no-cpu-baseline --cold-reps 0 --copy-mib {copy_mib} --workload {w.name}")
     out = {"workload": w.name, "source_hash": source_hash(), "copy_mib": copy_mib,
            "commands": [cmd.format(c="FETCH_SIZE", d=fetch_dir), cmd.format(c="WRITE_SIZE", d=write_dir),
                         f"python bench.py --summarize-pmc {fetch_dir} {write_dir} --copy-mib {copy_mib}"

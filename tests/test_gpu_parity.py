@@ -223,6 +223,28 @@ def test_no_decay_linear_attention(dtype):
     _check_forward(w, inp=inp)
 
 
+WEAK_DECAY = [
+    _wl("weak_decay_n128", "bf16", 1, 4096, 4, 64, 128, 1, 128),
+    _wl("weak_decay_n256", "bf16", 2, 3000, 3, 64, 256, 1, 256),
+    _wl("weak_decay_n512", "bf16", 1, 3000, 2, 64, 512, 2, 128),     # register-transposed state pass
+    _wl("weak_decay_fp32", "fp32", 1, 3000, 2, 64, 128, 1, 128),
+]
+
+
+@pytest.mark.parametrize("w", WEAK_DECAY, ids=[c.name for c in WEAK_DECAY])
+def test_grouped_weak_decay(w):
+    """A scaled by 1e-3: the decay over the whole sequence stays above one half, so the
+    state a group of chunks inherits (the group scan's carried state and the S + beta H
+    correction of the chunk output) is most of every chunk-start state and of hT."""
+    dev = require_gpu()
+    inp = make_inputs(w, 12)
+    inp["A"].mul_(1e-3)
+    total = (inp["A"][None, :] * inp["dt"].float().sum(dim=1)).exp()
+    assert float(total.min()) > 0.5
+    assert ssd.ssd_plan(ssd.problem_of(inp["x"], inp["B"], w.chunk))["sp_groups"] > 1
+    _check_forward(w, inp=inp, dev=dev)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_masked_exponent_overflow(dtype):
     """A = -16 and dt near 1: within a chunk |G2| passes 128, so the masked upper
