@@ -406,12 +406,19 @@ def bench_sweep(args):
                   for i, n in enumerate(STAGES)}
             alg = algorithmic(w)
             plan = ssd.ssd_plan(prob)
+            extra = {}
+            if args.autotune:
+                t = ssd.autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], None,
+                                 chunk=w.chunk, stream=stream)
+                extra = {"tuned_plan": t["plan"], "tuned_forward_us": t["forward_us"],
+                         "default_forward_us": t["default_forward_us"],
+                         "tuned_tokens_per_s": round(w.batch * L / (t["forward_us"] * 1e-6))}
             print(json.dumps({"workload": w.name, "tokens_per_s": round(w.batch * L / el),
                               "us_per_forward": round(el * 1e6, 2),
                               "kernel_median_us": {n: round(v, 2) for n, v in st.items()},
                               "frac_hbm": {n: round(alg[n]["bytes"] / (st[n] * 1e-6) / 1e9
                                                     / HBM_PEAK_GBS, 4) for n in st if n in alg},
-                              "plan": plan}),
+                              "plan": plan, **extra}),
                   flush=True)
             del d, y, ws
 
@@ -441,6 +448,9 @@ def main():
                     help="time the forward over the 1K-256K token x state 64-512 grid")
     ap.add_argument("--step", type=int, default=0, metavar="B",
                     help="time the decode step at batch B instead of the forward pass")
+    ap.add_argument("--autotune", action="store_true",
+                    help="search the launch configurations (ssd_plan_candidates) before the "
+                         "warm-up and run the fastest instead of the cost model's plan")
     args = ap.parse_args()
 
     if args.summarize_pmc or args.summarize_trace:
@@ -476,8 +486,13 @@ def main():
     y = torch.empty(w.batch, w.seqlen, w.nheads, w.headdim, device=dev, dtype=io)
     hT = torch.empty(w.batch, w.nheads, w.headdim, w.dstate, device=dev, dtype=torch.float32)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
-    ws = ssd.workspace_for(prob, dev)
     stream = torch.cuda.current_stream(dev)
+    tuned = None
+    if args.autotune:     # one-time setup before the warm-up, as a deployment would do it
+        tuned = ssd.autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                             chunk=w.chunk, stream=stream)
+    launch_plan = tuned["plan"] if tuned else None
+    ws = ssd.workspace_for(prob, dev, launch_plan)
     names = STAGES
     reps = max(args.steps, args.kernel_reps)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ssd.FORWARD_EVENTS)]
@@ -489,14 +504,16 @@ def main():
 
     def forward(events=None):
         ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
-                        y=y, hT=hT, workspace=ws, stream=stream, events=events)
+                        y=y, hT=hT, workspace=ws, stream=stream, events=events,
+                        launch_plan=launch_plan)
 
     # the timed loop calls the C entry point through a plan (arguments checked once), or
     # with --graph replays one forward recorded into a HIP graph on a side stream
     if args.graph:
         side = torch.cuda.Stream(dev)
         gplan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
-                                chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=side)
+                                chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=side,
+                                launch_plan=launch_plan)
         forward()                       # kernels loaded before the capture
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -505,11 +522,13 @@ def main():
         timed = graph.replay
     else:
         plan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
-                               chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream)
+                               chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream,
+                               launch_plan=launch_plan)
         timed = plan.run
     # stage launches for the kernel-alone timing, on the launch stream
     aplan = ssd.ForwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
-                            chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream)
+                            chunk=w.chunk, y=y, hT=hT, workspace=ws, stream=stream,
+                            launch_plan=launch_plan)
 
     if args.copy_mib > 0:   # a plain copy of known size, outside the timed region
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -647,7 +666,12 @@ def main():
         "kernels_in_forward": {n: {k: round(v, 3) for k, v in in_fwd[n].items()} for n in names},
         "roofline": roof,
         "launch": "graph" if args.graph else "plan",
+        "plan": aplan.launch_plan,
+        "plan_source": "autotune" if tuned else "cost model",
     }
+    if tuned:
+        out["autotune"] = {k: tuned[k] for k in ("forward_us", "default_forward_us", "candidates",
+                                                 "default_plan")}
     if cold:
         out["cold"] = {"reps": len(cold), "flush_mib": FLUSH_MIB,
                        "median_us": round(statistics.median(cold), 2),

@@ -45,8 +45,9 @@
  * Supported set: dtype SSD_F32 or SSD_BF16; headdim 64; dstate a multiple of 64
  * up to 512; chunk 64, 128 or 256; batch * nheads <= 65535; seqlen * nheads * headdim
  * and seqlen * ngroups * dstate below 2^30; chunk * nheads * headdim and chunk *
- * ngroups * dstate below 2^31; ceil(seqlen / chunk) * batch * nheads below 2^31 (the
- * workgroup count of the one-head output kernel); any seqlen >= 1 (a partial last chunk is
+ * ngroups * dstate below 2^31; ceil(seqlen / chunk) * batch * nheads below 2^31 / chunk
+ * (the one-head output kernel's grid of 2 * chunk threads per workgroup, counted in 32
+ * bits); any seqlen >= 1 (a partial last chunk is
  * zero-padded, which is exact: a token with dt = 0 and x = B = C = 0 changes
  * nothing).  Other shapes return SSD_ERR_UNSUPPORTED.
  *
@@ -73,8 +74,9 @@ typedef enum {
     SSD_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than ssd_workspace_bytes() */
     SSD_ERR_HIP = 5,          /* a HIP launch failed; see ssd_last_hip_error()        */
     SSD_ERR_MISALIGNED = 6,   /* a vector-accessed array does not start on 16 bytes  */
-    SSD_ERR_SCRATCH = 7       /* ssd_forward_noalloc: the problem needs more than
+    SSD_ERR_SCRATCH = 7,      /* ssd_forward_noalloc: the problem needs more than
                                  SSD_SCRATCH_BYTES of workspace                         */
+    SSD_ERR_PLAN = 8          /* a launch plan the kernels cannot run for the problem   */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -219,12 +221,57 @@ typedef struct {
     int32_t co_column_split;    /* 2: state columns split over wave pairs (N = 512) */
     int32_t co_workgroups;      /* chunk-output workgroups (ragged last chunk included) */
     int32_t co_threads;         /* threads per head-blocked (else one-head) workgroup */
-    int32_t sp_register_transposed; /* 1: the state pass transposes B in registers (N >= 512),
-                                       0: through LDS */
+    int32_t sp_register_transposed; /* 1: the state pass transposes B in registers (256
+                                       columns per workgroup), 0: through LDS */
     int32_t sp_threads;         /* threads per state-pass workgroup */
 } ssd_launch_plan;
 
 ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan);
+
+/* The search space of the forward's launch configuration for `problem` (the optimisations
+ * are chosen per shape together with block size and occupancy, by measuring every
+ * candidate: dbyun.net, section "Mamba-2 性能优化"; thetimeai.ru, section "Почему раскладка
+ * памяти важна не меньше формул").  A candidate combines
+ *   - a state-pass kernel: 256, 128 or 64 state columns per workgroup (those dividing
+ *     dstate; bf16 only, fp32 always 64), for 256 columns B transposed through LDS or in
+ *     registers (sp_register_transposed);
+ *   - a split of every chain of chunks into groups: the cost model's count for that
+ *     kernel, then 1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96 and 128 groups as far as the
+ *     chain has chunks (sp_group_chunks = ceil(nc / groups), sp_groups = ceil(nc /
+ *     sp_group_chunks));
+ *   - a chunk-output kernel: head-blocked with each divisor of nheads / ngroups up to 64
+ *     as heads per workgroup (bf16, chunk 128 or 256 with dstate 64, 128 or 256, and chunk
+ *     128 with dstate 512), or one head per workgroup;
+ * with the derived fields filled in, duplicates and configurations whose grids do not fit
+ * 32-bit work-item counts left out.  plans[0] is ssd_plan's choice.  Writes the first
+ * min(capacity, count) candidates to `plans` (NULL allowed when capacity is 0) and their
+ * number to *count.  Host-only; SSD_ERR_NULL_ARG for a NULL count, a negative capacity or
+ * NULL plans with capacity > 0. */
+ssd_status ssd_plan_candidates(const ssd_problem *problem, ssd_launch_plan *plans,
+                               int32_t capacity, int32_t *count);
+
+/* Workspace bytes of the forward under `plan` (NULL: ssd_plan's choice, the same as
+ * ssd_workspace_bytes); 0 if `problem` or `plan` is not valid.  Host-only. */
+size_t ssd_workspace_bytes_planned(const ssd_problem *problem, const ssd_launch_plan *plan);
+
+/* Launches first_stage .. last_stage (0 chunk cumsum, 1 state pass, 2 group scan, 3 chunk
+ * output; 0 .. 3 is the whole forward pass) under launch plan `plan` (NULL: ssd_plan's
+ * choice; ssd_forward, ssd_forward_timed and ssd_forward_stage are this call with a NULL
+ * plan), the results of any valid plan being the method's, with the rounding of its own
+ * grouping.  A plan is valid when its choices are among those ssd_plan_candidates
+ * describes, with any chunks per group from 1 to nc, and each derived field matches what
+ * these choices give (ssd_plan_candidates' output always is); else SSD_ERR_PLAN before any
+ * launch.  `workspace` must hold ssd_workspace_bytes_planned(problem, plan) bytes and is
+ * laid out per plan: stages of one forward run with the same plan.  `events` (NULL: no
+ * marks) has SSD_FORWARD_EVENTS entries indexed by stage: events[i] is recorded right
+ * before stage i and events[last_stage + 1] after the last, for first_stage <= i <=
+ * last_stage.  Stages outside 0 .. 3 or first_stage > last_stage: SSD_ERR_UNSUPPORTED.
+ * Stage repetition rules, other arguments and errors as for ssd_forward_stage. */
+ssd_status ssd_forward_planned(const ssd_problem *problem, const ssd_launch_plan *plan,
+                               const void *x, const void *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *h0, void *y, float *hT,
+                               void *workspace, size_t workspace_bytes, int32_t first_stage,
+                               int32_t last_stage, void *const *events, void *stream);
 
 /* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,

@@ -22,7 +22,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "ssd.h")
 SSD_F32, SSD_BF16 = 0, 1
 FORWARD_EVENTS = 5      # SSD_FORWARD_EVENTS: marks around stage 1, state pass, group scan, stage 3
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
-          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED", 7: "SSD_ERR_SCRATCH"}
+          4: "SSD_ERR_WORKSPACE", 5: "SSD_ERR_HIP", 6: "SSD_ERR_MISALIGNED", 7: "SSD_ERR_SCRATCH",
+          8: "SSD_ERR_PLAN"}
 SCRATCH_BYTES = 128 << 20   # SSD_SCRATCH_BYTES: the static workspace of ssd_forward_noalloc
 
 
@@ -82,6 +83,15 @@ def lib():
         L.ssd_forward_noalloc.restype = st
         L.ssd_step.argtypes, L.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_plan.argtypes, L.ssd_plan.restype = [P, ctypes.POINTER(SsdLaunchPlan)], st
+        L.ssd_plan_candidates.argtypes = [P, ctypes.POINTER(SsdLaunchPlan), ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_int32)]
+        L.ssd_plan_candidates.restype = st
+        L.ssd_workspace_bytes_planned.argtypes = [P, ctypes.POINTER(SsdLaunchPlan)]
+        L.ssd_workspace_bytes_planned.restype = ctypes.c_size_t
+        L.ssd_forward_planned.argtypes = [P, ctypes.POINTER(SsdLaunchPlan), vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.POINTER(vp), vp]
+        L.ssd_forward_planned.restype = st
         L.ssd_status_string.argtypes, L.ssd_status_string.restype = [st], ctypes.c_char_p
         L.ssd_last_hip_error.argtypes, L.ssd_last_hip_error.restype = [], ctypes.c_int
         _lib = L
@@ -140,6 +150,36 @@ def ssd_plan(problem: SsdProblem) -> dict:
     plan = SsdLaunchPlan()
     _raise(lib().ssd_plan(ctypes.byref(problem), ctypes.byref(plan)), "ssd_plan")
     return {n: getattr(plan, n) for n, _ in SsdLaunchPlan._fields_}
+
+
+def _plan_struct(plan) -> SsdLaunchPlan:
+    """An SsdLaunchPlan from a field-name dict (as ssd_plan / plan_candidates return) or
+    an SsdLaunchPlan."""
+    if isinstance(plan, SsdLaunchPlan):
+        return plan
+    missing = [n for n, _ in SsdLaunchPlan._fields_ if n not in plan]
+    if missing:
+        raise ValueError(f"launch plan lacks fields {missing}")
+    return SsdLaunchPlan(**{n: int(plan[n]) for n, _ in SsdLaunchPlan._fields_})
+
+
+def plan_candidates(problem: SsdProblem) -> list[dict]:
+    """The forward's launch configurations for `problem` (host only; ssd_plan_candidates):
+    a list of field-name dicts, ssd_plan's choice first."""
+    count = ctypes.c_int32(0)
+    _raise(lib().ssd_plan_candidates(ctypes.byref(problem), None, 0, ctypes.byref(count)),
+           "ssd_plan_candidates")
+    arr = (SsdLaunchPlan * max(1, count.value))()
+    _raise(lib().ssd_plan_candidates(ctypes.byref(problem), arr, count.value, ctypes.byref(count)),
+           "ssd_plan_candidates")
+    return [{n: getattr(arr[i], n) for n, _ in SsdLaunchPlan._fields_} for i in range(count.value)]
+
+
+def ssd_workspace_bytes_planned(problem: SsdProblem, launch_plan=None) -> int:
+    """Workspace bytes of the forward under `launch_plan` (None: ssd_plan's); 0 when the
+    problem or the plan is not valid."""
+    plan = None if launch_plan is None else ctypes.byref(_plan_struct(launch_plan))
+    return lib().ssd_workspace_bytes_planned(ctypes.byref(problem), plan)
 
 
 def ssd_status_string(status: int) -> str:
@@ -243,10 +283,10 @@ def ssd_chunk_out(problem: SsdProblem, x, B, C, G2, dtT, S, D, y=None, stream=No
     return y
 
 
-def workspace_for(problem: SsdProblem, device) -> torch.Tensor:
-    n = ssd_workspace_bytes(problem)
+def workspace_for(problem: SsdProblem, device, launch_plan=None) -> torch.Tensor:
+    n = ssd_workspace_bytes_planned(problem, launch_plan)
     if n == 0:
-        _raise(ssd_validate(problem) or 3, "ssd_workspace_bytes")
+        _raise(ssd_validate(problem) or 8, "ssd_workspace_bytes_planned")
     return torch.empty(n, device=device, dtype=torch.uint8)
 
 
@@ -273,12 +313,13 @@ def _io_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final):
     return problem, dev, y, hT
 
 
-def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream):
+def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream,
+                  launch_plan=None):
     """Checked ctypes arguments of ssd_forward, with the outputs and the workspace
-    (allocated here when not given)."""
+    (allocated here when not given, sized for `launch_plan`)."""
     problem, dev, y, hT = _io_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final)
     if workspace is None:
-        workspace = workspace_for(problem, dev)
+        workspace = workspace_for(problem, dev, launch_plan)
     if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     nbytes = workspace.numel() * workspace.element_size()
@@ -287,24 +328,39 @@ def _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, st
     return problem, args, y, hT, workspace
 
 
+def _event_array(events):
+    if len(events) != FORWARD_EVENTS or not all(getattr(e, "cuda_event", 0) for e in events):
+        raise ValueError(f"events must be {FORWARD_EVENTS} torch.cuda.Event objects "
+                         "recorded at least once")
+    return (ctypes.c_void_p * FORWARD_EVENTS)(*[e.cuda_event for e in events])
+
+
+def _planned(args, plan, first, last, events):
+    """ssd_forward_planned with the ssd_forward argument tuple `args`."""
+    return lib().ssd_forward_planned(args[0], plan, *args[1:-1], int(first), int(last), events,
+                                     args[-1])
+
+
 def ssd_forward(x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None, want_final=True,
-                workspace=None, stream=None, events=None):
+                workspace=None, stream=None, events=None, launch_plan=None):
     """Whole forward pass.  Returns (y [b,L,H,P], hT [b,H,P,N] float32 or None).
 
     ``events``: optional ``FORWARD_EVENTS`` (5) recorded-once ``torch.cuda.Event``
     objects; they are re-recorded on the launch stream around each of the four
     launches (stage 1, state pass, group scan, stage 3; ssd_forward_timed).
+    ``launch_plan``: a candidate of ``plan_candidates`` to run instead of ssd_plan's
+    choice (ssd_forward_planned); the workspace must then be sized for it.
     """
     _, args, y, hT, _ = _forward_args(x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace,
-                                      stream)
-    if events is None:
+                                      stream, launch_plan)
+    if launch_plan is not None:
+        arr = None if events is None else _event_array(events)
+        _raise(_planned(args, ctypes.byref(_plan_struct(launch_plan)), 0, FORWARD_EVENTS - 2, arr),
+               "ssd_forward_planned")
+    elif events is None:
         _raise(lib().ssd_forward(*args), "ssd_forward")
     else:
-        if len(events) != FORWARD_EVENTS or not all(getattr(e, "cuda_event", 0) for e in events):
-            raise ValueError(f"events must be {FORWARD_EVENTS} torch.cuda.Event objects "
-                             "recorded at least once")
-        arr = (ctypes.c_void_p * FORWARD_EVENTS)(*[e.cuda_event for e in events])
-        _raise(lib().ssd_forward_timed(*args, arr), "ssd_forward_timed")
+        _raise(lib().ssd_forward_timed(*args, _event_array(events)), "ssd_forward_timed")
     return y, hT
 
 
@@ -330,25 +386,48 @@ class ForwardPlan:
     synchronises nothing)."""
 
     def __init__(self, x, dt, A, B, C, D, h0=None, *, chunk: int, y=None, hT=None,
-                 want_final=True, workspace=None, stream=None):
+                 want_final=True, workspace=None, stream=None, launch_plan=None):
         self._keep = (x, dt, A, B, C, D, h0)
         self._problem, self._args, self.y, self.hT, self.workspace = _forward_args(
-            x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream)
+            x, dt, A, B, C, D, h0, chunk, y, hT, want_final, workspace, stream, launch_plan)
+        # the launch configuration: ssd_plan's choice (plain ssd_forward) or the caller's
+        self.launch_plan = (ssd_plan(self._problem) if launch_plan is None
+                            else {n: getattr(_plan_struct(launch_plan), n)
+                                  for n, _ in SsdLaunchPlan._fields_})
+        self._plan = None if launch_plan is None else _plan_struct(launch_plan)
         self._fn = lib().ssd_forward
 
     def run(self):
         """One forward; returns (y, hT) (the same tensors every call)."""
-        st = self._fn(*self._args)
+        if self._plan is None:
+            st = self._fn(*self._args)
+        else:
+            st = _planned(self._args, ctypes.byref(self._plan), 0, FORWARD_EVENTS - 2, None)
         if st != 0:
             _raise(st, "ssd_forward")
         return self.y, self.hT
 
     def run_stage(self, stage: int):
-        """Launch one stage of the forward alone (ssd_forward_stage: 0 chunk cumsum, 1 state
-        pass, 2 group scan, 3 chunk output) on the plan's workspace, for timing one kernel."""
-        st = lib().ssd_forward_stage(*self._args[:-1], int(stage), self._args[-1])
+        """Launch one stage of the forward alone (0 chunk cumsum, 1 state pass, 2 group scan,
+        3 chunk output; ssd_forward_stage, or ssd_forward_planned under a caller's plan) on
+        the plan's workspace, for timing one kernel."""
+        if self._plan is None:
+            st = lib().ssd_forward_stage(*self._args[:-1], int(stage), self._args[-1])
+        else:
+            st = _planned(self._args, ctypes.byref(self._plan), stage, stage, None)
         if st != 0:
             _raise(st, "ssd_forward_stage")
+
+    def run_timed(self, events):
+        """One forward with FORWARD_EVENTS marks around its launches (see ssd_forward)."""
+        arr = _event_array(events)
+        if self._plan is None:
+            st = lib().ssd_forward_timed(*self._args, arr)
+        else:
+            st = _planned(self._args, ctypes.byref(self._plan), 0, FORWARD_EVENTS - 2, arr)
+        if st != 0:
+            _raise(st, "ssd_forward_timed")
+        return self.y, self.hT
 
 
 def _step_args(x, dt, A, B, C, D, h, y, stream):

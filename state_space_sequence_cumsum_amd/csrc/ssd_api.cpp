@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <initializer_list>
+#include <vector>
 
 #include "ssd_launch.h"
 
@@ -40,8 +41,9 @@ ssd_status check_shape(const ssd_problem *p)
     if (p->batch > 65535 || p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->batch * p->nheads > 65535) return SSD_ERR_UNSUPPORTED;
     if (p->seqlen > (int64_t(1) << 30)) return SSD_ERR_UNSUPPORTED;
-    // one-head chunk output: one workgroup per (chunk, batch, head) in a 1-D grid
-    if ((p->seqlen + p->chunk - 1) / p->chunk * p->batch * p->nheads >= (int64_t(1) << 31))
+    // one-head chunk output: one workgroup of 2 * chunk threads per (chunk, batch, head) in
+    // a 1-D grid, whose work-item count the dispatch packet holds in 32 bits
+    if ((p->seqlen + p->chunk - 1) / p->chunk * p->batch * p->nheads >= (int64_t(1) << 31) / p->chunk)
         return SSD_ERR_UNSUPPORTED;
     // in-chunk element offsets are 32-bit, and so are byte offsets within one batch
     // of x and of B / C
@@ -87,30 +89,77 @@ ssd::Shape make_shape(const ssd_problem *p)
 
 struct Layout {
     size_t g2, dtt, wt, S, ug, gam, beta, hb, total;
-    ssd::Grouping gp;
 };
 
-// Workspace of ssd_forward: the stage-1 outputs, the chunk-start states and,
-// when the state pass is split into groups, the group states, group decays and
-// per-chunk decays since the group start.
-Layout layout_of(const ssd::Shape &s)
+// Workspace of the forward pass under launch plan lp: the stage-1 outputs, the
+// chunk-start states and, when the state pass is split into groups, the group states,
+// group decays and per-chunk decays since the group start.
+Layout layout_of(const ssd::Shape &s, const ssd::LaunchPlan &lp)
 {
     const size_t bh = size_t(s.b) * s.H;
     const size_t cum = bh * s.Lp * sizeof(float);
     const size_t snap = bh * s.nc * s.P * s.N * (s.bf16 ? 2 : 4);
+    const size_t ng = size_t(lp.sp_groups);
+    const bool grouped = ng > 1;
     Layout l;
-    l.gp = ssd::state_pass_groups(s);
-    const bool grouped = l.gp.ng > 1;
     l.g2 = 0;
     l.dtt = align_up(cum);
     l.wt = l.dtt + align_up(cum);
     l.S = l.wt + align_up(cum);
     l.ug = l.S + align_up(snap);
-    l.gam = l.ug + (grouped ? align_up(bh * l.gp.ng * s.P * s.N * sizeof(float)) : 0);
-    l.beta = l.gam + (grouped ? align_up(bh * l.gp.ng * sizeof(float)) : 0);
+    l.gam = l.ug + (grouped ? align_up(bh * ng * s.P * s.N * sizeof(float)) : 0);
+    l.beta = l.gam + (grouped ? align_up(bh * ng * sizeof(float)) : 0);
     l.hb = l.beta + (grouped ? align_up(bh * s.nc * sizeof(float)) : 0);
-    l.total = l.hb + ((grouped && s.bf16) ? align_up(bh * l.gp.ng * s.P * s.N * 2) : 0);
+    l.total = l.hb + ((grouped && s.bf16) ? align_up(bh * ng * s.P * s.N * 2) : 0);
     return l;
+}
+
+ssd::LaunchPlan to_internal(const ssd_launch_plan &p)
+{
+    ssd::LaunchPlan lp;
+    lp.sp_group_chunks = p.sp_group_chunks;
+    lp.sp_groups = p.sp_groups;
+    lp.sp_columns = p.sp_columns;
+    lp.sp_workgroups = p.sp_workgroups;
+    lp.scan = p.scan;
+    lp.co_head_blocked = p.co_head_blocked;
+    lp.co_heads_per_block = p.co_heads_per_block;
+    lp.co_column_split = p.co_column_split;
+    lp.co_workgroups = p.co_workgroups;
+    lp.co_threads = p.co_threads;
+    lp.sp_register_transposed = p.sp_register_transposed;
+    lp.sp_threads = p.sp_threads;
+    return lp;
+}
+
+ssd_launch_plan to_public(const ssd::LaunchPlan &lp)
+{
+    ssd_launch_plan p;
+    p.sp_group_chunks = lp.sp_group_chunks;
+    p.sp_groups = lp.sp_groups;
+    p.sp_columns = lp.sp_columns;
+    p.sp_workgroups = lp.sp_workgroups;
+    p.scan = lp.scan;
+    p.co_head_blocked = lp.co_head_blocked;
+    p.co_heads_per_block = lp.co_heads_per_block;
+    p.co_column_split = lp.co_column_split;
+    p.co_workgroups = lp.co_workgroups;
+    p.co_threads = lp.co_threads;
+    p.sp_register_transposed = lp.sp_register_transposed;
+    p.sp_threads = lp.sp_threads;
+    return p;
+}
+
+// The plan a forward call runs: the cost model's when `plan` is NULL, else the caller's
+// after checking that the kernels can run it.
+ssd_status resolve_plan(const ssd::Shape &s, const ssd_launch_plan *plan, ssd::LaunchPlan &lp)
+{
+    if (plan == nullptr) {
+        lp = ssd::plan_of(s);
+        return SSD_OK;
+    }
+    lp = to_internal(*plan);
+    return ssd::plan_valid(s, lp) ? SSD_OK : SSD_ERR_PLAN;
 }
 
 ssd_status hip_status(hipError_t e)
@@ -131,7 +180,17 @@ ssd_status ssd_validate(const ssd_problem *problem) { return check_shape(problem
 size_t ssd_workspace_bytes(const ssd_problem *problem)
 {
     if (check_shape(problem) != SSD_OK) return 0;
-    return layout_of(make_shape(problem)).total;
+    const ssd::Shape s = make_shape(problem);
+    return layout_of(s, ssd::plan_of(s)).total;
+}
+
+size_t ssd_workspace_bytes_planned(const ssd_problem *problem, const ssd_launch_plan *plan)
+{
+    if (check_shape(problem) != SSD_OK) return 0;
+    const ssd::Shape s = make_shape(problem);
+    ssd::LaunchPlan lp;
+    if (resolve_plan(s, plan, lp) != SSD_OK) return 0;
+    return layout_of(s, lp).total;
 }
 
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
@@ -140,7 +199,8 @@ ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (!off_G2 || !off_dtT || !off_wT || !off_S) return SSD_ERR_NULL_ARG;
-    const Layout l = layout_of(make_shape(problem));
+    const ssd::Shape s = make_shape(problem);
+    const Layout l = layout_of(s, ssd::plan_of(s));
     *off_G2 = l.g2;
     *off_dtT = l.dtt;
     *off_wT = l.wt;
@@ -153,19 +213,23 @@ ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan)
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
     if (plan == nullptr) return SSD_ERR_NULL_ARG;
-    const ssd::LaunchPlan lp = ssd::plan_of(make_shape(problem));
-    plan->sp_group_chunks = lp.sp_group_chunks;
-    plan->sp_groups = lp.sp_groups;
-    plan->sp_columns = lp.sp_columns;
-    plan->sp_workgroups = lp.sp_workgroups;
-    plan->scan = lp.scan;
-    plan->co_head_blocked = lp.co_head_blocked;
-    plan->co_heads_per_block = lp.co_heads_per_block;
-    plan->co_column_split = lp.co_column_split;
-    plan->co_workgroups = lp.co_workgroups;
-    plan->co_threads = lp.co_threads;
-    plan->sp_register_transposed = lp.sp_register_transposed;
-    plan->sp_threads = lp.sp_threads;
+    *plan = to_public(ssd::plan_of(make_shape(problem)));
+    return SSD_OK;
+}
+
+ssd_status ssd_plan_candidates(const ssd_problem *problem, ssd_launch_plan *plans,
+                               int32_t capacity, int32_t *count)
+{
+    const ssd_status st = check_shape(problem);
+    if (st != SSD_OK) return st;
+    if (count == nullptr || capacity < 0 || (capacity > 0 && plans == nullptr))
+        return SSD_ERR_NULL_ARG;
+    const ssd::Shape s = make_shape(problem);
+    const int n = ssd::plan_candidates(s, nullptr, 0);
+    std::vector<ssd::LaunchPlan> all((size_t)n);
+    ssd::plan_candidates(s, all.data(), n);
+    for (int i = 0; i < n && i < capacity; ++i) plans[i] = to_public(all[(size_t)i]);
+    *count = n;
     return SSD_OK;
 }
 
@@ -209,22 +273,26 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
 namespace {
 
 // Launches first..last (0 chunk cumsum, 1 state pass, 2 group scan, 3 chunk output) of
-// the forward on `stream`, with events[i] recorded right before launch i and
-// events[last + 1] after the last (events NULL: no marks).
-ssd_status forward_launches(const ssd_problem *problem, const void *x, const void *dt,
-                            const float *A, const void *B, const void *C, const float *D,
-                            const float *h0, void *y, float *hT, void *workspace,
-                            size_t workspace_bytes, void *stream, void *const *events, int first,
-                            int last)
+// the forward under `plan` (NULL: the cost model's) on `stream`, with events[i] recorded
+// right before launch i and events[last + 1] after the last (events NULL: no marks).
+ssd_status forward_launches(const ssd_problem *problem, const ssd_launch_plan *plan,
+                            const void *x, const void *dt, const float *A, const void *B,
+                            const void *C, const float *D, const float *h0, void *y, float *hT,
+                            void *workspace, size_t workspace_bytes, void *stream,
+                            void *const *events, int first, int last)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
+    if (first < 0 || last > SSD_FORWARD_EVENTS - 2 || first > last) return SSD_ERR_UNSUPPORTED;
     if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_NULL_ARG;
     if (events != nullptr)
         for (int i = first; i <= last + 1; ++i)
             if (!events[i]) return SSD_ERR_NULL_ARG;
     const ssd::Shape s = make_shape(problem);
-    const Layout l = layout_of(s);
+    ssd::LaunchPlan lp;
+    const ssd_status pst = resolve_plan(s, plan, lp);
+    if (pst != SSD_OK) return pst;
+    const Layout l = layout_of(s, lp);
     if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
     if (!aligned16({x, B, C, h0, y, hT, workspace})) return SSD_ERR_MISALIGNED;
     char *ws = static_cast<char *>(workspace);
@@ -244,11 +312,11 @@ ssd_status forward_launches(const ssd_problem *problem, const void *x, const voi
         switch (i) {
         case 0: return ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs);
         case 1:
-            return ssd::launch_state_pass_grouped(s, l.gp, x, B, G2, wT, h0, S, hT, Ug, gam, beta,
+            return ssd::launch_state_pass_grouped(s, lp, x, B, G2, wT, h0, S, hT, Ug, gam, beta,
                                                   hs);
-        case 2: return ssd::launch_group_scan(s, l.gp, hT, Ug, Hb, gam, hs);
+        case 2: return ssd::launch_group_scan(s, lp, hT, Ug, Hb, gam, hs);
         default:
-            return ssd::launch_chunk_out_corrected(s, l.gp, x, B, C, G2, dtT, S, D, y, Ug, Hb,
+            return ssd::launch_chunk_out_corrected(s, lp, x, B, C, G2, dtT, S, D, y, Ug, Hb,
                                                    beta, hs);
         }
     };
@@ -270,16 +338,16 @@ ssd_status ssd_forward_timed(const ssd_problem *problem, const void *x, const vo
                              const float *h0, void *y, float *hT, void *workspace,
                              size_t workspace_bytes, void *stream, void *const *events)
 {
-    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
-                            stream, events, 0, SSD_FORWARD_EVENTS - 2);
+    return forward_launches(problem, nullptr, x, dt, A, B, C, D, h0, y, hT, workspace,
+                            workspace_bytes, stream, events, 0, SSD_FORWARD_EVENTS - 2);
 }
 
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt, const float *A,
                        const void *B, const void *C, const float *D, const float *h0, void *y,
                        float *hT, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
-                            stream, nullptr, 0, SSD_FORWARD_EVENTS - 2);
+    return forward_launches(problem, nullptr, x, dt, A, B, C, D, h0, y, hT, workspace,
+                            workspace_bytes, stream, nullptr, 0, SSD_FORWARD_EVENTS - 2);
 }
 
 ssd_status ssd_forward_stage(const ssd_problem *problem, const void *x, const void *dt,
@@ -287,12 +355,18 @@ ssd_status ssd_forward_stage(const ssd_problem *problem, const void *x, const vo
                              const float *h0, void *y, float *hT, void *workspace,
                              size_t workspace_bytes, int stage, void *stream)
 {
-    if (stage < 0 || stage > SSD_FORWARD_EVENTS - 2) {
-        const ssd_status st = check_shape(problem);
-        return st != SSD_OK ? st : SSD_ERR_UNSUPPORTED;
-    }
-    return forward_launches(problem, x, dt, A, B, C, D, h0, y, hT, workspace, workspace_bytes,
-                            stream, nullptr, stage, stage);
+    return forward_launches(problem, nullptr, x, dt, A, B, C, D, h0, y, hT, workspace,
+                            workspace_bytes, stream, nullptr, stage, stage);
+}
+
+ssd_status ssd_forward_planned(const ssd_problem *problem, const ssd_launch_plan *plan,
+                               const void *x, const void *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *h0, void *y, float *hT,
+                               void *workspace, size_t workspace_bytes, int32_t first_stage,
+                               int32_t last_stage, void *const *events, void *stream)
+{
+    return forward_launches(problem, plan, x, dt, A, B, C, D, h0, y, hT, workspace,
+                            workspace_bytes, stream, events, first_stage, last_stage);
 }
 
 ssd_status ssd_step(const ssd_problem *problem, const void *x, const void *dt, const float *A,
@@ -322,6 +396,7 @@ const char *ssd_status_string(ssd_status status)
     case SSD_ERR_SCRATCH:
         return "the problem needs more workspace than the static scratch of ssd_forward_noalloc "
                "holds (SSD_SCRATCH_BYTES); use ssd_forward with a workspace";
+    case SSD_ERR_PLAN: return "the launch plan is not one the kernels can run for this problem";
     }
     return "unknown status";
 }

@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "ssd_device.h"
 #include "ssd_launch.h"
@@ -1542,14 +1543,14 @@ constexpr int kSpRtDepth = 2;
 static bool sp_register_transposed(const Shape &s) { return s.N >= 512 && s.N % 256 == 0; }
 
 template <int Q, int NR>
-static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const float *G2,
+static hipError_t sp_launch(const Shape &s, bool rt, const void *x, const void *B, const float *G2,
                             const float *wT, const float *h0, void *S, float *hT, float *Ug,
                             float *gam, float *beta, int K, int ng, hipStream_t st)
 {
     const int units = (int)(s.b * s.H * (s.N / NR));
     const int xcd = (ng % 8 == 0) ? 1 : 0;
     if constexpr (NR == 256) {
-        if (sp_register_transposed(s)) {
+        if (rt) {
             hipLaunchKernelGGL((state_pass_rt_kernel<Q, 256, kSpRtDepth>), dim3((unsigned)(units * ng)),
                                dim3(256), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT, h0,
                                (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
@@ -1568,25 +1569,29 @@ static hipError_t sp_launch(const Shape &s, const void *x, const void *B, const 
 static int sp_cols(const Shape &s) { return (s.N % 256 == 0) ? 256 : (s.N % 128 == 0) ? 128 : 64; }
 
 template <int Q>
-static hipError_t sp_dispatch_q(const Shape &s, const void *x, const void *B, const float *G2,
-                                const float *wT, const float *h0, void *S, float *hT, float *Ug,
-                                float *gam, float *beta, int K, int ng, hipStream_t st)
+static hipError_t sp_dispatch_q(const Shape &s, int cols, bool rt, const void *x, const void *B,
+                                const float *G2, const float *wT, const float *h0, void *S,
+                                float *hT, float *Ug, float *gam, float *beta, int K, int ng,
+                                hipStream_t st)
 {
-    switch (sp_cols(s)) {
-    case 256: return sp_launch<Q, 256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return sp_launch<Q, 128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return sp_launch<Q, 64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    switch (cols) {
+    case 256: return sp_launch<Q, 256>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_launch<Q, 128>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_launch<Q, 64>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
-static hipError_t sp_dispatch(const Shape &s, const void *x, const void *B, const float *G2,
-                              const float *wT, const float *h0, void *S, float *hT, float *Ug,
-                              float *gam, float *beta, int K, int ng, hipStream_t st)
+// bf16 state pass with `cols` state columns per workgroup (B transposed in registers
+// when rt, cols = 256) over ng groups of K chunks per chain
+static hipError_t sp_dispatch(const Shape &s, int cols, bool rt, const void *x, const void *B,
+                              const float *G2, const float *wT, const float *h0, void *S,
+                              float *hT, float *Ug, float *gam, float *beta, int K, int ng,
+                              hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return sp_dispatch_q<64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return sp_dispatch_q<128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return sp_dispatch_q<256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 64: return sp_dispatch_q<64>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_dispatch_q<128>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_dispatch_q<256>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
@@ -1594,13 +1599,19 @@ hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, 
                                   const float *wT, const float *h0, void *S, float *hT,
                                   hipStream_t st)
 {
-    return sp_dispatch(s, x, B, G2, wT, h0, S, hT, nullptr, nullptr, nullptr, (int)s.nc, 1, st);
+    return sp_dispatch(s, sp_cols(s), sp_register_transposed(s), x, B, G2, wT, h0, S, hT, nullptr,
+                       nullptr, nullptr, (int)s.nc, 1, st);
 }
 
-Grouping state_pass_groups(const Shape &s)
+// Chunks per group and groups per chain for the state pass with `cols` columns per
+// workgroup (B transposed in registers when rt): the cost model of the default plan.
+struct Grouping {
+    int K, ng;
+};
+static Grouping state_pass_groups(const Shape &s, int cols, bool rt)
 {
     Grouping gp;
-    const int64_t units = s.b * s.H * (s.N / (s.bf16 ? sp_cols(s) : 64));
+    const int64_t units = s.b * s.H * (s.N / cols);
     if (!s.bf16) {
         // fp32 (64 columns per workgroup): as many workgroups as the LDS of its Q
         // lets the CUs hold at once
@@ -1620,7 +1631,7 @@ Grouping state_pass_groups(const Shape &s)
     // The scan reads and writes every group's state (~6 bytes per element at
     // ~5 TB/s) and walks the groups in order, eight loads in flight (~1.5 us per
     // eight groups): whichever is longer.
-    const int64_t slots = (sp_register_transposed(s) || sp_cols(s) == 64) ? 512 : 256;
+    const int64_t slots = (rt || cols == 64) ? 512 : 256;
     const double tchunk = (double)s.Q / 64 * 1.2e-6;
     const int64_t ng_max = std::min<int64_t>(s.nc, 8 * slots / units + 1);
     double best = 1e300;
@@ -1644,28 +1655,37 @@ Grouping state_pass_groups(const Shape &s)
     return gp;
 }
 
-hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
+hipError_t launch_state_pass_grouped(const Shape &s, const LaunchPlan &lp, const void *x,
                                      const void *B, const float *G2, const float *wT,
                                      const float *h0, void *S, float *hT, float *Ug, float *gam,
                                      float *beta, hipStream_t st)
 {
-    if (gp.ng <= 1) return launch_state_pass(s, x, B, G2, wT, h0, S, hT, st);
-    return s.bf16 ? sp_dispatch(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, gp.K, gp.ng, st)
-                  : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta, gp.K,
-                                                  gp.ng, st);
+    const int K = lp.sp_group_chunks, ng = lp.sp_groups;
+    if (!s.bf16)
+        return ng <= 1 ? launch_state_pass(s, x, B, G2, wT, h0, S, hT, st)
+                       : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta, K,
+                                                       ng, st);
+    const bool rt = lp.sp_register_transposed != 0;
+    if (ng <= 1)
+        return sp_dispatch(s, lp.sp_columns, rt, x, B, G2, wT, h0, S, hT, nullptr, nullptr,
+                           nullptr, (int)s.nc, 1, st);
+    return sp_dispatch(s, lp.sp_columns, rt, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K, ng,
+                       st);
 }
 
-hipError_t launch_group_scan(const Shape &s, const Grouping &gp, float *hT, float *Ug, void *Hb,
+hipError_t launch_group_scan(const Shape &s, const LaunchPlan &lp, float *hT, float *Ug, void *Hb,
                              const float *gam, hipStream_t st)
 {
-    if (gp.ng <= 1) return hipSuccess;   // one serial chain: the state pass wrote hT itself
+    const int K = lp.sp_group_chunks, ng = lp.sp_groups;
+    if (ng <= 1) return hipSuccess;   // one serial chain: the state pass wrote hT itself
     const int PN = (int)(s.P * s.N);
     dim3 grid((unsigned)((PN / 4 + 255) / 256), (unsigned)(s.b * s.H));
-    // fp32 group-start states are read only by single-head chunk-output launches
+    // fp32 group-start states are read only by one-head chunk-output launches: with the
+    // head-blocked kernel, only the ragged last chunk's group (none when L % Q == 0)
     int g_f32 = 1;
-    if (s.bf16 && head_blocked(s)) g_f32 = (s.L % s.Q != 0) ? (int)((s.nc - 1) / gp.K) : gp.ng;
+    if (s.bf16 && lp.co_head_blocked) g_f32 = (s.L % s.Q != 0) ? (int)((s.nc - 1) / K) : ng;
     hipLaunchKernelGGL(group_scan_kernel<8>, grid, dim3(256), 0, st, Ug, gam, hT,
-                       s.bf16 ? (bf16 *)Hb : (bf16 *)nullptr, PN, gp.ng, g_f32);
+                       s.bf16 ? (bf16 *)Hb : (bf16 *)nullptr, PN, ng, g_f32);
     return hipGetLastError();
 }
 
@@ -1725,55 +1745,145 @@ static int heads_per_block(const Shape &s)
     return best;
 }
 
+// The plan of the given choices with its derived fields; false when a workgroup count
+// or a grid's work-item count (32 bits in the dispatch packet) does not fit.
+static bool plan_from(const Shape &s, int K, int ng, int cols, int rt, int co_hb, int hb,
+                      LaunchPlan &lp)
+{
+    const int64_t sp_wg = s.b * s.H * (s.N / cols) * ng;
+    const int sp_threads = !s.bf16 ? 256 : rt ? 256 : (cols == 64 ? 256 : 512);
+    int64_t co_wg, co_threads;
+    int split = 1;
+    if (co_hb) {
+        const int64_t nc_full = s.L / s.Q;
+        split = s.N > 256 ? 2 : 1;
+        co_wg = nc_full * s.b * s.G * (s.H / s.G / hb) + (nc_full < s.nc ? s.b * s.H : 0);
+        co_threads = 2 * s.Q * split;
+    } else {
+        hb = 1;
+        co_wg = s.nc * s.b * s.H;
+        co_threads = s.bf16 ? 2 * s.Q : chunk_out_f32_threads(s);
+    }
+    const int64_t lim = int64_t(1) << 32;
+    if (sp_wg * sp_threads >= lim || co_wg * co_threads >= lim) return false;
+    lp.sp_group_chunks = K;
+    lp.sp_groups = ng;
+    lp.sp_columns = cols;
+    lp.sp_workgroups = (int)sp_wg;
+    lp.scan = ng > 1 ? 1 : 0;
+    lp.co_head_blocked = co_hb;
+    lp.co_heads_per_block = hb;
+    lp.co_column_split = split;
+    lp.co_workgroups = (int)co_wg;
+    lp.co_threads = (int)co_threads;
+    lp.sp_register_transposed = rt;
+    lp.sp_threads = sp_threads;
+    return true;
+}
+
+static bool plan_same(const LaunchPlan &a, const LaunchPlan &b)
+{
+    return a.sp_group_chunks == b.sp_group_chunks && a.sp_groups == b.sp_groups &&
+           a.sp_columns == b.sp_columns && a.sp_workgroups == b.sp_workgroups &&
+           a.scan == b.scan && a.co_head_blocked == b.co_head_blocked &&
+           a.co_heads_per_block == b.co_heads_per_block &&
+           a.co_column_split == b.co_column_split && a.co_workgroups == b.co_workgroups &&
+           a.co_threads == b.co_threads && a.sp_register_transposed == b.sp_register_transposed &&
+           a.sp_threads == b.sp_threads;
+}
+
 LaunchPlan plan_of(const Shape &s)
 {
+    const int cols = s.bf16 ? sp_cols(s) : 64;
+    const bool rt = s.bf16 && sp_register_transposed(s);
+    const Grouping gp = state_pass_groups(s, cols, rt);
+    const bool hbk = s.bf16 && head_blocked(s);
+    // fits for every shape the C ABI accepts: its checks bound the one-head output grid,
+    // the largest of these launches, to 2^32 work-items
     LaunchPlan lp;
-    const Grouping gp = state_pass_groups(s);
-    lp.sp_group_chunks = gp.K;
-    lp.sp_groups = gp.ng;
-    if (!s.bf16) {   // fp32 kernels: 64 columns per state-pass workgroup, one (chunk, head) per output workgroup
-        lp.sp_columns = 64;
-        lp.sp_workgroups = (int)(s.b * s.H * (s.N / 64) * gp.ng);
-        lp.sp_register_transposed = 0;
-        lp.sp_threads = 256;
-        lp.scan = gp.ng > 1 ? 1 : 0;
-        lp.co_head_blocked = 0;
-        lp.co_heads_per_block = 1;
-        lp.co_column_split = 1;
-        lp.co_workgroups = (int)(s.nc * s.b * s.H);
-        lp.co_threads = chunk_out_f32_threads(s);
-        return lp;
-    }
-    lp.sp_columns = sp_cols(s);
-    lp.sp_workgroups = (int)(s.b * s.H * (s.N / lp.sp_columns) * gp.ng);
-    lp.sp_register_transposed = sp_register_transposed(s) ? 1 : 0;
-    lp.sp_threads = lp.sp_register_transposed ? 256 : (lp.sp_columns == 64 ? 256 : 512);
-    lp.scan = gp.ng > 1 ? 1 : 0;
-    lp.co_head_blocked = head_blocked(s) ? 1 : 0;
-    if (lp.co_head_blocked) {
-        const int64_t nc_full = s.L / s.Q;
-        lp.co_heads_per_block = heads_per_block(s);
-        lp.co_column_split = s.N > 256 ? 2 : 1;
-        lp.co_workgroups = (int)(nc_full * s.b * s.G * (s.H / s.G / lp.co_heads_per_block) +
-                                 (nc_full < s.nc ? s.b * s.H : 0));
-        lp.co_threads = (int)(2 * s.Q * lp.co_column_split);
-    } else {
-        lp.co_heads_per_block = 1;
-        lp.co_column_split = 1;
-        lp.co_workgroups = (int)(s.nc * s.b * s.H);
-        lp.co_threads = (int)(2 * s.Q);
-    }
+    plan_from(s, gp.K, gp.ng, cols, rt ? 1 : 0, hbk ? 1 : 0, hbk ? heads_per_block(s) : 1, lp);
     return lp;
+}
+
+bool plan_valid(const Shape &s, const LaunchPlan &lp)
+{
+    const int64_t K = lp.sp_group_chunks;
+    if (K < 1 || K > s.nc || lp.sp_groups != (s.nc + K - 1) / K) return false;
+    if (s.bf16) {
+        if (lp.sp_columns != 64 && lp.sp_columns != 128 && lp.sp_columns != 256) return false;
+        if (s.N % lp.sp_columns != 0) return false;
+        if (lp.sp_register_transposed != 0 && (lp.sp_register_transposed != 1 || lp.sp_columns != 256))
+            return false;
+        if (lp.co_head_blocked != 0) {
+            if (lp.co_head_blocked != 1 || !head_blocked(s)) return false;
+            if (lp.co_heads_per_block < 1 || (s.H / s.G) % lp.co_heads_per_block != 0) return false;
+        }
+    } else if (lp.sp_columns != 64 || lp.sp_register_transposed != 0 || lp.co_head_blocked != 0) {
+        return false;
+    }
+    LaunchPlan ref;
+    return plan_from(s, (int)K, lp.sp_groups, lp.sp_columns, lp.sp_register_transposed,
+                     lp.co_head_blocked, lp.co_heads_per_block, ref) &&
+           plan_same(ref, lp);
+}
+
+int plan_candidates(const Shape &s, LaunchPlan *out, int cap)
+{
+    std::vector<LaunchPlan> all;
+    auto push = [&](const LaunchPlan &lp) {
+        for (const LaunchPlan &q : all)
+            if (plan_same(q, lp)) return;
+        all.push_back(lp);
+    };
+    push(plan_of(s));
+    // state-pass kernels: (columns per workgroup, B transposed in registers)
+    std::vector<std::pair<int, int>> kernels;
+    if (s.bf16) {
+        for (int cols : {256, 128, 64}) {
+            if (s.N % cols != 0) continue;
+            kernels.push_back({cols, 0});
+            if (cols == 256) kernels.push_back({cols, 1});
+        }
+    } else {
+        kernels.push_back({64, 0});
+    }
+    // chunk-output kernels: (head-blocked, heads per workgroup)
+    std::vector<std::pair<int, int>> outs;
+    if (s.bf16 && head_blocked(s)) {
+        const int64_t hpg = s.H / s.G;
+        for (int64_t hb = 1; hb <= std::min<int64_t>(hpg, 64); ++hb)
+            if (hpg % hb == 0) outs.push_back({1, (int)hb});
+    }
+    outs.push_back({0, 1});
+    for (const auto &kr : kernels) {
+        // group counts: the cost model's for this kernel, then 1, 2, 3, 4, 6, 8, ... chunks
+        // apart as far as the chain has chunks
+        std::vector<Grouping> groups;
+        groups.push_back(state_pass_groups(s, kr.first, kr.second != 0));
+        for (int64_t g : {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128}) {
+            if (g > s.nc) break;
+            const int64_t K = (s.nc + g - 1) / g;
+            groups.push_back({(int)K, (int)((s.nc + K - 1) / K)});
+        }
+        for (const Grouping &gp : groups)
+            for (const auto &co : outs) {
+                LaunchPlan lp;
+                if (plan_from(s, gp.K, gp.ng, kr.first, kr.second, co.first, co.second, lp))
+                    push(lp);
+            }
+    }
+    const int n = (int)all.size();
+    for (int i = 0; i < std::min(n, cap); ++i) out[i] = all[i];
+    return n;
 }
 
 template <int Q, int NN>
 static hipError_t hb_launch(const Shape &s, const void *x, const void *B, const void *C,
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, const void *Hb, const float *beta, int K, int ng, int nc_full,
-                            hipStream_t st)
+                            int HB, hipStream_t st)
 {
     constexpr int SPL = NN > 256 ? 2 : 1;
-    const int HB = heads_per_block(s);
     const int xcd = (nc_full % 8 == 0) ? 1 : 0;
     const dim3 grid((unsigned)(nc_full * s.b * s.G * (s.H / s.G / HB))), block(2 * Q * SPL);
     if (Hb != nullptr)
@@ -1792,17 +1902,17 @@ static hipError_t hb_launch(const Shape &s, const void *x, const void *B, const 
 template <int Q>
 static hipError_t hb_dispatch_q(const Shape &s, const void *x, const void *B, const void *C,
                                 const float *G2, const float *dtT, const void *S, const float *D,
-                                void *y, const void *Hb, const float *beta, int K, int ng,
+                                void *y, const void *Hb, const float *beta, int K, int ng, int HB,
                                 hipStream_t st)
 {
     const int nc_full = (int)(s.L / s.Q);
     switch (s.N) {
-    case 64: return hb_launch<Q, 64>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
-    case 128: return hb_launch<Q, 128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
-    case 256: return hb_launch<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+    case 64: return hb_launch<Q, 64>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, HB, st);
+    case 128: return hb_launch<Q, 128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, HB, st);
+    case 256: return hb_launch<Q, 256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, HB, st);
     default:
         if constexpr (Q == 128)
-            return hb_launch<Q, 512>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, st);
+            return hb_launch<Q, 512>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, nc_full, HB, st);
         return hipErrorInvalidValue;   // not head-blocked: never dispatched here
     }
 }
@@ -1811,7 +1921,7 @@ static hipError_t hb_dispatch_q(const Shape &s, const void *x, const void *B, co
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
                                  void *y, const float *Hg, const void *Hb, const float *beta, int K,
-                                 int ng, hipStream_t st)
+                                 int ng, int hb, hipStream_t st)
 {
     auto single = [&](int c_first, int nc_grid) {
         switch (s.Q) {
@@ -1820,13 +1930,13 @@ hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, c
         default: return co_launch<256>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, c_first, nc_grid, st);
         }
     };
-    if (!head_blocked(s)) return single(0, (int)s.nc);
-    // full chunks head-blocked, a ragged last chunk on the single-head kernel
+    if (hb <= 0 || !head_blocked(s)) return single(0, (int)s.nc);
+    // full chunks head-blocked, a ragged last chunk on the one-head kernel
     const int nc_full = (int)(s.L / s.Q);
     hipError_t e = hipSuccess;
     if (nc_full > 0) {
-        e = (s.Q == 128) ? hb_dispatch_q<128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, st)
-                         : hb_dispatch_q<256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, st);
+        e = (s.Q == 128) ? hb_dispatch_q<128>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, hb, st)
+                         : hb_dispatch_q<256>(s, x, B, C, G2, dtT, S, D, y, Hb, beta, K, ng, hb, st);
         if (e != hipSuccess) return e;
     }
     if (nc_full < s.nc) e = single(nc_full, 1);

@@ -542,20 +542,34 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, hipStream_t st)
 {
-    return s.bf16 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, nullptr,
-                                          (int)s.nc, 1, st)
-                  : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, (int)s.nc, 1, st);
+    if (!s.bf16)
+        return chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, (int)s.nc, 1, st);
+    const LaunchPlan lp = plan_of(s);
+    return launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, nullptr,
+                                 (int)s.nc, 1, lp.co_head_blocked ? lp.co_heads_per_block : 0, st);
 }
 
-hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const void *x,
+hipError_t launch_chunk_out_corrected(const Shape &s, const LaunchPlan &lp, const void *x,
                                       const void *B, const void *C, const float *G2,
                                       const float *dtT, const void *S, const float *D, void *y,
                                       const float *Hg, const void *Hb, const float *beta,
                                       hipStream_t st)
 {
-    if (gp.ng <= 1) return launch_chunk_out(s, x, B, C, G2, dtT, S, D, y, st);
-    if (!s.bf16) return chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, gp.K, gp.ng, st);
-    return launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, Hg, Hb, beta, gp.K, gp.ng, st);
+    const int K = lp.sp_group_chunks, ng = lp.sp_groups;
+    const int hb = lp.co_head_blocked ? lp.co_heads_per_block : 0;
+    if (ng <= 1) {
+        Hg = nullptr;
+        Hb = nullptr;
+        beta = nullptr;
+    }
+    if (!s.bf16)
+        return ng <= 1 ? chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr,
+                                            (int)s.nc, 1, st)
+                       : chunk_out_t<float>(s, x, B, C, G2, dtT, S, D, y, Hg, beta, K, ng, st);
+    return ng <= 1 ? launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, nullptr, nullptr, nullptr,
+                                           (int)s.nc, 1, hb, st)
+                   : launch_chunk_out_bf16(s, x, B, C, G2, dtT, S, D, y, Hg, Hb, beta, K, ng, hb,
+                                           st);
 }
 
 }  // namespace ssd

@@ -27,18 +27,32 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
                             const float *G2, const float *dtT, const void *S, const float *D,
                             void *y, hipStream_t st);
 
-// Split of each serial state chain into ng groups of K chunks (ng = 1: one chain).
-struct Grouping {
-    int K, ng;
+// The launch configuration of the forward pass (host only): the state pass's kernel
+// (state columns per workgroup, B transposed in registers or through LDS), the split of
+// each serial chain of chunks into sp_groups groups of sp_group_chunks chunks (1 group:
+// one chain), and the chunk output's kernel (head-blocked with co_heads_per_block heads
+// per workgroup, or one head per workgroup); the other fields follow from these.
+struct LaunchPlan {
+    int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
+    int co_head_blocked, co_heads_per_block, co_column_split, co_workgroups, co_threads;
+    int sp_register_transposed, sp_threads;
 };
-Grouping state_pass_groups(const Shape &s);
+// The cost model's choice for shape s.
+LaunchPlan plan_of(const Shape &s);
+// Every configuration of the search space for shape s, plan_of(s) first; writes at most
+// cap of them and returns how many there are.
+int plan_candidates(const Shape &s, LaunchPlan *out, int cap);
+// True when lp is a configuration the kernels can run for s: its choices are among the
+// kernels' supported ones (any chunks per group from 1 to nc) and its derived fields are
+// the ones these choices give.
+bool plan_valid(const Shape &s, const LaunchPlan &lp);
 
-// Grouped state pass as used by the forward pass: with ng > 1, S receives
+// Grouped state pass as used by the forward pass: with lp.sp_groups > 1, S receives
 // chunk-start states relative to their group, Ug the final local state of each
 // group, gam each group's decay and beta the per-chunk decay since the group
-// start; with ng == 1 it is the plain state pass (true states, hT written).
-// launch_group_scan then (ng > 1 only) turns Ug into the true group-start states
-// H_g and writes hT.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng], beta [b*H, nc],
+// start; with one group it is the plain state pass (true states, hT written).
+// launch_group_scan then (more than one group only) turns Ug into the true group-start
+// states H_g and writes hT.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng], beta [b*H, nc],
 // all fp32, and for bf16 problems Hb [b*H, ng, P, N] bf16 (H_g rounded, zeros for
 // group 0).
 // fp32 state pass over ng groups of K chunks (ssd_kernels.hip): local chunk-start
@@ -47,16 +61,16 @@ hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const vo
                                          const float *G2, const float *wT, const float *h0,
                                          void *S, float *Ug, float *gam, float *beta, int K,
                                          int ng, hipStream_t st);
-hipError_t launch_state_pass_grouped(const Shape &s, const Grouping &gp, const void *x,
+hipError_t launch_state_pass_grouped(const Shape &s, const LaunchPlan &lp, const void *x,
                                      const void *B, const float *G2, const float *wT,
                                      const float *h0, void *S, float *hT, float *Ug, float *gam,
                                      float *beta, hipStream_t st);
-hipError_t launch_group_scan(const Shape &s, const Grouping &gp, float *hT, float *Ug, void *Hb,
+hipError_t launch_group_scan(const Shape &s, const LaunchPlan &lp, float *hT, float *Ug, void *Hb,
                              const float *gam, hipStream_t st);
 
 // Chunk output that adds beta_c H_g to the handed-over chunk-start states
-// (Hg == NULL: S already holds true states).  Hg is fp32, Hb its bf16 copy.
-hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const void *x,
+// (one group: S already holds true states).  Hg is fp32, Hb its bf16 copy.
+hipError_t launch_chunk_out_corrected(const Shape &s, const LaunchPlan &lp, const void *x,
                                       const void *B, const void *C, const float *G2,
                                       const float *dtT, const void *S, const float *D, void *y,
                                       const float *Hg, const void *Hb, const float *beta,
@@ -67,14 +81,6 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const Grouping &gp, const 
 // side), else Q (Q/64 waves with two row tiles each).
 int chunk_out_f32_threads(const Shape &s);
 
-// The launch configuration of the forward pass for shape s (host only).
-struct LaunchPlan {
-    int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
-    int co_head_blocked, co_heads_per_block, co_column_split, co_workgroups, co_threads;
-    int sp_register_transposed, sp_threads;
-};
-LaunchPlan plan_of(const Shape &s);
-
 // One decode step per (batch, head), h updated in place (ssd_step.hip).
 hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, float *h, void *y,
@@ -84,9 +90,11 @@ hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, con
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
                                   const float *wT, const float *h0, void *S, float *hT,
                                   hipStream_t st);
+// hb: heads per head-blocked workgroup for the full chunks (0: every chunk on the
+// one-head kernel)
 hipError_t launch_chunk_out_bf16(const Shape &s, const void *x, const void *B, const void *C,
                                  const float *G2, const float *dtT, const void *S, const float *D,
                                  void *y, const float *Hg, const void *Hb, const float *beta, int K,
-                                 int ng, hipStream_t st);
+                                 int ng, int hb, hipStream_t st);
 
 }  // namespace ssd

@@ -163,7 +163,7 @@ def test_step_validates_before_launching(kw, status):
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert ssd.ssd_status_string(s)
     assert "unknown" in ssd.ssd_status_string(42)
 
@@ -267,6 +267,130 @@ def test_launch_plan_per_shape():
     # the one-head output kernel's workgroup count
     (dict(batch=9362, nheads=7, ngroups=7, seqlen=(1 << 21) + 192, dstate=64, chunk=64), 3),
     (dict(batch=9362, nheads=7, ngroups=7, seqlen=1 << 15, dstate=64, chunk=64), 0),
+    # ... and its work-items (2 * chunk per workgroup), counted in 32 bits
+    (dict(batch=8192, nheads=1, seqlen=256 * 1024, dstate=64, chunk=256), 3),
+    (dict(batch=8192, nheads=1, seqlen=256 * 1023, dstate=64, chunk=256), 0),
 ])
 def test_validate_size_limits(kw, status):
     assert ssd.ssd_validate(_p(**kw)) == status
+
+
+PLAN_SHAPES = [
+    dict(),                                                     # headline
+    dict(seqlen=65536, dstate=512, chunk=128),
+    dict(batch=2, seqlen=2048, nheads=24, dstate=128),
+    dict(seqlen=262144, nheads=16, ngroups=2, dstate=128),
+    dict(seqlen=700, nheads=4, ngroups=2, dstate=384, chunk=128),
+    dict(seqlen=300, nheads=3, dstate=64, chunk=64),
+    dict(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"),
+    dict(seqlen=1, nheads=2, dstate=512, chunk=256),
+]
+
+
+@pytest.mark.parametrize("kw", PLAN_SHAPES)
+def test_plan_candidates(kw):
+    """The search space of the launch configuration (host only): ssd_plan's choice first,
+    no duplicates, every candidate valid with a workspace size, the documented choices."""
+    p = _p(**kw)
+    cands = ssd.plan_candidates(p)
+    assert cands[0] == ssd.ssd_plan(p)
+    keys = [tuple(sorted(c.items())) for c in cands]
+    assert len(set(keys)) == len(keys)
+    nc = p.nchunks
+    for c in cands:
+        assert ssd.ssd_workspace_bytes_planned(p, c) > 0
+        K, ng = c["sp_group_chunks"], c["sp_groups"]
+        assert 1 <= K <= nc and ng == -(-nc // K) and c["scan"] == (ng > 1)
+        assert p.dstate % c["sp_columns"] == 0
+        assert c["sp_workgroups"] == p.batch * p.nheads * (p.dstate // c["sp_columns"]) * ng
+        if c["sp_register_transposed"]:
+            assert c["sp_columns"] == 256 and c["sp_threads"] == 256
+        if c["co_head_blocked"]:
+            assert (p.nheads // p.ngroups) % c["co_heads_per_block"] == 0
+        else:
+            assert c["co_heads_per_block"] == 1 and c["co_workgroups"] == nc * p.batch * p.nheads
+    # the groupings: 1, 2, 3, 4, 6, 8, ... groups as far as the chain has chunks
+    groups = {c["sp_groups"] for c in cands}
+    for g in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128):
+        if g <= nc:
+            assert -(-nc // -(-nc // g)) in groups
+    if p.dtype == binding.SSD_F32:
+        assert {(c["sp_columns"], c["sp_register_transposed"], c["co_head_blocked"]) for c in cands} == {(64, 0, 0)}
+    else:
+        kinds = {(c["sp_columns"], c["sp_register_transposed"]) for c in cands}
+        want = {(cols, 0) for cols in (64, 128, 256) if p.dstate % cols == 0}
+        want |= {(256, 1)} if p.dstate % 256 == 0 else set()
+        assert kinds == want
+    # the workspace follows the grouping
+    one = [c for c in cands if c["sp_groups"] == 1]
+    assert one and ssd.ssd_workspace_bytes_planned(p, one[0]) <= min(
+        ssd.ssd_workspace_bytes_planned(p, c) for c in cands)
+
+
+def test_plan_candidates_capacity():
+    lib = binding.lib()
+    p = _p()
+    count = ctypes.c_int32(-1)
+    assert lib.ssd_plan_candidates(ctypes.byref(p), None, 0, ctypes.byref(count)) == 0
+    n = count.value
+    assert n > 10
+    arr = (binding.SsdLaunchPlan * 3)()
+    assert lib.ssd_plan_candidates(ctypes.byref(p), arr, 3, ctypes.byref(count)) == 0
+    assert count.value == n
+    assert {f: getattr(arr[0], f) for f, _ in binding.SsdLaunchPlan._fields_} == ssd.ssd_plan(p)
+    assert lib.ssd_plan_candidates(ctypes.byref(p), None, 3, ctypes.byref(count)) == 1
+    assert lib.ssd_plan_candidates(ctypes.byref(p), arr, -1, ctypes.byref(count)) == 1
+    assert lib.ssd_plan_candidates(ctypes.byref(p), arr, 3, None) == 1
+    assert lib.ssd_plan_candidates(ctypes.byref(_p(dstate=96)), arr, 3, ctypes.byref(count)) == 3
+
+
+def _altered(plan, **kw):
+    q = dict(plan)
+    q.update(kw)
+    return q
+
+
+def test_invalid_plans_rejected_without_launching():
+    """A plan the kernels cannot run is refused with SSD_ERR_PLAN before any launch, and
+    has no workspace size (host only: fake device pointers are never touched)."""
+    lib = binding.lib()
+    p = _p()
+    d = ssd.ssd_plan(p)
+    bad = [
+        _altered(d, sp_columns=96),
+        _altered(d, sp_columns=512),
+        _altered(d, sp_register_transposed=1, sp_columns=128, sp_workgroups=d["sp_workgroups"] * 2),
+        _altered(d, sp_group_chunks=0),
+        _altered(d, sp_group_chunks=65),
+        _altered(d, sp_groups=7),                      # not ceil(nc / K)
+        _altered(d, sp_workgroups=d["sp_workgroups"] + 1),
+        _altered(d, co_heads_per_block=3),             # does not divide the heads per group
+        _altered(d, co_threads=256),
+        _altered(d, scan=0),
+        _altered(d, co_head_blocked=2),
+    ]
+    fake = ctypes.c_void_p(256)
+    for q in bad:
+        assert ssd.ssd_workspace_bytes_planned(p, q) == 0, q
+        st = lib.ssd_forward_planned(ctypes.byref(p), ctypes.byref(binding._plan_struct(q)),
+                                     *([fake] * 6), None, fake, None, fake, 10**12, 0, 3, None, None)
+        assert st == 8, q
+    # the one-head kernel for 64-token chunks only; fp32 takes no other state-pass kernel
+    p64 = _p(chunk=64)
+    d64 = ssd.ssd_plan(p64)
+    assert ssd.ssd_workspace_bytes_planned(p64, _altered(d64, co_head_blocked=1)) == 0
+    pf = _p(dtype="fp32", dstate=128, chunk=64)
+    df = ssd.ssd_plan(pf)
+    assert ssd.ssd_workspace_bytes_planned(pf, _altered(df, sp_columns=128,
+                                                        sp_workgroups=df["sp_workgroups"] // 2)) == 0
+    # a valid plan other than the default, and the NULL plan, pass the checks and stop at
+    # the next one (workspace too small)
+    other = [c for c in ssd.plan_candidates(p) if c != d][0]
+    for q in (ctypes.byref(binding._plan_struct(other)), None):
+        assert lib.ssd_forward_planned(ctypes.byref(p), q, *([fake] * 6), None, fake, None, fake,
+                                       100, 0, 3, None, None) == 4
+    # stage range
+    for first, last in ((-1, 3), (0, 4), (3, 2)):
+        assert lib.ssd_forward_planned(ctypes.byref(p), None, *([fake] * 6), None, fake, None,
+                                       fake, 10**12, first, last, None, None) == 3
+    assert lib.ssd_last_hip_error() == 0
