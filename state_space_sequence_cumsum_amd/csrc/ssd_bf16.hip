@@ -1128,26 +1128,24 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     constexpr int NSW = NN < NS ? NN : NS;      // slice width
     constexpr int NIT = NSL / SPL;              // slice steps (SPL slices staged per step)
     constexpr int NF = NN / 16 / SPL;           // C fragments per lane (its column half)
-    constexpr int XP = Q + 8, BP = frag_pitch(NSW), SFP = NN + 8;
-    constexpr int SLICE_EL = Q * (NSW / 8);     // 16-byte pieces of one B slice
-    constexpr int BPC = SPL * SLICE_EL / NTHR;  // 16-byte B pieces per thread per step
+    constexpr int XP = Q + 8, SFP = NN + 8;
     constexpr int SPT = P * (NN / 8) / NTHR;    // 16-byte S pieces per thread
     // the next head's S (and H_g) pieces are requested before the decay products when
     // they take at most 32 registers per thread, else after them
     constexpr bool EARLY_S = SPL == 1 && SPT * (CORR ? 2 : 1) <= 8;
-    static_assert(BPC >= 1 && SPT >= 1 && NN % 16 == 0 && NSL % SPL == 0, "staging cover");
+    static_assert(SPT >= 1 && NN % 16 == 0 && NSL % SPL == 0 && NSW == 64, "staging cover");
     static_assert(SPL == 1 || SPL == 2, "one or two column halves");
     constexpr int NTILE = NI * (NI + 1) / 2;    // causal tiles
     constexpr int CB_EL = NTILE * 32 * 32;      // bf16 C B^T tiles
     constexpr int XC_EL = SPL == 2 ? NW * 2 * 1024 * 2 : 0;   // fp32 partial-Y swap area
-    constexpr int U_EL = (SPL * Q * BP > CB_EL + XC_EL) ? SPL * Q * BP : CB_EL + XC_EL;
+    constexpr int U_EL = CB_EL + XC_EL;
     static_assert(SPL == 1 || 4 * CB_EL <= 2 * P * SFP, "partial C B^T fits the S area");
     // raw x^T [p][position] (token order permuted within 16-token groups: the
     // middle two 4-token blocks swapped, so the accumulator token order of a lane
-    // becomes 8 consecutive positions); Un holds the B slices during C B^T and then
-    // the bf16 C B^T tiles: tile (I, J) at (I(I+1)/2 + J) * 1024 elements, lane l's
-    // elements 0..7 at 8 l and 8..15 at 512 + 8 l, followed (SPL = 2) by the
-    // partial-Y swap area
+    // becomes 8 consecutive positions); Un holds the bf16 C B^T tiles: tile (I, J) at
+    // (I(I+1)/2 + J) * 1024 elements, lane l's elements 0..7 at 8 l and 8..15 at
+    // 512 + 8 l, followed (SPL = 2) by the partial-Y swap area.  During the C B^T
+    // products Un, Sf and Xd hold the B slices instead.
     __shared__ __attribute__((aligned(16))) bf16 Xd[P * XP];
     __shared__ __attribute__((aligned(16))) bf16 Un[U_EL];
     __shared__ __attribute__((aligned(16))) bf16 Sf[P * SFP];
@@ -1155,7 +1153,8 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     __shared__ __attribute__((aligned(16))) float Wd[Q];   // exp2(G_e - G_j) dt_j
     __shared__ __attribute__((aligned(16))) float Dt[Q];   // dt_j
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile loops
     const int hf = SPL == 1 ? 0 : w / NW;      // column half
     const int wi = SPL == 1 ? w : w % NW;      // wave within the half
     const int I = (wi < NW / 2) ? wi : NW - 1 - (wi - NW / 2);
@@ -1193,45 +1192,55 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
 #pragma unroll
         for (int f = 0; f < NF; ++f)
             cfa[f] = *reinterpret_cast<const bf16x8 *>(Cb + (uint32_t)(crow_off + f * 32));
-        // step it stages slice it + s NIT (s < SPL) at Un + s Q BP: half s's columns
-        int bo[BPC];
-#pragma unroll
-        for (int r = 0; r < BPC; ++r) {
-            const int id = tid + NTHR * r, sh = id / SLICE_EL, i2 = id % SLICE_EL;
-            const int t = i2 / (NSW / 8), oc = i2 % (NSW / 8);
-            bo[r] = t * brow + oc * 16 + sh * NIT * NSW * 2;
-        }
-        bf16x8 bq[BPC];
-        auto load_b = [&](int n0) {
-#pragma unroll
-            for (int r = 0; r < BPC; ++r) bq[r] = *reinterpret_cast<const bf16x8 *>(Bb + (uint32_t)(bo[r] + n0 * 2));
+        // Every B slice [Q tokens][64 columns] goes to LDS by 16-byte global-to-LDS loads
+        // before the first product: the slices fill Un, then Sf, then Xd (both free until
+        // the first head is staged), unpadded, with 16-byte unit u of row r stored at unit
+        // u ^ ((r >> 1) & 7), so that the 16 rows of a quarter-wave operand read fall in
+        // 16 different bank groups.  One load instruction covers 8 rows (1 KB).
+        constexpr int SL_EL = Q * NSW;
+        constexpr int IN_UN = U_EL / SL_EL, IN_SF = P * SFP / SL_EL, IN_XD = P * XP / SL_EL;
+        static_assert(IN_UN + IN_SF + IN_XD >= NSL, "every B slice fits the LDS free before the heads");
+        constexpr int IPS = Q / 8, NWV = NTHR / 64;
+        static_assert((NSL * IPS) % NWV == 0, "B load cover");
+        auto slice_base = [&](int sl) -> bf16 * {
+            return sl < IN_UN ? Un + sl * SL_EL
+                              : (sl < IN_UN + IN_SF ? Sf + (sl - IN_UN) * SL_EL
+                                                    : Xd + (sl - IN_UN - IN_SF) * SL_EL);
         };
+        {
+            const rsrc_t br = make_rsrc(Bb, Q * brow);
+            const int rl = lane >> 3, ul = lane & 7;
+#pragma unroll
+            for (int kk = 0; kk < NSL * IPS / NWV; ++kk) {
+                const int k = kk * NWV + w, sl = k / IPS, ki = k % IPS;
+                const int row = ki * 8 + rl;
+                const int u = ul ^ ((row >> 1) & 7);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    br, (lds_void *)(slice_base(sl) + ki * 8 * NSW), 16,
+                    row * brow + (sl * NSW + 8 * u) * 2, 0, 0, 0);
+            }
+        }
         f32x16 cb[NI];
 #pragma unroll
         for (int J = 0; J < NI; ++J) cb[J] = zero_acc();
-        load_b(0);
+        __syncthreads();   // every slice has landed (the barrier waits for this wave's loads)
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            __syncthreads();   // previous slices consumed
-#pragma unroll
-            for (int r = 0; r < BPC; ++r) {
-                const int id = tid + NTHR * r, sh = id / SLICE_EL, i2 = id % SLICE_EL;
-                const int t = i2 / (NSW / 8), oc = i2 % (NSW / 8);
-                *reinterpret_cast<bf16x8 *>(&Un[sh * Q * BP + t * BP + oc * 8]) = bq[r];
-            }
-            if (it + 1 < NIT) load_b((it + 1) * NSW);
-            __syncthreads();
+            const bf16 *sb = slice_base(hf * NIT + it);
 #pragma unroll
             for (int J = 0; J < NI; ++J) {
                 if (J <= I) {
-                    const bf16 *brw = Un + hf * Q * BP + (J * 32 + (lane & 31)) * BP + kq;
+                    const int row = J * 32 + (lane & 31);
+                    const bf16 *rp = sb + row * NSW;
 #pragma unroll
-                    for (int ks = 0; ks < NSW / 16; ++ks)
-                        mma(cb[J], *reinterpret_cast<const bf16x8 *>(brw + ks * 16), cfa[it * (NSW / 16) + ks]);
+                    for (int ks = 0; ks < NSW / 16; ++ks) {
+                        const int u = ((lane >> 5) + 2 * ks) ^ ((row >> 1) & 7);
+                        mma(cb[J], *reinterpret_cast<const bf16x8 *>(rp + 8 * u), cfa[it * (NSW / 16) + ks]);
+                    }
                 }
             }
         }
-        __syncthreads();   // the B slice area becomes the C B^T store
+        __syncthreads();   // slices consumed: Un becomes the C B^T store, Sf and Xd free
         if constexpr (SPL == 2) {
             // half 1 hands its partial C B^T (fp32) to half 0 through the S area
             float *pcb = reinterpret_cast<float *>(Sf) + (I * (I + 1) / 2) * 1024 + 4 * lane;
@@ -1282,7 +1291,7 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     // two 4-column halves of one 8-column block
     const int tg = (wi >> 1) * 8 + (lane & 7), cg = (wi & 1) * 8 + 2 * ((lane >> 3) & 3) + (lane >> 5);
     struct XRegs {
-        u32x2 xv[8];
+        u32x4 raw[4];   // the four 16-byte x loads as they arrive (lanes swapped at staging)
         float gt, ge, dt;
     };
     struct SRegs {
@@ -1296,20 +1305,13 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
         const int h = h_first + hl, bh = b * H + h;
         const char *xbb = reinterpret_cast<const char *>(x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P);
         // 16-byte loads: lane l reads tokens 0..3 of the group, lane l + 32 tokens 4..7, both
-        // the whole 8-column block; swapping the upper and lower 32 lanes leaves lane l with
-        // columns 0..3 and lane l + 32 with columns 4..7 of all 8 tokens
+        // the whole 8-column block (rearranged by stage_head, so that nothing here waits
+        // for them)
         const int c8 = (cg & ~1) * 4, tsel = 4 * (lane >> 5);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+        for (int r = 0; r < 4; ++r)
+            R.raw[r] = *reinterpret_cast<const u32x4 *>(
                 xbb + (uint32_t)(((tg * 8 + tsel + r) * (int)xstride + c8) * 2));
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(v[d], v[2 + d], false, false);
-                R.xv[r][d] = sw[0];
-                R.xv[4 + r][d] = sw[1];
-            }
-        }
         const float *Gh = G2 + (int64_t)bh * Lp + t0;
         R.gt = Gh[tq];
         R.ge = Gh[tq | 31];
@@ -1341,6 +1343,17 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
     };
     // head registers -> LDS: raw x^T (permuted positions), decay tables, S_eff
     auto stage_head = [&](const XRegs &R, const SRegs &T) {
+        // swapping the upper and lower 32 lanes leaves lane l with columns 0..3 and lane
+        // l + 32 with columns 4..7 of all 8 tokens
+        u32x2 xv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(R.raw[r][d], R.raw[r][2 + d], false, false);
+                xv[r][d] = sw[0];
+                xv[4 + r][d] = sw[1];
+            }
         const int pos0 = (tg >> 1) * 16 + ((tg & 1) ? 4 : 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1348,8 +1361,8 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
             u32x2 lo, hi;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                lo[k] = pack_halves(R.xv[2 * k][j >> 1], R.xv[2 * k + 1][j >> 1], j & 1);
-                hi[k] = pack_halves(R.xv[4 + 2 * k][j >> 1], R.xv[5 + 2 * k][j >> 1], j & 1);
+                lo[k] = pack_halves(xv[2 * k][j >> 1], xv[2 * k + 1][j >> 1], j & 1);
+                hi[k] = pack_halves(xv[4 + 2 * k][j >> 1], xv[5 + 2 * k][j >> 1], j & 1);
             }
             bf16 *row = Xd + (cg * 4 + j) * XP + pos0;
             *reinterpret_cast<u32x2 *>(row) = lo;
