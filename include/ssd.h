@@ -34,7 +34,9 @@
  *
  * Every call validates its arguments on the host before any launch and returns a
  * status; nothing is launched when it is not SSD_OK.  The library never allocates
- * memory, never synchronises and keeps no global mutable state apart from the
+ * device memory (and no host memory either, except ssd_plan_candidates, a host-only
+ * query that builds its list on the host heap), never synchronises and keeps no
+ * global mutable state apart from the
  * thread-local HIP error code and the static scratch of ssd_forward_noalloc (a
  * device array that the code object holds on each GPU, plus its per-device address).  Work is asynchronous on `stream`; buffers must stay
  * valid until it completes.  Inputs and outputs must not overlap, except that
