@@ -285,13 +285,17 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] *= a;
     };
+    // The first chunk of every group after the first starts from the zero state: it is not
+    // stored (the chunk output reads it as zero).  Its stores still issue, into an empty
+    // buffer range, so the wait counts below stay exact.
     auto state_out = [&](int c) {
-        char *Sc = reinterpret_cast<char *>(S + ((int64_t)bh * nc + c) * P * N + n0);
+        const bool empty = grp > 0 && c == c0;
+        const rsrc_t sr = make_rsrc(S + ((int64_t)bh * nc + c) * P * N + n0, empty ? 0 : (P * N - n0) * 2);
 #pragma unroll
         for (int r = 0; r < SPT; ++r) {
             const int id = tid + NTHR * r, p = id / (NR / 8), c8 = id % (NR / 8);
-            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(&Ss[p * SSP + 8 * c8]);
-            *reinterpret_cast<bf16x8 *>(Sc + (uint32_t)((p * N + 8 * c8) * 2)) = v;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(&Ss[p * SSP + 8 * c8]);
+            buf_store_b128(sr, (uint32_t)((p * N + 8 * c8) * 2), v);
         }
     };
     // transpose-read operand: lane l reads 4 tokens (rows) of 4 columns; rows
@@ -613,17 +617,19 @@ __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
             }
         }
     };
-    // chunk start: the state goes to S[c] (bf16, straight from the accumulators), then decays
+    // chunk start: the state goes to S[c] (bf16, straight from the accumulators), then
+    // decays.  As in the kernel above, the zero first state of a group after the first is
+    // not stored (its stores go to an empty range).
     const uint32_t srow_off = (uint32_t)((4 * half * N + ncol) * 2);   // lane part of the S offsets
     auto chunk_start = [&](float gl, int c) {
-        char *Sc = reinterpret_cast<char *>(S + ((int64_t)bh * nc + c) * P * N);
+        const bool empty = grp > 0 && c == c0;
+        const rsrc_t sr = make_rsrc(S + ((int64_t)bh * nc + c) * P * N, empty ? 0 : P * N * 2);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int prow = 32 * pt + 8 * (v >> 2) + (v & 3);   // acc_row without the lane part
-                *reinterpret_cast<uint32_t *>(Sc + (int64_t)prow * N * 2 + srow_off) =
-                    pack_bf16(acc[pt][0][v], acc[pt][1][v]);
+                buf_store_b32(sr, (uint32_t)(prow * N * 2) + srow_off, pack_bf16(acc[pt][0][v], acc[pt][1][v]));
             }
         const float a = fast_exp2(gl);
 #pragma unroll
@@ -847,11 +853,14 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
     const bf16 *xb = x + ((int64_t)b * L + t0) * xstride + (int64_t)h * P;
     const char *Bb = reinterpret_cast<const char *>(Bm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
     const char *Cb = reinterpret_cast<const char *>(Cm + ((int64_t)b * L + t0) * cstride + (int64_t)g * N);
-    const char *Sb = reinterpret_cast<const char *>(S + ((int64_t)bh * nc + c) * P * N);
     const float *Gh = G2 + (int64_t)bh * Lp + t0;
     const float *dh = dtT + (int64_t)bh * Lp + t0;
     const int kq = 8 * (lane >> 5);
     const int cgrp = CORR ? c / K : 0;
+    // the first chunk of a group after the first starts from zero (the state pass stores
+    // nothing for it): its S loads read an empty range, which returns zeros
+    const rsrc_t sr = make_rsrc(S + ((int64_t)bh * nc + c) * P * N,
+                                (CORR && cgrp > 0 && c % K == 0) ? 0 : P * N * 2);
     const char *Hc = reinterpret_cast<const char *>(CORR ? Hg + ((int64_t)bh * ng + cgrp) * P * N : nullptr);
     const float bc = (CORR && cgrp > 0) ? beta[(int64_t)bh * nc + c] : 0.0f;
 
@@ -887,7 +896,7 @@ __global__ __launch_bounds__(2 * Q) void chunk_out_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < SPC; ++r) {
                     const int id = s_piece(r), p = id >> 3, col = nb + 64 * q + (id & 7) * 8;
-                    sq[q][r] = *reinterpret_cast<const bf16x8 *>(Sb + (uint32_t)((p * N + col) * 2));
+                    sq[q][r] = __builtin_bit_cast(bf16x8, buf_load_b128(sr, (uint32_t)((p * N + col) * 2)));
                     if constexpr (CORR) {
                         hq[q][r][0] = *reinterpret_cast<const f32x4 *>(Hc + (uint32_t)((p * N + col) * 4));
                         hq[q][r][1] = *reinterpret_cast<const f32x4 *>(Hc + (uint32_t)((p * N + col) * 4 + 16));
@@ -1317,14 +1326,17 @@ __global__ __launch_bounds__(2 * Q * SPL) void chunk_out_hb_kernel(
         R.ge = Gh[tq | 31];
         R.dt = dtT[(int64_t)bh * Lp + t0 + tq];
     };
+    // the first chunk of a group after the first starts from zero (the state pass stores
+    // nothing for it): its S loads read an empty range, which returns zeros
+    const bool s_zero = CORR && c >= K && c % K == 0;
     auto load_s = [&](SRegs &R, int hl) {
         hl = min(hl, HB - 1);
         const int h = h_first + hl, bh = b * H + h;
-        const char *Sb = reinterpret_cast<const char *>(S + ((int64_t)bh * nc + c) * P * N);
+        const rsrc_t sr = make_rsrc(S + ((int64_t)bh * nc + c) * P * N, s_zero ? 0 : P * N * 2);
 #pragma unroll
         for (int r = 0; r < SPT; ++r) {
             const int id = tid + NTHR * r, pp = id / (NN / 8), oc = id % (NN / 8);
-            R.sq[r] = *reinterpret_cast<const bf16x8 *>(Sb + (uint32_t)((pp * N + oc * 8) * 2));
+            R.sq[r] = __builtin_bit_cast(bf16x8, buf_load_b128(sr, (uint32_t)((pp * N + oc * 8) * 2)));
         }
         if constexpr (CORR) {
             const int cgrp = c / K;

@@ -119,6 +119,24 @@ __device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off)
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
+__device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Stores past the end of the range are dropped; with a zero-byte range the instructions
+// still issue (and count in the wait counters) but write nothing.
+__device__ __forceinline__ void buf_store_b32(rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_b128(rsrc_t r, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           (int)off, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // LDS transpose reads (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives, for e = 0..3, element i%4 of the 4-element row segment
