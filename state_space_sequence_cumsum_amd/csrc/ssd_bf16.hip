@@ -125,6 +125,21 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F &&f)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// LDS stores written as inline assembly.  The compiler cannot tell which LDS bytes a
+// global-to-LDS load writes, so before an ordinary LDS store it waits for every such
+// load still in flight, including the B tile just requested for two sub-steps later;
+// these stores carry no such wait.  The state pass uses them only for buffers no
+// global-to-LDS load in flight writes (the k-packed x~ tiles and the chunk-start
+// staging tile), and waits for them itself (lgkmcnt(0) before each barrier).
+__device__ __forceinline__ void lds_st64(void *p, u32x2 v)
+{
+    asm volatile("ds_write_b64 %0, %1" ::"v"((uint32_t)(uintptr_t)(lds_void *)p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_st128(void *p, u32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"((uint32_t)(uintptr_t)(lds_void *)p), "v"(v) : "memory");
+}
+
 template <int Q, int NR>
 __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
@@ -253,11 +268,11 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
             f1[k2] = pack_bf16(bf_hi(a) * w0, bf_hi(c) * w1);
         }
         if constexpr (TPP == 8) {
-            *reinterpret_cast<u32x4 *>(&Xk[kx][xk_off(2 * pp, tq)]) = u32x4{f0[0], f0[1], f0[2], f0[3]};
-            *reinterpret_cast<u32x4 *>(&Xk[kx][xk_off(2 * pp + 1, tq)]) = u32x4{f1[0], f1[1], f1[2], f1[3]};
+            lds_st128(&Xk[kx][xk_off(2 * pp, tq)], u32x4{f0[0], f0[1], f0[2], f0[3]});
+            lds_st128(&Xk[kx][xk_off(2 * pp + 1, tq)], u32x4{f1[0], f1[1], f1[2], f1[3]});
         } else {
-            *reinterpret_cast<u32x2 *>(&Xk[kx][xk_off(2 * pp, tq >> 1) + 4 * (tq & 1)]) = u32x2{f0[0], f0[1]};
-            *reinterpret_cast<u32x2 *>(&Xk[kx][xk_off(2 * pp + 1, tq >> 1) + 4 * (tq & 1)]) = u32x2{f1[0], f1[1]};
+            lds_st64(&Xk[kx][xk_off(2 * pp, tq >> 1) + 4 * (tq & 1)], u32x2{f0[0], f0[1]});
+            lds_st64(&Xk[kx][xk_off(2 * pp + 1, tq >> 1) + 4 * (tq & 1)], u32x2{f1[0], f1[1]});
         }
     };
 
@@ -274,7 +289,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
                     bf16x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[i][j][4 * q + r];
-                    *reinterpret_cast<bf16x4 *>(&Ss[p * SSP + n + 8 * q]) = o;
+                    lds_st64(&Ss[p * SSP + n + 8 * q], __builtin_bit_cast(u32x2, o));
                 }
             }
         const float a = fast_exp2(gl);

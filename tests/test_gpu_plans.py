@@ -32,6 +32,7 @@ SHAPES = [
     (_wl("p_n64_q64", "bf16", 1, 512, 2, 64, 1, 64), 1.0),              # one-head output only
     (_wl("p_n256_q256", "bf16", 1, 1024, 8, 256, 2, 256), 1e-2),        # 4 heads per group
     (_wl("p_n384_q128", "bf16", 1, 384, 2, 384, 1, 128), 1.0),          # 128 / 64 columns
+    (_wl("p_n256_q64", "bf16", 1, 330, 2, 256, 1, 64), 1e-2),           # one sub-step per chunk
     (_wl("p_fp32_q64", "fp32", 1, 300, 2, 128, 1, 64), 1e-2),
 ]
 
