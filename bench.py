@@ -76,8 +76,8 @@ def algorithmic(w):
     """Bytes and flops each kernel must move/compute for workload w (one launch).
 
     Per (token, head), e = input element bytes, s = snapshot element bytes:
-      cumsum:     e (dt) + 12 (G2, dtT and wT written, fp32)
-      state pass: e*P (x) + 4 (wT) + e*N*G/H (B, shared by a group) + s*P*N/Q (S written)
+      cumsum:     e (dt) + 8 (G2 and dtT written, fp32)
+      state pass: e*P (x) + 8 (G2, dtT) + e*N*G/H (B, shared by a group) + s*P*N/Q (S written)
                   + 8*P*N per (batch, head) for h0 and hT;  flops 2*N*P
       chunk out:  2*e*P (x, y) + 8 (G2, dtT) + 2*e*N*G/H (B, C) + s*P*N/Q (S read);
                   flops 2*N*P + (Q+1)*P + (Q+1)*N*G/H  (causal lower triangle, C B^T once per group)
@@ -88,8 +88,8 @@ def algorithmic(w):
     th = w.batch * w.seqlen * H          # (token, head) pairs
     bh = w.batch * H
     return {
-        "chunk_cumsum": {"bytes": th * (e + 12), "flops": 2 * th},
-        "state_pass": {"bytes": th * (e * P + 4 + e * N * G / H + s * P * N / Q)
+        "chunk_cumsum": {"bytes": th * (e + 8), "flops": 2 * th},
+        "state_pass": {"bytes": th * (e * P + 8 + e * N * G / H + s * P * N / Q)
                        + (8 * P * N * bh if w.has_h0 else 4 * P * N * bh),
                        "flops": th * 2 * N * P},
         "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),

@@ -23,11 +23,11 @@
  *     B, C    [b, L, G, N]      element type `dtype`; head h reads group h / (H / G)
  *     A, D    [H]               float32 (per-head decay rate and skip weight)
  *     h0, hT  [b, H, P, N]      float32 (initial and final state)
- *     G2, dtT, wT [b, H, Lp]    float32 (stage-1 outputs, token-contiguous per head)
+ *     G2, dtT [b, H, Lp]        float32 (stage-1 outputs, token-contiguous per head)
  *     S       [b, H, nc, P, N]  bfloat16 when dtype is SSD_BF16, float32 when SSD_F32
  * `problem` is a host pointer.  `stream` is a hipStream_t (NULL = the null stream).
  *
- * Alignment: x, y, B, C, S, G2, dtT, wT, h0, hT, h and the workspace are read or
+ * Alignment: x, y, B, C, S, G2, dtT, h0, hT, h and the workspace are read or
  * written with 8- and 16-byte vector accesses and must start on a 16-byte boundary
  * (hipMalloc and torch allocations do); dt, A and D need only their element
  * alignment.  A misaligned pointer returns SSD_ERR_MISALIGNED.
@@ -91,30 +91,30 @@ typedef struct {
 /* Host-only checks of `problem` (dimensions, divisibility, supported set).  No GPU. */
 ssd_status ssd_validate(const ssd_problem *problem);
 
-/* Bytes of device workspace ssd_forward needs (G2, dtT, wT, S and the state pass's group
+/* Bytes of device workspace ssd_forward needs (G2, dtT, S and the state pass's group
  * state, each 256-byte aligned); 0 if `problem` is not valid.  Host-only. */
 size_t ssd_workspace_bytes(const ssd_problem *problem);
 
 /* Stage 1 (section "Kernel 1：计算累积和"): for each (b, h) and token t of chunk c,
  *     G2[b,h,t]  = log2(e) * sum_{k = cQ .. t} A[h] * dt[b,k,h]     (fp32 sum, then scaled)
  *     dtT[b,h,t] = float(dt[b,t,h])
- *     wT[b,h,t]  = dtT[b,h,t] * exp2(G2[b,h,cQ+Q-1] - G2[b,h,t])  (the state-pass weight of
- *                  token t: its dt times the decay from t to the end of its chunk)
- * For padded positions t >= L: dtT = wT = 0 and G2 repeats the chunk's last valid value.
- * Reads dt, A; writes G2, dtT and wT ([b, H, Lp]). */
+ * For padded positions t >= L: dtT = 0 and G2 repeats the chunk's last valid value (so
+ * G2 at a chunk's last position is the cumsum at its last valid token).
+ * Reads dt, A; writes G2 and dtT ([b, H, Lp]). */
 ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A,
-                            float *G2, float *dtT, float *wT, void *stream);
+                            float *G2, float *dtT, void *stream);
 
 /* Stage 2 (section "Kernel 2: fwd_pass_state", the decayed chunk jump): serially over
  * chunks c, S[b,h,c] = h (the state at the chunk start, h = h0 or 0 for c = 0), then
- *     h <- exp2(G2_last) h + Xw_c^T B_c,   Xw_c[t,p] = round(wT_t x[t,p])
- * with G2_last = G2 at the chunk's last position.  The weight wT_t multiplies the
+ *     h <- exp2(G2_last) h + Xw_c^T B_c,   Xw_c[t,p] = round(w_t x[t,p]),
+ *     w_t = dtT_t exp2(G2_last - G2_t)   (token t's dt times its decay to the chunk's end)
+ * with G2_last = G2 at the chunk's last position.  The weight w_t multiplies the
  * 64-wide x row (rounded to the input type) instead of the N-wide B row; the product
- * is the same sum of wT_t x[t,p] B[t,n].
+ * is the same sum of w_t x[t,p] B[t,n].
  * After the last chunk hT = h (skipped when hT is NULL).  h0 may be NULL (zero
- * initial state).  Reads x, B, G2, wT, h0; writes S, hT. */
+ * initial state).  Reads x, B, G2, dtT, h0; writes S, hT. */
 ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
-                          const float *G2, const float *wT, const float *h0, void *S,
+                          const float *G2, const float *dtT, const float *h0, void *S,
                           float *hT, void *stream);
 
 /* Stage 3 (section "Kernel 3：compute_out", the decayed chunk output): for each chunk,
@@ -130,10 +130,11 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
 
 /* The whole forward pass: stage 1, 2 and 3 on `stream`, no host synchronisation.
  * `workspace` (device, >= ssd_workspace_bytes(problem) bytes) holds the intermediates.
- * On return G2, dtT and wT hold the stage-1 outputs.  The state pass may split each
+ * On return G2 and dtT hold the stage-1 outputs.  The state pass may split each
  * (batch, head) chain of chunks into groups that run in parallel from a zero state (the
  * jump is linear), combine the group-final states with a short scan and let stage 3 add
- * the carried-in state; S then holds chunk-start states relative to their group, and
+ * the carried-in state; S then holds chunk-start states relative to their group (the
+ * first chunk of every group after the first, whose state is zero, is not written), and
  * its contents are otherwise unspecified.  h0 may be NULL; hT may be
  * NULL (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
@@ -275,9 +276,9 @@ ssd_status ssd_forward_planned(const ssd_problem *problem, const ssd_launch_plan
                                void *workspace, size_t workspace_bytes, int32_t first_stage,
                                int32_t last_stage, void *const *events, void *stream);
 
-/* Offsets (bytes) of G2, dtT, wT and S inside an ssd_forward workspace.  Host-only. */
+/* Offsets (bytes) of G2, dtT and S inside an ssd_forward workspace.  Host-only. */
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
-                                size_t *off_wT, size_t *off_S);
+                                size_t *off_S);
 
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);

@@ -67,9 +67,9 @@ def lib():
         P, vp, st = ctypes.POINTER(SsdProblem), ctypes.c_void_p, ctypes.c_int
         L.ssd_validate.argtypes, L.ssd_validate.restype = [P], st
         L.ssd_workspace_bytes.argtypes, L.ssd_workspace_bytes.restype = [P], ctypes.c_size_t
-        L.ssd_workspace_layout.argtypes = [P] + [ctypes.POINTER(ctypes.c_size_t)] * 4
+        L.ssd_workspace_layout.argtypes = [P] + [ctypes.POINTER(ctypes.c_size_t)] * 3
         L.ssd_workspace_layout.restype = st
-        L.ssd_chunk_cumsum.argtypes, L.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp, vp, vp], st
+        L.ssd_chunk_cumsum.argtypes, L.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp, vp], st
         L.ssd_state_pass.argtypes, L.ssd_state_pass.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_chunk_out.argtypes, L.ssd_chunk_out.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
         L.ssd_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -137,9 +137,9 @@ def ssd_workspace_bytes(problem: SsdProblem) -> int:
     return lib().ssd_workspace_bytes(ctypes.byref(problem))
 
 
-def ssd_workspace_layout(problem: SsdProblem) -> tuple[int, int, int, int]:
-    """Byte offsets of (G2, dtT, wT, S) inside an ssd_forward workspace."""
-    offs = [ctypes.c_size_t() for _ in range(4)]
+def ssd_workspace_layout(problem: SsdProblem) -> tuple[int, int, int]:
+    """Byte offsets of (G2, dtT, S) inside an ssd_forward workspace."""
+    offs = [ctypes.c_size_t() for _ in range(3)]
     _raise(lib().ssd_workspace_layout(ctypes.byref(problem), *[ctypes.byref(o) for o in offs]),
            "ssd_workspace_layout")
     return tuple(o.value for o in offs)
@@ -223,24 +223,24 @@ def _io_dtype(p: SsdProblem):
     return torch.bfloat16 if p.dtype == SSD_BF16 else torch.float32
 
 
-def ssd_chunk_cumsum(problem: SsdProblem, dt, A, G2=None, dtT=None, wT=None, stream=None):
-    """Stage 1.  Returns (G2, dtT, wT), all float32 [b, H, nc*Q]."""
+def ssd_chunk_cumsum(problem: SsdProblem, dt, A, G2=None, dtT=None, stream=None):
+    """Stage 1.  Returns (G2, dtT), both float32 [b, H, nc*Q]."""
     b, L, H, G, P, N, Q, nc = _dims(problem)
     dev = dt.device
     _dev(dt, "dt", _io_dtype(problem), (b, L, H), None)
     _dev(A, "A", torch.float32, (H,), dev)
     out = []
-    for name, t in (("G2", G2), ("dtT", dtT), ("wT", wT)):
+    for name, t in (("G2", G2), ("dtT", dtT)):
         if t is None:
             t = torch.empty(b, H, nc * Q, device=dev, dtype=torch.float32)
         out.append(_dev(t, name, torch.float32, (b, H, nc * Q), dev))
-    G2, dtT, wT = out
+    G2, dtT = out
     _raise(lib().ssd_chunk_cumsum(ctypes.byref(problem), _ptr(dt), _ptr(A), _ptr(G2), _ptr(dtT),
-                                  _ptr(wT), _stream(stream, dev)), "ssd_chunk_cumsum")
-    return G2, dtT, wT
+                                  _stream(stream, dev)), "ssd_chunk_cumsum")
+    return G2, dtT
 
 
-def ssd_state_pass(problem: SsdProblem, x, B, G2, wT, h0=None, S=None, hT=None, want_final=True,
+def ssd_state_pass(problem: SsdProblem, x, B, G2, dtT, h0=None, S=None, hT=None, want_final=True,
                    stream=None):
     """Stage 2.  Returns (S [b,H,nc,P,N] in the input dtype, hT [b,H,P,N] float32 or None)."""
     b, L, H, G, P, N, Q, nc = _dims(problem)
@@ -249,7 +249,7 @@ def ssd_state_pass(problem: SsdProblem, x, B, G2, wT, h0=None, S=None, hT=None, 
     _dev(x, "x", io, (b, L, H, P), None)
     _dev(B, "B", io, (b, L, G, N), dev)
     _dev(G2, "G2", torch.float32, (b, H, nc * Q), dev)
-    _dev(wT, "wT", torch.float32, (b, H, nc * Q), dev)
+    _dev(dtT, "dtT", torch.float32, (b, H, nc * Q), dev)
     _dev(h0, "h0", torch.float32, (b, H, P, N), dev)
     if S is None:
         S = torch.empty(b, H, nc, P, N, device=dev, dtype=io)
@@ -257,7 +257,7 @@ def ssd_state_pass(problem: SsdProblem, x, B, G2, wT, h0=None, S=None, hT=None, 
         hT = torch.empty(b, H, P, N, device=dev, dtype=torch.float32)
     _dev(S, "S", io, (b, H, nc, P, N), dev)
     _dev(hT, "hT", torch.float32, (b, H, P, N), dev)
-    _raise(lib().ssd_state_pass(ctypes.byref(problem), _ptr(x), _ptr(B), _ptr(G2), _ptr(wT),
+    _raise(lib().ssd_state_pass(ctypes.byref(problem), _ptr(x), _ptr(B), _ptr(G2), _ptr(dtT),
                                 _ptr(h0), _ptr(S), _ptr(hT), _stream(stream, dev)), "ssd_state_pass")
     return S, hT
 
@@ -482,12 +482,12 @@ class StepPlan:
 
 
 def workspace_views(problem: SsdProblem, workspace: torch.Tensor) -> dict:
-    """Typed views (G2, dtT, wT, S) of an ssd_forward workspace tensor."""
+    """Typed views (G2, dtT, S) of an ssd_forward workspace tensor."""
     b, L, H, G, P, N, Q, nc = _dims(problem)
-    g2, dtt, wt, so = ssd_workspace_layout(problem)
+    g2, dtt, so = ssd_workspace_layout(problem)
     cnt = b * H * nc * Q
     f32 = lambda off: workspace[off:off + 4 * cnt].view(torch.float32).view(b, H, nc * Q)
     io = _io_dtype(problem)
     es = 2 if io == torch.bfloat16 else 4
     S = workspace[so:so + es * b * H * nc * P * N].view(io).view(b, H, nc, P, N)
-    return {"G2": f32(g2), "dtT": f32(dtt), "wT": f32(wt), "S": S}
+    return {"G2": f32(g2), "dtT": f32(dtt), "S": S}

@@ -194,16 +194,15 @@ size_t ssd_workspace_bytes_planned(const ssd_problem *problem, const ssd_launch_
 }
 
 ssd_status ssd_workspace_layout(const ssd_problem *problem, size_t *off_G2, size_t *off_dtT,
-                                size_t *off_wT, size_t *off_S)
+                                size_t *off_S)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!off_G2 || !off_dtT || !off_wT || !off_S) return SSD_ERR_NULL_ARG;
+    if (!off_G2 || !off_dtT || !off_S) return SSD_ERR_NULL_ARG;
     const ssd::Shape s = make_shape(problem);
     const Layout l = layout_of(s, ssd::plan_of(s));
     *off_G2 = l.g2;
     *off_dtT = l.dtt;
-    *off_wT = l.wt;
     *off_S = l.S;
     return SSD_OK;
 }
@@ -234,25 +233,25 @@ ssd_status ssd_plan_candidates(const ssd_problem *problem, ssd_launch_plan *plan
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_problem *problem, const void *dt, const float *A, float *G2,
-                            float *dtT, float *wT, void *stream)
+                            float *dtT, void *stream)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!dt || !A || !G2 || !dtT || !wT) return SSD_ERR_NULL_ARG;
-    if (!aligned16({G2, dtT, wT})) return SSD_ERR_MISALIGNED;
-    return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT, wT,
+    if (!dt || !A || !G2 || !dtT) return SSD_ERR_NULL_ARG;
+    if (!aligned16({G2, dtT})) return SSD_ERR_MISALIGNED;
+    return hip_status(ssd::launch_chunk_cumsum(make_shape(problem), dt, A, G2, dtT, nullptr,
                                                (hipStream_t)stream));
 }
 
 ssd_status ssd_state_pass(const ssd_problem *problem, const void *x, const void *B,
-                          const float *G2, const float *wT, const float *h0, void *S, float *hT,
+                          const float *G2, const float *dtT, const float *h0, void *S, float *hT,
                           void *stream)
 {
     const ssd_status st = check_shape(problem);
     if (st != SSD_OK) return st;
-    if (!x || !B || !G2 || !wT || !S) return SSD_ERR_NULL_ARG;
-    if (!aligned16({x, B, G2, wT, h0, S, hT})) return SSD_ERR_MISALIGNED;
-    return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, wT, h0, S, hT,
+    if (!x || !B || !G2 || !dtT || !S) return SSD_ERR_NULL_ARG;
+    if (!aligned16({x, B, G2, dtT, h0, S, hT})) return SSD_ERR_MISALIGNED;
+    return hip_status(ssd::launch_state_pass(make_shape(problem), x, B, G2, dtT, h0, S, hT,
                                              (hipStream_t)stream));
 }
 

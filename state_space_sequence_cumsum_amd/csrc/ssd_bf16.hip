@@ -140,10 +140,12 @@ __device__ __forceinline__ void lds_st128(void *p, u32x4 v)
     asm volatile("ds_write_b128 %0, %1" ::"v"((uint32_t)(uintptr_t)(lds_void *)p), "v"(v) : "memory");
 }
 
-template <int Q, int NR>
+// WT: the weights w_t come precomputed (wt = wT of stage 1); otherwise wt is dtT and the
+// kernel forms w_t = dtT_t exp2(G2_last - G2_t) from it and the cumsum
+template <int Q, int NR, bool WT>
 __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
+    const float *__restrict__ wt, const float *__restrict__ h0, bf16 *__restrict__ S,
     float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
     float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng, int xcd)
 {
@@ -175,7 +177,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     const int rt0 = (wave / (2 / CTW)) * RTW, ct0 = (wave % (2 / CTW)) * CTW;
     const int64_t st_off = (int64_t)bh * P * N;
     const float *Gh = G2 + (int64_t)bh * Lp;
-    const float *wh = wT + (int64_t)bh * Lp;
+    const float *wh = wt + (int64_t)bh * Lp;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     const char *xbytes = reinterpret_cast<const char *>(x + (int64_t)b * L * xstride + (int64_t)h * P);
     const char *Bbytes = reinterpret_cast<const char *>(Bm + (int64_t)b * L * bstride + (int64_t)g * N + n0);
@@ -223,8 +225,9 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     const uint32_t xoff = (uint32_t)(TPP * tq * xrow + 4 * pp);
     struct Regs {
         uint32_t xv[TPP];
-        f32x4 w[TPP / 4];
-        float gl;
+        f32x4 w[TPP / 4];              // the tokens' weights (WT) or their dt
+        f32x4 g[WT ? 1 : TPP / 4];     // (without WT) their cumsum values
+        float gl;                      // cumsum at the end of the sub-step's chunk
     };
     const int last_sub = U - 1;
     auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
@@ -238,13 +241,16 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
             __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(dst + (wave * IPW + k) * RPI * NR),
                                                      16, (int)bdoff[k], 0, 0, 0);
     };
-    // x, weights and (for the first sub-step of a chunk, the only one that uses it) the
-    // chunk-end cumsum value of sub-step u; `with_gl` is a compile-time constant, so the
-    // number of memory instructions a call issues is known
+    // the chunk-end cumsum value (with WT only where sub-step u starts a chunk, the one
+    // place that uses it then), the weights (or dt and cumsum) of this thread's tokens and
+    // x of sub-step u; `with_gl` is a compile-time constant, so the number of memory
+    // instructions a call issues (NLD_GL with it, NLD_NOGL without) is known
+    constexpr int NLD_GL = WT ? 1 + TPP / 4 + TPP : 1 + 2 * (TPP / 4) + TPP;
+    constexpr int NLD_NOGL = WT ? TPP / 4 + TPP : NLD_GL;
     auto load = [&](Regs &R, int u, auto with_gl) {
         u = min(u, last_sub);
         const int t0 = tok0(u);
-        if constexpr (decltype(with_gl)::value) {
+        if constexpr (!WT || decltype(with_gl)::value) {
             int gi = (c0 + u / NSUB) * Q + Q - 1;
             asm volatile("" : "+v"(gi));   // per-lane load: a scalar one would share the LDS wait counter
             R.gl = Gh[gi];
@@ -252,9 +258,21 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
         const float *wb = wh + t0 + TPP * tq;
 #pragma unroll
         for (int k = 0; k < TPP / 4; ++k) R.w[k] = *reinterpret_cast<const f32x4 *>(wb + 4 * k);
+        if constexpr (!WT) {
+            const float *gb = Gh + t0 + TPP * tq;
+#pragma unroll
+            for (int k = 0; k < TPP / 4; ++k) R.g[k] = *reinterpret_cast<const f32x4 *>(gb + 4 * k);
+        }
         const rsrc_t xr = make_rsrc(xbytes + (int64_t)t0 * xrow, (L - t0) * xrow);
 #pragma unroll
         for (int k = 0; k < TPP; ++k) R.xv[k] = buf_load_b32(xr, xoff + k * xrow);
+    };
+    // the state-pass weight of token e of a sub-step: its dt times its decay to the chunk's end
+    auto weight = [](const Regs &R, int e) {
+        if constexpr (WT)
+            return R.w[e >> 2][e & 3];
+        else
+            return R.w[e >> 2][e & 3] * fast_exp2(R.gl - R.g[e >> 2][e & 3]);
     };
     // k-packed x~ row p: 16-byte unit u (8 tokens) stored at unit u ^ ((p >> 4) & 1)
     auto xk_off = [](int p, int u) { return p * XKP + 8 * (u ^ ((p >> 4) & 1)); };
@@ -262,7 +280,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
         uint32_t f0[TPP / 2], f1[TPP / 2];
 #pragma unroll
         for (int k2 = 0; k2 < TPP / 2; ++k2) {
-            const float w0 = R.w[k2 >> 1][2 * (k2 & 1)], w1 = R.w[k2 >> 1][2 * (k2 & 1) + 1];
+            const float w0 = weight(R, 2 * k2), w1 = weight(R, 2 * k2 + 1);
             const uint32_t a = R.xv[2 * k2], c = R.xv[2 * k2 + 1];
             f0[k2] = pack_bf16(bf_lo(a) * w0, bf_lo(c) * w1);
             f1[k2] = pack_bf16(bf_hi(a) * w0, bf_hi(c) * w1);
@@ -340,14 +358,14 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
         }
     };
     // memory instructions issued after the B DMA of step j - 1 and before the barrier of step j
-    // (a lower bound, so the wait never falls short): step j - 1's x loads and late state
-    // stores, step j's DMA, x loads and late state stores
-    // (nx: the x loads a step issues, with the chunk-end value when sub-step s + 2 starts a
+    // (a lower bound, so the wait never falls short): step j - 1's loads and late state
+    // stores, step j's DMA, loads and late state stores
+    // (nx: the loads a step issues, with the chunk-end value when sub-step s + 2 starts a
     // chunk; the step before position 0 is the prologue or the previous block's last step,
-    // which issue the same x loads)
+    // which issue the same loads)
     constexpr auto wait_n = [](int j) {
         const auto so_late = [](int i) { return (NSUB > 1 && i % NSUB == 1) ? SPT : 0; };
-        const auto nx = [](int i) { return TPP + TPP / 4 + (((i + 2) % NSUB == 0) ? 1 : 0); };
+        const auto nx = [](int i) { return ((i + 2) % NSUB == 0) ? NLD_GL : NLD_NOGL; };
         return nx(j > 0 ? j - 1 : lcm3(NSUB, 3, 2) - 1) + (j > 0 ? so_late(j - 1) : 0) + IPW + nx(j) +
                so_late(j);
     };
@@ -404,7 +422,7 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
     load(R[1], 1, std::integral_constant<bool, NSUB == 1>{});
     asm volatile("" ::: "memory");
     stageX(R[0], 0);
-    constexpr int nwait0 = (TPP + TPP / 4 + 1) + IPW + (TPP + TPP / 4 + (NSUB == 1 ? 1 : 0));
+    constexpr int nwait0 = NLD_GL + IPW + (NSUB == 1 ? NLD_GL : NLD_NOGL);
     SP_BARRIER(nwait0);   // B of sub-step 0
     constexpr int UNR = lcm3(NSUB, 3, 2);
     int s = 0;
@@ -486,10 +504,11 @@ __global__ __launch_bounds__((SpCfg<Q, NR>::NTHR)) void state_pass_dma_kernel(
 // to its last sub-step, so the loop has no branches around memory operations.
 // Groups and the decay products for the group scan as in the LDS-transposed kernel.
 // ===========================================================================
-template <int Q, int NR, int D>
+// WT as for the kernel above
+template <int Q, int NR, int D, bool WT>
 __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ wT, const float *__restrict__ h0, bf16 *__restrict__ S,
+    const float *__restrict__ wt, const float *__restrict__ h0, bf16 *__restrict__ S,
     float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
     float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng, int xcd)
 {
@@ -510,7 +529,7 @@ __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int64_t st_off = (int64_t)bh * P * N;
     const float *Gh = G2 + (int64_t)bh * Lp;
-    const float *wh = wT + (int64_t)bh * Lp;
+    const float *wh = wt + (int64_t)bh * Lp;
     const int64_t xstride = (int64_t)H * P, bstride = (int64_t)G * N;
     // x and B are read through buffer resources based at the first row of each tile and
     // ending at row L, so rows past the sequence read as zero (their weight is 0 too);
@@ -564,7 +583,8 @@ __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
     struct Regs {
         uint32_t b[KS][8];      // B words of k-step ks: token 16 ks + 8 half + k, columns ncol, ncol + 1
         uint32_t xv[XPT][8];    // x words of piece r: token 8 to + k, columns 2 pp, 2 pp + 1
-        f32x4 w[XPT][2];        // the weights of those 8 tokens
+        f32x4 w[XPT][2];        // the weights (WT) or dt of those 8 tokens
+        f32x4 g[WT ? 1 : XPT][2];   // (without WT) their cumsum values
         float gl;               // cumsum value at the end of the sub-step's chunk
     };
     auto tok0 = [&](int u) { return (c0 + u / NSUB) * Q + (u % NSUB) * TS; };
@@ -581,6 +601,11 @@ __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
             const float *wb = wh + t0 + 8 * tov[r];
             R.w[r][0] = *reinterpret_cast<const f32x4 *>(wb);
             R.w[r][1] = *reinterpret_cast<const f32x4 *>(wb + 4);
+            if constexpr (!WT) {
+                const float *gb = Gh + t0 + 8 * tov[r];
+                R.g[r][0] = *reinterpret_cast<const f32x4 *>(gb);
+                R.g[r][1] = *reinterpret_cast<const f32x4 *>(gb + 4);
+            }
 #pragma unroll
             for (int k = 0; k < 8; ++k) R.xv[r][k] = buf_load_b32(xr, xoff[r] + k * xrow);
         }
@@ -603,7 +628,13 @@ __global__ __launch_bounds__(NR) void state_pass_rt_kernel(
             u32x4 f0, f1;
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) {
-                const float w0 = R.w[r][k2 >> 1][2 * (k2 & 1)], w1 = R.w[r][k2 >> 1][2 * (k2 & 1) + 1];
+                // the state-pass weight: dt times the decay to the end of the token's chunk
+                const int e0 = 2 * k2, e1 = 2 * k2 + 1;
+                float w0 = R.w[r][e0 >> 2][e0 & 3], w1 = R.w[r][e1 >> 2][e1 & 3];
+                if constexpr (!WT) {
+                    w0 *= fast_exp2(R.gl - R.g[WT ? 0 : r][e0 >> 2][e0 & 3]);
+                    w1 *= fast_exp2(R.gl - R.g[WT ? 0 : r][e1 >> 2][e1 & 3]);
+                }
                 const uint32_t a = R.xv[r][2 * k2], c = R.xv[r][2 * k2 + 1];
                 f0[k2] = pack_bf16(bf_lo(a) * w0, bf_lo(c) * w1);
                 f1[k2] = pack_bf16(bf_hi(a) * w0, bf_hi(c) * w1);
@@ -1582,65 +1613,76 @@ constexpr int kSpRtDepth = 2;
 // times the address-unit issue of 16-byte loads per byte.
 static bool sp_register_transposed(const Shape &s) { return s.N >= 512 && s.N % 256 == 0; }
 
-template <int Q, int NR>
-static hipError_t sp_launch(const Shape &s, bool rt, const void *x, const void *B, const float *G2,
-                            const float *wT, const float *h0, void *S, float *hT, float *Ug,
-                            float *gam, float *beta, int K, int ng, hipStream_t st)
+// wt: the stage-1 weights wT when wpre, else dtT (the kernel forms the weights)
+template <int Q, int NR, bool WPRE>
+static hipError_t sp_launch_w(const Shape &s, bool rt, const void *x, const void *B, const float *G2,
+                              const float *wt, const float *h0, void *S, float *hT, float *Ug,
+                              float *gam, float *beta, int K, int ng, hipStream_t st)
 {
     const int units = (int)(s.b * s.H * (s.N / NR));
     const int xcd = (ng % 8 == 0) ? 1 : 0;
     if constexpr (NR == 256) {
         if (rt) {
-            hipLaunchKernelGGL((state_pass_rt_kernel<Q, 256, kSpRtDepth>), dim3((unsigned)(units * ng)),
-                               dim3(256), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT, h0,
+            hipLaunchKernelGGL((state_pass_rt_kernel<Q, 256, kSpRtDepth, WPRE>), dim3((unsigned)(units * ng)),
+                               dim3(256), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wt, h0,
                                (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
                                (int)s.nc, (int)s.Lp, K, ng, xcd);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((state_pass_dma_kernel<Q, NR>), dim3((unsigned)(units * ng)),
-                       dim3(SpCfg<Q, NR>::NTHR), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wT,
+    hipLaunchKernelGGL((state_pass_dma_kernel<Q, NR, WPRE>), dim3((unsigned)(units * ng)),
+                       dim3(SpCfg<Q, NR>::NTHR), 0, st, (const bf16 *)x, (const bf16 *)B, G2, wt,
                        h0, (bf16 *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G, (int)s.N,
                        (int)s.nc, (int)s.Lp, K, ng, xcd);
     return hipGetLastError();
+}
+
+template <int Q, int NR>
+static hipError_t sp_launch(const Shape &s, bool rt, bool wpre, const void *x, const void *B,
+                            const float *G2, const float *wt, const float *h0, void *S, float *hT,
+                            float *Ug, float *gam, float *beta, int K, int ng, hipStream_t st)
+{
+    return wpre ? sp_launch_w<Q, NR, true>(s, rt, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st)
+                : sp_launch_w<Q, NR, false>(s, rt, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
 }
 
 // columns per state-pass workgroup: the largest of 256, 128, 64 dividing N
 static int sp_cols(const Shape &s) { return (s.N % 256 == 0) ? 256 : (s.N % 128 == 0) ? 128 : 64; }
 
 template <int Q>
-static hipError_t sp_dispatch_q(const Shape &s, int cols, bool rt, const void *x, const void *B,
-                                const float *G2, const float *wT, const float *h0, void *S,
-                                float *hT, float *Ug, float *gam, float *beta, int K, int ng,
-                                hipStream_t st)
+static hipError_t sp_dispatch_q(const Shape &s, int cols, bool rt, bool wpre, const void *x,
+                                const void *B, const float *G2, const float *wt, const float *h0,
+                                void *S, float *hT, float *Ug, float *gam, float *beta, int K,
+                                int ng, hipStream_t st)
 {
     switch (cols) {
-    case 256: return sp_launch<Q, 256>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return sp_launch<Q, 128>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return sp_launch<Q, 64>(s, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 256: return sp_launch<Q, 256>(s, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_launch<Q, 128>(s, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_launch<Q, 64>(s, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
 // bf16 state pass with `cols` state columns per workgroup (B transposed in registers
-// when rt, cols = 256) over ng groups of K chunks per chain
-static hipError_t sp_dispatch(const Shape &s, int cols, bool rt, const void *x, const void *B,
-                              const float *G2, const float *wT, const float *h0, void *S,
-                              float *hT, float *Ug, float *gam, float *beta, int K, int ng,
-                              hipStream_t st)
+// when rt, cols = 256) over ng groups of K chunks per chain; wt is the stage-1 weights
+// wT when wpre, else dtT
+static hipError_t sp_dispatch(const Shape &s, int cols, bool rt, bool wpre, const void *x,
+                              const void *B, const float *G2, const float *wt, const float *h0,
+                              void *S, float *hT, float *Ug, float *gam, float *beta, int K,
+                              int ng, hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return sp_dispatch_q<64>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return sp_dispatch_q<128>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return sp_dispatch_q<256>(s, cols, rt, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 64: return sp_dispatch_q<64>(s, cols, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return sp_dispatch_q<128>(s, cols, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return sp_dispatch_q<256>(s, cols, rt, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
-                                  const float *wT, const float *h0, void *S, float *hT,
+                                  const float *dtT, const float *h0, void *S, float *hT,
                                   hipStream_t st)
 {
-    return sp_dispatch(s, sp_cols(s), sp_register_transposed(s), x, B, G2, wT, h0, S, hT, nullptr,
-                       nullptr, nullptr, (int)s.nc, 1, st);
+    return sp_dispatch(s, sp_cols(s), sp_register_transposed(s), false, x, B, G2, dtT, h0, S, hT,
+                       nullptr, nullptr, nullptr, (int)s.nc, 1, st);
 }
 
 // Chunks per group and groups per chain for the state pass with `cols` columns per
@@ -1702,15 +1744,14 @@ hipError_t launch_state_pass_grouped(const Shape &s, const LaunchPlan &lp, const
 {
     const int K = lp.sp_group_chunks, ng = lp.sp_groups;
     if (!s.bf16)
-        return ng <= 1 ? launch_state_pass(s, x, B, G2, wT, h0, S, hT, st)
-                       : launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, Ug, gam, beta, K,
-                                                       ng, st);
+        return launch_state_pass_f32_grouped(s, x, B, G2, wT, h0, S, ng <= 1 ? hT : nullptr,
+                                             ng <= 1 ? nullptr : Ug, gam, beta, K, ng, st);
     const bool rt = lp.sp_register_transposed != 0;
     if (ng <= 1)
-        return sp_dispatch(s, lp.sp_columns, rt, x, B, G2, wT, h0, S, hT, nullptr, nullptr,
+        return sp_dispatch(s, lp.sp_columns, rt, true, x, B, G2, wT, h0, S, hT, nullptr, nullptr,
                            nullptr, (int)s.nc, 1, st);
-    return sp_dispatch(s, lp.sp_columns, rt, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K, ng,
-                       st);
+    return sp_dispatch(s, lp.sp_columns, rt, true, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K,
+                       ng, st);
 }
 
 hipError_t launch_group_scan(const Shape &s, const LaunchPlan &lp, float *hT, float *Ug, void *Hb,

@@ -22,11 +22,12 @@ namespace ssd {
 // scans its head's Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane
 // shuffle scan adds the lane prefixes, and the results are written
 // token-contiguous.  Padded tokens (last chunk) get dt = 0 and repeat the last
-// valid cumsum value exactly.  The same pass emits each token's state-pass
-// weight w_t = dt_t exp2(G_last - G_t) (its decay to the end of its chunk), so
-// the serial state pass reads it instead of recomputing it per state tile.
+// valid cumsum value exactly, so G2 at a chunk's last position is the value at its
+// last valid token.  With wT the same pass also writes each token's state-pass weight
+// w_t = dt_t exp2(G_last - G_t) (its decay to the end of its chunk), which the
+// forward's state pass then reads instead of forming it per state tile.
 // ===========================================================================
-template <typename T, int Q>
+template <typename T, int Q, bool WOUT>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__ dt,
                                                            const float *__restrict__ A,
                                                            float *__restrict__ G2,
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
         const float d = tile[t][hh];
         G2[base + j] = gt;
         dtT[base + j] = d;
-        wT[base + j] = d * fast_exp2(glast - gt);
+        if constexpr (WOUT) wT[base + j] = d * fast_exp2(glast - gt);
     }
 }
 
@@ -110,10 +111,12 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
 // beta_c (group start to chunk c) and gamma_g (the whole group) for the group
 // scan; without Ug (one group) the final state goes to hT.
 // ===========================================================================
-template <typename T, int Q>
+// WPRE: wt holds the stage-1 weights wT; otherwise it holds dtT and the kernel forms the
+// weights from it and the cumsum
+template <typename T, int Q, bool WPRE>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const T *__restrict__ x, const T *__restrict__ Bm, const float *__restrict__ G2,
-    const float *__restrict__ wT, const float *__restrict__ h0, T *__restrict__ S,
+    const float *__restrict__ wt, const float *__restrict__ h0, T *__restrict__ S,
     float *__restrict__ hT, float *__restrict__ Ug, float *__restrict__ gam,
     float *__restrict__ beta, int L, int H, int G, int N, int nc, int Lp, int K, int ng)
 {
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     }
 
     const float *Gh = G2 + (int64_t)bh * Lp;
-    const float *wh = wT + (int64_t)bh * Lp;
+    const float *wh = wt + (int64_t)bh * Lp;
     const int64_t xrow = (int64_t)H * P;   // x token stride
     const int64_t brow = (int64_t)G * N;   // B token stride
     // the chunk-end cumsum value of chunk c0 + lane (clamped to the group), for the decay
@@ -155,7 +158,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     for (int c = c0; c < c1; ++c) {
         const int t0 = c * Q;
         const float glast = Gh[t0 + Q - 1];
-        for (int t = tid; t < Q; t += 256) wsh[t] = wh[t0 + t];
+        // the state-pass weight of token t: dt times the decay to the end of its chunk
+        for (int t = tid; t < Q; t += 256)
+            wsh[t] = WPRE ? wh[t0 + t] : wh[t0 + t] * fast_exp2(glast - Gh[t0 + t]);
         __syncthreads();
 
         // X_c [Q x 64] -> XT[p][t]
@@ -427,8 +432,12 @@ static hipError_t cumsum_tq(const Shape &s, const void *dt, const float *A, floa
                             float *wT, hipStream_t st)
 {
     dim3 grid((unsigned)s.nc, (unsigned)((s.H + 3) / 4), (unsigned)s.b);
-    hipLaunchKernelGGL((chunk_cumsum_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)dt, A, G2,
-                       dtT, wT, (int)s.L, (int)s.H, (int)s.Lp);
+    if (wT != nullptr)
+        hipLaunchKernelGGL((chunk_cumsum_kernel<T, Q, true>), grid, dim3(256), 0, st, (const T *)dt,
+                           A, G2, dtT, wT, (int)s.L, (int)s.H, (int)s.Lp);
+    else
+        hipLaunchKernelGGL((chunk_cumsum_kernel<T, Q, false>), grid, dim3(256), 0, st, (const T *)dt,
+                           A, G2, dtT, wT, (int)s.L, (int)s.H, (int)s.Lp);
     return hipGetLastError();
 }
 
@@ -451,44 +460,53 @@ hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, f
 }
 
 template <typename T, int Q>
-static hipError_t state_pass_tq(const Shape &s, const void *x, const void *B, const float *G2,
-                                const float *wT, const float *h0, void *S, float *hT, float *Ug,
-                                float *gam, float *beta, int K, int ng, hipStream_t st)
+static hipError_t state_pass_tq(const Shape &s, bool wpre, const void *x, const void *B,
+                                const float *G2, const float *wt, const float *h0, void *S,
+                                float *hT, float *Ug, float *gam, float *beta, int K, int ng,
+                                hipStream_t st)
 {
     dim3 grid((unsigned)(s.N / 64), (unsigned)(s.b * s.H), (unsigned)ng);
-    hipLaunchKernelGGL((state_pass_kernel<T, Q>), grid, dim3(256), 0, st, (const T *)x, (const T *)B,
-                       G2, wT, h0, (T *)S, hT, Ug, gam, beta, (int)s.L, (int)s.H, (int)s.G,
-                       (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
+    auto launch = [&](auto wc) {
+        hipLaunchKernelGGL((state_pass_kernel<T, Q, decltype(wc)::value>), grid, dim3(256), 0, st,
+                           (const T *)x, (const T *)B, G2, wt, h0, (T *)S, hT, Ug, gam, beta,
+                           (int)s.L, (int)s.H, (int)s.G, (int)s.N, (int)s.nc, (int)s.Lp, K, ng);
+    };
+    if (wpre)
+        launch(std::true_type{});
+    else
+        launch(std::false_type{});
     return hipGetLastError();
 }
 
+// wt: the stage-1 weights wT when wpre, else dtT (the kernel forms the weights)
 template <typename T>
-static hipError_t state_pass_t(const Shape &s, const void *x, const void *B, const float *G2,
-                               const float *wT, const float *h0, void *S, float *hT, float *Ug,
-                               float *gam, float *beta, int K, int ng, hipStream_t st)
+static hipError_t state_pass_t(const Shape &s, bool wpre, const void *x, const void *B,
+                               const float *G2, const float *wt, const float *h0, void *S,
+                               float *hT, float *Ug, float *gam, float *beta, int K, int ng,
+                               hipStream_t st)
 {
     switch (s.Q) {
-    case 64: return state_pass_tq<T, 64>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    case 128: return state_pass_tq<T, 128>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
-    default: return state_pass_tq<T, 256>(s, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 64: return state_pass_tq<T, 64>(s, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    case 128: return state_pass_tq<T, 128>(s, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
+    default: return state_pass_tq<T, 256>(s, wpre, x, B, G2, wt, h0, S, hT, Ug, gam, beta, K, ng, st);
     }
 }
 
 hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const float *G2,
-                             const float *wT, const float *h0, void *S, float *hT,
+                             const float *dtT, const float *h0, void *S, float *hT,
                              hipStream_t st)
 {
-    return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, wT, h0, S, hT, st)
-                  : state_pass_t<float>(s, x, B, G2, wT, h0, S, hT, nullptr, nullptr, nullptr,
-                                        (int)s.nc, 1, st);
+    return s.bf16 ? launch_state_pass_bf16(s, x, B, G2, dtT, h0, S, hT, st)
+                  : state_pass_t<float>(s, false, x, B, G2, dtT, h0, S, hT, nullptr, nullptr,
+                                        nullptr, (int)s.nc, 1, st);
 }
 
 hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const void *B,
                                          const float *G2, const float *wT, const float *h0,
-                                         void *S, float *Ug, float *gam, float *beta, int K,
-                                         int ng, hipStream_t st)
+                                         void *S, float *hT, float *Ug, float *gam, float *beta,
+                                         int K, int ng, hipStream_t st)
 {
-    return state_pass_t<float>(s, x, B, G2, wT, h0, S, nullptr, Ug, gam, beta, K, ng, st);
+    return state_pass_t<float>(s, true, x, B, G2, wT, h0, S, hT, Ug, gam, beta, K, ng, st);
 }
 
 int chunk_out_f32_threads(const Shape &s)

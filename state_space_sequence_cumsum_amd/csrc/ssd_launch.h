@@ -16,11 +16,12 @@ struct Shape {
     bool bf16;
 };
 
+// wT may be NULL (not written): the forward's state-pass weights, see below
 hipError_t launch_chunk_cumsum(const Shape &s, const void *dt, const float *A, float *G2,
                                float *dtT, float *wT, hipStream_t st);
 
 hipError_t launch_state_pass(const Shape &s, const void *x, const void *B, const float *G2,
-                             const float *wT, const float *h0, void *S, float *hT,
+                             const float *dtT, const float *h0, void *S, float *hT,
                              hipStream_t st);
 
 hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const void *C,
@@ -55,12 +56,16 @@ bool plan_valid(const Shape &s, const LaunchPlan &lp);
 // states H_g and writes hT.  Scratch: Ug [b*H, ng, P, N], gam [b*H, ng], beta [b*H, nc],
 // all fp32, and for bf16 problems Hb [b*H, ng, P, N] bf16 (H_g rounded, zeros for
 // group 0).
+// The forward's state passes read the weights w_t = dtT_t exp2(G2_last - G2_t) that its
+// stage 1 wrote to the workspace (wT [b, H, Lp]); the public stage-2 entry point
+// (launch_state_pass) forms them from dtT and G2 instead.
 // fp32 state pass over ng groups of K chunks (ssd_kernels.hip): local chunk-start
-// states into S, final local states into Ug, decays into gam and beta.
+// states into S, final local states into Ug, decays into gam and beta; with one group
+// (Ug NULL) true states and hT.
 hipError_t launch_state_pass_f32_grouped(const Shape &s, const void *x, const void *B,
                                          const float *G2, const float *wT, const float *h0,
-                                         void *S, float *Ug, float *gam, float *beta, int K,
-                                         int ng, hipStream_t st);
+                                         void *S, float *hT, float *Ug, float *gam, float *beta,
+                                         int K, int ng, hipStream_t st);
 hipError_t launch_state_pass_grouped(const Shape &s, const LaunchPlan &lp, const void *x,
                                      const void *B, const float *G2, const float *wT,
                                      const float *h0, void *S, float *hT, float *Ug, float *gam,
@@ -88,7 +93,7 @@ hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, con
 
 // bf16 kernels (ssd_bf16.hip)
 hipError_t launch_state_pass_bf16(const Shape &s, const void *x, const void *B, const float *G2,
-                                  const float *wT, const float *h0, void *S, float *hT,
+                                  const float *dtT, const float *h0, void *S, float *hT,
                                   hipStream_t st);
 // hb: heads per head-blocked workgroup for the full chunks (0: every chunk on the
 // one-head kernel)

@@ -51,18 +51,19 @@ def test_validate_null_problem():
 
 def test_workspace_size_and_layout():
     p = _p()
-    g2, dtt, wt, s = ssd.ssd_workspace_layout(p)
+    g2, dtt, s = ssd.ssd_workspace_layout(p)
     cum = 1 * 32 * 64 * 256 * 4          # b*H*Lp fp32
     snap = 1 * 32 * 64 * 64 * 256 * 2    # b*H*nc*P*N bf16
-    assert (g2, dtt, wt, s) == (0, cum, 2 * cum, 3 * cum)
+    # G2, dtT, the forward's own state-pass weights, then S
+    assert (g2, dtt, s) == (0, cum, 3 * cum)
     # plus the grouped state pass's scratch: group states, group and chunk decays
     assert ssd.ssd_workspace_bytes(p) >= 3 * cum + snap
-    assert all(o % 256 == 0 for o in (g2, dtt, wt, s))
+    assert all(o % 256 == 0 for o in (g2, dtt, s))
     # ragged length: padded to whole chunks, fp32 snapshots for fp32 problems
     q = _p(seqlen=1000, chunk=128, dtype="fp32", dstate=64)
     nc = 8
-    g2, dtt, wt, s = ssd.ssd_workspace_layout(q)
-    assert dtt >= 32 * nc * 128 * 4 and dtt % 256 == 0 and wt >= 2 * dtt
+    g2, dtt, s = ssd.ssd_workspace_layout(q)
+    assert dtt >= 32 * nc * 128 * 4 and dtt % 256 == 0 and s >= 3 * dtt
     assert ssd.ssd_workspace_bytes(q) >= s + 32 * nc * 64 * 64 * 4
     assert ssd.ssd_workspace_bytes(_p(dstate=100)) == 0
 
@@ -72,8 +73,8 @@ def test_entry_points_reject_bad_arguments_without_launching():
     p = _p()
     fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
     # missing pointers
-    assert lib.ssd_chunk_cumsum(ctypes.byref(p), None, fake, fake, fake, fake, None) == 1
-    assert lib.ssd_chunk_cumsum(ctypes.byref(p), fake, fake, fake, fake, None, None) == 1
+    assert lib.ssd_chunk_cumsum(ctypes.byref(p), None, fake, fake, fake, None) == 1
+    assert lib.ssd_chunk_cumsum(ctypes.byref(p), fake, fake, fake, None, None) == 1
     assert lib.ssd_state_pass(ctypes.byref(p), fake, None, fake, fake, None, fake, None, None) == 1
     assert lib.ssd_chunk_out(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, None) == 1
     assert lib.ssd_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None, None,
@@ -115,7 +116,7 @@ def test_misaligned_pointers_are_rejected_without_launching():
     p = _p()
     ok = ctypes.c_void_p(4096)
     off = ctypes.c_void_p(4096 + 8)   # element-aligned, not on 16 bytes
-    assert lib.ssd_chunk_cumsum(ctypes.byref(p), off, ok, ok, off, ok, None) == 6
+    assert lib.ssd_chunk_cumsum(ctypes.byref(p), off, ok, ok, off, None) == 6
     assert lib.ssd_state_pass(ctypes.byref(p), off, ok, ok, ok, None, ok, None, None) == 6
     assert lib.ssd_state_pass(ctypes.byref(p), ok, ok, ok, ok, off, ok, None, None) == 6
     assert lib.ssd_chunk_out(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, off, None) == 6

@@ -140,17 +140,17 @@ def test_stages_graph_replay():
     w = _wl("stages_graph", "bf16", 2, 1280, 4, 64, 128, 2, 64)
     d = to_dev(make_inputs(w, 11), dev)
     prob = ssd.problem_of(d["x"], d["B"], w.chunk)
-    G2, dtT, wT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
-    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"])
+    G2, dtT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    S, hT = ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"])
     y = ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"])
     torch.cuda.synchronize()
-    outs = {"G2": G2, "dtT": dtT, "wT": wT, "S": S, "hT": hT, "y": y}
+    outs = {"G2": G2, "dtT": dtT, "S": S, "hT": hT, "y": y}
     ref = {k: v.clone() for k, v in outs.items()}
     side = torch.cuda.Stream(dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, wT, stream=side)
-        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, wT, d["h0"], S=S, hT=hT, stream=side)
+        ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"], G2, dtT, stream=side)
+        ssd.ssd_state_pass(prob, d["x"], d["B"], G2, dtT, d["h0"], S=S, hT=hT, stream=side)
         ssd.ssd_chunk_out(prob, d["x"], d["B"], d["C"], G2, dtT, S, d["D"], y=y, stream=side)
     for k in range(3):
         for t in outs.values():
