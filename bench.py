@@ -62,7 +62,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 KERNEL_SOURCE_GLOBS = ["state_space_sequence_cumsum_amd/csrc/*", "include/ssd.h",
                        "state_space_sequence_cumsum_amd/build.py"]
 KERNEL_NAMES = {"chunk_cumsum": "chunk_cumsum_kernel", "state_pass": "state_pass",
-                "group_scan": "group_scan_kernel", "chunk_out": "chunk_out"}
+                "group_scan": "group_scan_kernel", "chunk_out": "chunk_out",
+                "forward_small": "forward_small"}
 # the four launches of a forward, in order; ssd_forward_timed records an event before
 # the first and after each
 STAGES = ["chunk_cumsum", "state_pass", "group_scan", "chunk_out"]
@@ -81,6 +82,9 @@ def algorithmic(w):
                   + 8*P*N per (batch, head) for h0 and hT;  flops 2*N*P
       chunk out:  2*e*P (x, y) + 8 (G2, dtT) + 2*e*N*G/H (B, C) + s*P*N/Q (S read);
                   flops 2*N*P + (Q+1)*P + (Q+1)*N*G/H  (causal lower triangle, C B^T once per group)
+      forward_small (the one-launch forward, which keeps every intermediate on chip):
+                  e*(2*P + 1) (x, y, dt) + 2*e*N*G/H (B, C) + h0 and hT; flops those of the
+                  state pass and the chunk output together
     """
     e = 2 if w.dtype == "bf16" else 4
     s = e
@@ -94,6 +98,9 @@ def algorithmic(w):
                        "flops": th * 2 * N * P},
         "chunk_out": {"bytes": th * (2 * e * P + 8 + 2 * e * N * G / H + s * P * N / Q),
                       "flops": th * (2 * N * P + (Q + 1) * P + (Q + 1) * N * G / H)},
+        "forward_small": {"bytes": th * (e * (2 * P + 1) + 2 * e * N * G / H)
+                          + (8 * P * N * bh if w.has_h0 else 4 * P * N * bh),
+                          "flops": th * (4 * N * P + (Q + 1) * P + (Q + 1) * N * G / H)},
     }
 
 
@@ -561,6 +568,12 @@ def main():
 
     per = {n: [evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(reps)]
            for i, n in enumerate(names)}   # microseconds
+    # a one-launch plan runs the whole forward as its last stage's launch (the other stages
+    # launch nothing)
+    fused = bool(aplan.launch_plan.get("fused"))
+    if fused:
+        names = ["forward_small"]
+        per = {"forward_small": per["chunk_out"]}
     in_fwd = {n: {"mean_us": statistics.fmean(v), "median_us": statistics.median(v),
                   "p10_us": pct(v, 10), "p90_us": pct(v, 90), "min_us": min(v)}
               for n, v in per.items()}
@@ -576,7 +589,8 @@ def main():
     nb = 10
     rb = max(1, reps // nb)
     kern = {}
-    for n, stage in (("chunk_out", 3), ("chunk_cumsum", 0), ("state_pass", 1)):
+    alone = (("forward_small", 3),) if fused else (("chunk_out", 3), ("chunk_cumsum", 0), ("state_pass", 1))
+    for n, stage in alone:
         pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(nb)]
         for a, z in pairs:
@@ -591,7 +605,8 @@ def main():
                    "launches": nb * rb}
     aplan.run()       # the workspace as a whole forward leaves it
     torch.cuda.synchronize()
-    kern["group_scan"] = dict(in_fwd["group_scan"], timing="in-forward event pair")
+    if not fused:
+        kern["group_scan"] = dict(in_fwd["group_scan"], timing="in-forward event pair")
     kern = {n: kern[n] for n in names}
 
     # --- cold region: each forward after a write of FLUSH_MIB through the caches, so
@@ -621,7 +636,7 @@ def main():
         peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
         if n != "chunk_cumsum":
             kern[n]["frac_mfma"] = kern[n]["TFLOP_s"] / peak
-    dom = max(("state_pass", "chunk_out"), key=lambda n: kern[n]["mean_us"])
+    dom = "forward_small" if fused else max(("state_pass", "chunk_out"), key=lambda n: kern[n]["mean_us"])
     traffic = None
     try:
         with open(traffic_file(w)) as fh:

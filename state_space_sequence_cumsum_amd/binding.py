@@ -50,7 +50,7 @@ class SsdLaunchPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "sp_group_chunks", "sp_groups", "sp_columns", "sp_workgroups", "scan", "co_head_blocked",
         "co_heads_per_block", "co_column_split", "co_workgroups", "co_threads",
-        "sp_register_transposed", "sp_threads")]
+        "sp_register_transposed", "sp_threads", "fused")]
 
 
 _lib = None

@@ -12,6 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBRARY = os.path.join(PKG, "libssd.so")
 SOURCES = [os.path.join(CSRC, "ssd_kernels.hip"), os.path.join(CSRC, "ssd_bf16.hip"),
            os.path.join(CSRC, "ssd_step.hip"), os.path.join(CSRC, "ssd_noalloc.hip"),
+           os.path.join(CSRC, "ssd_small.hip"),
            os.path.join(CSRC, "ssd_api.cpp")]
 
 HIPCC_FLAGS = [

@@ -129,6 +129,7 @@ ssd::LaunchPlan to_internal(const ssd_launch_plan &p)
     lp.co_threads = p.co_threads;
     lp.sp_register_transposed = p.sp_register_transposed;
     lp.sp_threads = p.sp_threads;
+    lp.fused = p.fused;
     return lp;
 }
 
@@ -147,6 +148,7 @@ ssd_launch_plan to_public(const ssd::LaunchPlan &lp)
     p.co_threads = lp.co_threads;
     p.sp_register_transposed = lp.sp_register_transposed;
     p.sp_threads = lp.sp_threads;
+    p.fused = lp.fused;
     return p;
 }
 
@@ -308,6 +310,9 @@ ssd_status forward_launches(const ssd_problem *problem, const ssd_launch_plan *p
         return events ? hip_status(hipEventRecord((hipEvent_t)events[i], hs)) : SSD_OK;
     };
     auto launch = [&](int i) -> hipError_t {
+        if (lp.fused)   // the whole forward is the last stage's one launch
+            return i == 3 ? ssd::launch_forward_small(s, x, dt, A, B, C, D, h0, y, hT, G2, dtT, hs)
+                          : hipSuccess;
         switch (i) {
         case 0: return ssd::launch_chunk_cumsum(s, dt, A, G2, dtT, wT, hs);
         case 1:

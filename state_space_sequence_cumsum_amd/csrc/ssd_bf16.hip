@@ -1859,7 +1859,28 @@ static bool plan_from(const Shape &s, int K, int ng, int cols, int rt, int co_hb
     lp.co_threads = (int)co_threads;
     lp.sp_register_transposed = rt;
     lp.sp_threads = sp_threads;
+    lp.fused = 0;
     return true;
+}
+
+// The one-launch plan (forward_small): one workgroup of 256 threads per (batch, head, chunk)
+static LaunchPlan plan_fused(const Shape &s)
+{
+    LaunchPlan lp;
+    lp.sp_group_chunks = (int)s.nc;
+    lp.sp_groups = 1;
+    lp.sp_columns = (int)s.N;
+    lp.sp_workgroups = 0;
+    lp.scan = 0;
+    lp.co_head_blocked = 0;
+    lp.co_heads_per_block = 1;
+    lp.co_column_split = 1;
+    lp.co_workgroups = (int)(s.b * s.H * s.nc);
+    lp.co_threads = 256;
+    lp.sp_register_transposed = 0;
+    lp.sp_threads = 0;
+    lp.fused = 1;
+    return lp;
 }
 
 static bool plan_same(const LaunchPlan &a, const LaunchPlan &b)
@@ -1870,11 +1891,14 @@ static bool plan_same(const LaunchPlan &a, const LaunchPlan &b)
            a.co_heads_per_block == b.co_heads_per_block &&
            a.co_column_split == b.co_column_split && a.co_workgroups == b.co_workgroups &&
            a.co_threads == b.co_threads && a.sp_register_transposed == b.sp_register_transposed &&
-           a.sp_threads == b.sp_threads;
+           a.sp_threads == b.sp_threads && a.fused == b.fused;
 }
 
 LaunchPlan plan_of(const Shape &s)
 {
+    // a few chunks: the one-launch forward (its repeated state work is bounded by the chunk
+    // count; the launches and round trips of the general path cost more)
+    if (forward_small_eligible(s)) return plan_fused(s);
     const int cols = s.bf16 ? sp_cols(s) : 64;
     const bool rt = s.bf16 && sp_register_transposed(s);
     const Grouping gp = state_pass_groups(s, cols, rt);
@@ -1888,6 +1912,7 @@ LaunchPlan plan_of(const Shape &s)
 
 bool plan_valid(const Shape &s, const LaunchPlan &lp)
 {
+    if (lp.fused != 0) return lp.fused == 1 && forward_small_eligible(s) && plan_same(lp, plan_fused(s));
     const int64_t K = lp.sp_group_chunks;
     if (K < 1 || K > s.nc || lp.sp_groups != (s.nc + K - 1) / K) return false;
     if (s.bf16) {
@@ -1917,6 +1942,7 @@ int plan_candidates(const Shape &s, LaunchPlan *out, int cap)
         all.push_back(lp);
     };
     push(plan_of(s));
+    if (forward_small_eligible(s)) push(plan_fused(s));
     // state-pass kernels: (columns per workgroup, B transposed in registers)
     std::vector<std::pair<int, int>> kernels;
     if (s.bf16) {

@@ -33,10 +33,12 @@ hipError_t launch_chunk_out(const Shape &s, const void *x, const void *B, const 
 // each serial chain of chunks into sp_groups groups of sp_group_chunks chunks (1 group:
 // one chain), and the chunk output's kernel (head-blocked with co_heads_per_block heads
 // per workgroup, or one head per workgroup); the other fields follow from these.
+// fused = 1: the whole forward as one launch (forward_small below); the state-pass and
+// group-scan fields then describe no launch.
 struct LaunchPlan {
     int sp_group_chunks, sp_groups, sp_columns, sp_workgroups, scan;
     int co_head_blocked, co_heads_per_block, co_column_split, co_workgroups, co_threads;
-    int sp_register_transposed, sp_threads;
+    int sp_register_transposed, sp_threads, fused;
 };
 // The cost model's choice for shape s.
 LaunchPlan plan_of(const Shape &s);
@@ -85,6 +87,16 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const LaunchPlan &lp, cons
 // 64-token chunks when the grid has fewer than 1024 workgroups (the chunk's tiles side by
 // side), else Q (Q/64 waves with two row tiles each).
 int chunk_out_f32_threads(const Shape &s);
+
+// The whole forward in one launch for fp32 problems of at most kSmallMaxChunks chunks of 64
+// tokens, headdim 64, dstate 64 or 128 (ssd_small.hip): one workgroup per (batch, head,
+// chunk) walks the jump over the earlier chunks and computes its chunk's output; writes y,
+// hT (may be NULL) and the chunk cumsum and dt into G2 and dtT.
+constexpr int kSmallMaxChunks = 8;
+bool forward_small_eligible(const Shape &s);
+hipError_t launch_forward_small(const Shape &s, const void *x, const void *dt, const float *A,
+                                const void *B, const void *C, const float *D, const float *h0,
+                                void *y, float *hT, float *G2, float *dtT, hipStream_t st);
 
 // One decode step per (batch, head), h updated in place (ssd_step.hip).
 hipError_t launch_decode_step(const Shape &s, const void *x, const void *dt, const float *A,

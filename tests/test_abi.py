@@ -214,7 +214,7 @@ def test_launch_plan_per_shape():
     assert ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256)) == dict(
         sp_group_chunks=8, sp_groups=8, sp_columns=256, sp_workgroups=256, scan=1,
         co_head_blocked=1, co_heads_per_block=8, co_column_split=1, co_workgroups=256,
-        co_threads=512, sp_register_transposed=0, sp_threads=512)
+        co_threads=512, sp_register_transposed=0, sp_threads=512, fused=0)
     # N = 512 with 128-token chunks: the register-transposed state pass, two 256-column
     # workgroups of 4 waves per chain and two per CU (8 groups of 64 chunks), the chunk
     # output's columns split over wave pairs
@@ -234,16 +234,25 @@ def test_launch_plan_per_shape():
     for kw in (dict(chunk=64), dict(dstate=384, chunk=128)):
         q = ssd.ssd_plan(_p(**kw))
         assert q["co_head_blocked"] == 0 and q["co_heads_per_block"] == 1
-    # fp32: 64 columns per state-pass workgroup, chains split into groups up to four
+    # fp32 with at most 8 chunks of 64 tokens and dstate 64 or 128: the whole forward as one
+    # launch, one 256-thread workgroup per (batch, head, chunk)
+    f0 = ssd.ssd_plan(_p(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"))
+    assert (f0["fused"], f0["co_workgroups"], f0["co_threads"], f0["sp_workgroups"], f0["scan"]) == (1, 16, 256, 0, 0)
+    assert ssd.ssd_plan(_p(seqlen=512, nheads=4, dstate=128, chunk=64, dtype="fp32"))["fused"] == 1
+    for kw in (dict(seqlen=513), dict(dstate=256), dict(chunk=128), dict(dtype="bf16")):
+        args = dict(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32")
+        args.update(kw)
+        assert ssd.ssd_plan(_p(**args))["fused"] == 0, kw
+    # fp32 otherwise: 64 columns per state-pass workgroup, chains split into groups up to four
     # workgroups per CU at 64-token chunks (here one chunk per group), then the scan
-    f = ssd.ssd_plan(_p(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"))
+    f = ssd.ssd_plan(_p(seqlen=576, nheads=4, dstate=64, chunk=64, dtype="fp32"))
     assert (f["sp_group_chunks"], f["sp_groups"], f["sp_columns"], f["sp_workgroups"], f["scan"],
-            f["co_head_blocked"]) == (1, 4, 64, 16, 1, 0)
+            f["co_head_blocked"], f["fused"]) == (1, 9, 64, 36, 1, 0, 0)
     f2 = ssd.ssd_plan(_p(seqlen=16384, nheads=32, dstate=256, chunk=256, dtype="fp32"))
     assert (f2["sp_group_chunks"], f2["sp_groups"], f2["sp_workgroups"]) == (32, 2, 256)
     # fp32 chunk output: two waves (one row tile each) for 64-token chunks below 1024
     # workgroups, else Q threads (Q/64 waves with two row tiles each)
-    assert (f["co_workgroups"], f["co_threads"]) == (16, 128)
+    assert (f["co_workgroups"], f["co_threads"]) == (36, 128)
     f3 = ssd.ssd_plan(_p(batch=2, seqlen=4096, nheads=16, dstate=128, chunk=64, dtype="fp32"))
     assert (f3["co_workgroups"], f3["co_threads"]) == (2048, 64)
     assert ssd.ssd_plan(_p(batch=2, seqlen=4096, nheads=7, dstate=128, chunk=64, dtype="fp32"))["co_threads"] == 128
@@ -298,6 +307,13 @@ def test_plan_candidates(kw):
     keys = [tuple(sorted(c.items())) for c in cands]
     assert len(set(keys)) == len(keys)
     nc = p.nchunks
+    fused = [c for c in cands if c["fused"]]
+    if fused:   # the one-launch forward: one workgroup of 256 threads per (batch, head, chunk)
+        assert len(fused) == 1 and fused[0] == ssd.ssd_plan(p)
+        assert (fused[0]["co_workgroups"], fused[0]["co_threads"], fused[0]["sp_workgroups"]) == (
+            nc * p.batch * p.nheads, 256, 0)
+        assert ssd.ssd_workspace_bytes_planned(p, fused[0]) > 0
+        cands = [c for c in cands if not c["fused"]]
     for c in cands:
         assert ssd.ssd_workspace_bytes_planned(p, c) > 0
         K, ng = c["sp_group_chunks"], c["sp_groups"]

@@ -41,7 +41,10 @@ def _check_contract(d, steps, warmup, workload):
     # achieved = algorithmic bytes per launch / mean launch time
     assert abs(r["achieved"] - r["algorithmic_bytes_per_launch"] / (r["mean_launch_us"] * 1e-6) / 1e9) \
         < 0.01 * r["achieved"] + 1
-    assert set(d["kernels"]) == {"chunk_cumsum", "state_pass", "group_scan", "chunk_out"}
+    if d["plan"]["fused"]:   # the one-launch forward
+        assert set(d["kernels"]) == {"forward_small"} and r["kernel"] == "forward_small"
+    else:
+        assert set(d["kernels"]) == {"chunk_cumsum", "state_pass", "group_scan", "chunk_out"}
     assert d["plan"]["sp_groups"] >= 1
 
 
@@ -60,7 +63,7 @@ def test_bench_line_fp32_with_cpu_baseline(monkeypatch, capsys):
     d = _run(monkeypatch, capsys, "--steps", "3", "--warmup", "2", "--kernel-reps", "6",
              "--cold-reps", "0", "--cpu-budget", "0.5", "--workload", wl)
     _check_contract(d, 3, 2, wl)
-    assert d["dtype"] == "f32"
+    assert d["dtype"] == "f32" and d["plan"]["fused"] == 1
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s" and cb["value"] > 0
     assert cb["cores"] >= 1 and cb["threads"] >= 1 and cb["usable_cores"] >= 1 and cb["sample"]

@@ -127,3 +127,50 @@ def test_autotune_picks_a_candidate(w, scale):
     check(f64(y), ref["y"], TOL[w.dtype], "y under the tuned plan")
     check(f64(hT), ref["hT"], TOL[w.dtype], "hT under the tuned plan")
     assert np.isfinite(f64(y)).all()
+
+
+# the one-launch forward (fp32, 64-token chunks, dstate 64 or 128, at most 8 chunks)
+FUSED = [
+    (_wl("fused_n64_8chunks", "fp32", 2, 512, 3, 64, 1, 64), 1.0),       # the longest chain
+    (_wl("fused_n128_g2_ragged", "fp32", 1, 450, 4, 128, 2, 64), 1e-2),  # ragged, 2 B/C groups
+    (_wl("fused_one_chunk", "fp32", 3, 40, 2, 64, 1, 64, h0=False), 1.0),  # one partial chunk
+]
+
+
+@pytest.mark.parametrize("w,scale", FUSED, ids=[w.name for w, _ in FUSED])
+def test_one_launch_forward(w, scale):
+    """The one-launch plan against the oracle and against the general four-launch path,
+    with and without the final state; the stage-1 values it leaves in the workspace equal
+    ssd_chunk_cumsum's bit for bit."""
+    dev = require_gpu()
+    inp = _inputs(w, scale)
+    d = to_dev(inp, dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    plan = ssd.ssd_plan(prob)
+    assert plan["fused"] == 1
+    print(f"case {w.name}: {plan}", flush=True)
+    ws = ssd.workspace_for(prob, dev)
+    ws.fill_(0xFF)
+    y, hT = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                            chunk=w.chunk, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["h0"], chunk=w.chunk)
+    tol = TOL[w.dtype]
+    check(f64(y), ref["y"], tol, "y (one launch)")
+    check(f64(hT), ref["hT"], tol, "hT (one launch)")
+    G2, dtT = ssd.ssd_chunk_cumsum(prob, d["dt"], d["A"])
+    torch.cuda.synchronize()
+    v = ssd.workspace_views(prob, ws)
+    assert torch.equal(v["G2"], G2) and torch.equal(v["dtT"], dtT)
+    general = [c for c in ssd.plan_candidates(prob) if not c["fused"]][0]
+    y2, h2 = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                             chunk=w.chunk, launch_plan=general)
+    torch.cuda.synchronize()
+    check_dev(y, y2, tol, "y: one launch against the general path")
+    check_dev(hT, h2, tol, "hT: one launch against the general path")
+    y3 = torch.full_like(y, float("nan"))
+    ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=w.chunk,
+                    y=y3, want_final=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y3, y)
