@@ -109,20 +109,6 @@ struct SpCfg {
     static_assert(Q % TS == 0, "sub-steps per chunk");
 };
 
-// s_waitcnt immediate with vmcnt = n and expcnt, lgkmcnt at their maxima (gfx9 encoding)
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-// f(std::integral_constant<int, i>) for i = 0 .. n - 1, unrolled at compile time
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
-{
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F> __device__ __forceinline__ void static_for(F &&f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS stores written as inline assembly.  The compiler cannot tell which LDS bytes a
@@ -1875,7 +1861,7 @@ static LaunchPlan plan_fused(const Shape &s)
     lp.co_head_blocked = 0;
     lp.co_heads_per_block = 1;
     lp.co_column_split = 1;
-    lp.co_workgroups = (int)(s.b * s.H * s.nc);
+    lp.co_workgroups = (int)forward_small_workgroups(s);
     lp.co_threads = 256;
     lp.sp_register_transposed = 0;
     lp.sp_threads = 0;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ssd {
 
 typedef __bf16 bf16;
@@ -213,6 +215,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     r[0] = (bf16)lo;
     r[1] = (bf16)hi;
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------------------
+// s_waitcnt immediate with vmcnt = n and expcnt, lgkmcnt at their maxima (gfx9 encoding)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// f(std::integral_constant<int, i>) for i = 0 .. n - 1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace ssd

@@ -89,11 +89,13 @@ hipError_t launch_chunk_out_corrected(const Shape &s, const LaunchPlan &lp, cons
 int chunk_out_f32_threads(const Shape &s);
 
 // The whole forward in one launch for fp32 problems of at most kSmallMaxChunks chunks of 64
-// tokens, headdim 64, dstate 64 or 128 (ssd_small.hip): one workgroup per (batch, head,
-// chunk) walks the jump over the earlier chunks and computes its chunk's output; writes y,
-// hT (may be NULL) and the chunk cumsum and dt into G2 and dtT.
+// tokens, headdim 64, dstate 64 (ssd_small.hip): one workgroup per (batch, head, chunk,
+// half of the headdim rows) walks the jump over the earlier chunks and computes its
+// chunk's output, one more per (batch, head, half) the final state; writes y, hT (may be
+// NULL) and the chunk cumsum and dt into G2 and dtT.
 constexpr int kSmallMaxChunks = 8;
 bool forward_small_eligible(const Shape &s);
+int64_t forward_small_workgroups(const Shape &s);
 hipError_t launch_forward_small(const Shape &s, const void *x, const void *dt, const float *A,
                                 const void *B, const void *C, const float *D, const float *h0,
                                 void *y, float *hT, float *G2, float *dtT, hipStream_t st);

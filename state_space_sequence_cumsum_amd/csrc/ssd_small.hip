@@ -7,57 +7,200 @@
 //
 // With a few chunks per sequence the four launches of the general path (cumsum, state
 // pass, group scan, chunk output) and their memory round trips take longer than the
-// arithmetic.  Here one workgroup per (batch, head, chunk c) does all of it: it walks the
-// jump over chunks 0 .. c-1 itself (every workgroup repeats the state work of the chunks
-// before its own, which the planner bounds by allowing this kernel for short chains
-// only), keeps the chunk-start state in LDS and computes chunk c's output from it.  Only
-// y, the final state (from the last chunk's workgroup) and chunk c's cumsum and dt (the
-// stage-1 values the forward leaves in its workspace) go to memory.  The arithmetic of
-// every step is the general path's: the same cumsum and weights bit for bit, the same
-// products on fp32 MFMA (v_mfma_f32_32x32x2f32), the state stored in fp32.
+// arithmetic.  Here the state rows are split in two halves (headdim 64 = 2 x 32 rows p;
+// the rows of the state and of y do not depend on one another), and one workgroup per
+// (batch, head, chunk c, half) does all of it for its 32 rows:
+//   * the cumsum of chunks 0 .. c (the general path's arithmetic, so G2 and dt equal the
+//     stage-1 kernel's bit for bit; they go to the workspace from chunk c's workgroups);
+//   * the intra-chunk term of chunk c's output, x^T M with M[j][i] = (i >= j) C_i.B_j
+//     exp2(G_i - G_j) dt_j, while the tiles of the chain are still arriving;
+//   * the jump h <- exp2(G_last) h + X^T (w B) over chunks 0 .. c-1 from the zero state (or
+//     h0), every workgroup repeating the state work of the chunks before its own (bounded by
+//     allowing this kernel for short chains only);
+//   * the inter-chunk term exp2(G_i) h C^T, then y = both terms + D x.
+// One more workgroup per (batch, head, half) walks the jump over all chunks and writes the
+// final state.  Products run on fp32 MFMA (v_mfma_f32_32x32x2f32).  Every tile of x and B
+// the chain needs is requested at the start with 16-byte global-to-LDS loads into a ring of
+// four chunk slots, so their latency is paid about once.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-// Chunks of 64 tokens, headdim 64, dstate 64 * NT; 256 threads (four waves).
-//   jump:   wave w keeps h[p][n] (fp32 MFMA accumulators, row p, column n) for the 32 rows
-//           p of half w % 2 and, in each 64-column tile of n, the 32 columns of half w / 2;
-//   output: wave w computes Y^T[p][i] for the rows p of half w % 2 and the 32 tokens i of
-//           row tile I = w / 2.
-template <int NT>
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// LDS stores as inline assembly: before an ordinary store the compiler waits for every
+// global-to-LDS load in flight, since it cannot tell which LDS bytes those write.  These
+// stores go only to buffers no such load writes; the barrier below waits for them.
+__device__ __forceinline__ void st_lds32(float *p, float v)
+{
+    asm volatile("ds_write_b32 %0, %1" ::"v"((uint32_t)(uintptr_t)(lds_ptr_t *)p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_lds128(float *p, f32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" ::"v"((uint32_t)(uintptr_t)(lds_ptr_t *)p), "v"(v) : "memory");
+}
+
+}  // namespace
+
+// A workgroup barrier that waits for this wave's LDS operations (lgkmcnt) only, not for its
+// global loads in flight, as __syncthreads() would.
+#define FS_BARRIER()                                                                            \
+    do {                                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");                         \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+
+// Chunks of 64 tokens, headdim 64 in two halves of 32 rows, dstate 64; 256 threads (four
+// waves).  Wave w:
+//   chain:  state columns n in 32 (w & 1) + [0, 32), tokens 32 (w >> 1) + [0, 32) of each
+//           chunk (the two token halves keep partial states, summed where read);
+//   output: token tile I = w >> 1 of Y^T[p][i], contraction half w & 1 (the partials are
+//           summed in LDS before the store); waves 0, 1, 2 compute the C B^T tiles
+//           (J, I) = (0, 0), (0, 1), (1, 1).
 __global__ __launch_bounds__(256) void forward_small_f32_kernel(
     const float *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ D,
     const float *__restrict__ h0, float *__restrict__ y, float *__restrict__ hT,
     float *__restrict__ G2, float *__restrict__ dtT, int L, int H, int G, int nc, int Lp)
 {
-    constexpr int Q = 64, P = 64, N = 64 * NT, XP = Q + 4, SSP = N + 4, NF = N / 16;
-    __shared__ __attribute__((aligned(16))) float XT[P * XP];     // x^T [p][token]
-    __shared__ __attribute__((aligned(16))) float WT[N * XP];     // (w B)^T [n][token]
-    __shared__ __attribute__((aligned(16))) float Ss[P * SSP];    // chunk-start state [p][n]
-    __shared__ float Gs[Q], Ds[Q], Ws[Q];   // cumsum (log2 e scaled), dt, jump weight
-    __shared__ float alpha_s;               // exp2(cumsum at the chunk's end)
+    constexpr int Q = 64, P = 64, PW = 32, N = 64, NF = N / 16;
+    constexpr int R = 4;                          // ring slots
+    constexpr int XI = 2, BI = 4, CI = XI + BI;   // 1 KB loads per wave: x half-rows, B rows, a chunk
+    constexpr int MP = Q + 4, SSP = N + 4, YP = PW + 4;
+    // ring slot: x half-rows of a chunk [token][p], then its B rows [token][n] (one array per
+    // slot, so the compiler tells the slots apart when it places waits for loads into LDS)
+    constexpr int SLOT = Q * PW + Q * N;
+    __shared__ __attribute__((aligned(16))) float R0[SLOT], R1[SLOT], R2[SLOT], R3[SLOT];
+    __shared__ __attribute__((aligned(16))) float XC[Q * PW];         // x half-rows of chunk c [j][p]
+    __shared__ __attribute__((aligned(16))) float MT[Q * MP];         // M^T [i][j]; later y partials
+    __shared__ __attribute__((aligned(16))) float Ss[2 * PW * SSP];   // state partials [p][n]
+    __shared__ __attribute__((aligned(16))) float Gs[kSmallMaxChunks * Q];   // cumsum, log2 e scaled
+    __shared__ __attribute__((aligned(16))) float Ws[kSmallMaxChunks * Q];   // jump weights
+    __shared__ __attribute__((aligned(16))) float Ds[Q];                     // dt of chunk c
+    __shared__ float Al[kSmallMaxChunks];                                    // exp2(chunk-end cumsum)
+    auto xsl = [&](auto k) -> float * {
+        constexpr int j = decltype(k)::value;
+        return j == 0 ? R0 : (j == 1 ? R1 : (j == 2 ? R2 : R3));
+    };
+    auto bsl = [&](auto k) -> float * { return xsl(k) + Q * PW; };
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hl = lane >> 5, kq = 8 * hl;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int c = blockIdx.x % nc, bh = blockIdx.x / nc;
+    const int ncw = nc + 1;
+    const int pw = blockIdx.x & 1, rest = blockIdx.x >> 1;
+    const int c = rest % ncw, bh = rest / ncw;
+    const bool out = c < nc;                 // chunk c's output (else the final state)
+    if (!out && hT == nullptr) return;
+    const int nchain = out ? c : nc;         // chunks the jump walks
+    const int ncs = out ? c + 1 : nc;        // chunks whose cumsum is needed
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
-    const float *xb = x + (int64_t)b * L * xrow + (int64_t)h * P;
+    const float *xb = x + (int64_t)b * L * xrow + (int64_t)h * P + PW * pw;
     const float *Bb = Bm + (int64_t)b * L * brow + (int64_t)g * N;
     const float *Cb = Cm + (int64_t)b * L * brow + (int64_t)g * N;
+    float *yb = y + (int64_t)b * L * xrow + (int64_t)h * P + PW * pw;
     const float a = A[h];
-    const int ph = w & 1, nh = w >> 1;
-    const int kq = 8 * (lane >> 5);
+    const int tn = w & 1, kt = w >> 1;       // chain: column tile, token half
+    const int I = w >> 1, kh = w & 1;        // output: token tile, contraction half
+    const int t0c = c * Q, lastc = min(L - t0c, Q) - 1;   // chunk c (output workgroups)
 
-    // wave 0: chunk ck's cumsum, dt and weights into LDS, the arithmetic of the stage-1
-    // kernel for 64-token chunks (one token per lane, a 64-lane shuffle scan; padded
-    // tokens get dt = 0 and repeat the last valid cumsum value)
-    auto cumsum = [&](int ck, bool write_out) {
-        if (w != 0) return;
-        const int t0 = ck * Q, t = t0 + lane;
-        const float d = t < L ? dt[((int64_t)b * L + t) * H + h] : 0.0f;
+    // -- loads, in the order the waits below count them: dt, C and B rows and h0 into
+    //    registers, then x of chunk c and the first R chunks of the chain into LDS.  Every
+    //    wave issues the same loads whatever the workgroup's role (an unused one reads an
+    //    empty buffer range or a clamped row), so the compiler's own wait counts stay exact.
+    float dv[2];
+    {
+        // dt of token t at byte t H 4 from (b, 0, h): tokens at or past L are out of range (0)
+        const rsrc_t dr = make_rsrc(dt + (int64_t)b * L * H + h, (int)((L * (int64_t)H - h) * 4));
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            dv[r] = __uint_as_float(buf_load_b32(dr, (uint32_t)(((w + 4 * r) * Q + lane) * H * 4)));
+    }
+    // C rows for h C^T; B and C rows for the C B^T tile (the final-state workgroup's
+    // clamped rows are row L-1)
+    f32x8 cs[NF / 2], bf[NF], cf[NF];
+    const int cbJ = (w == 2) ? 1 : 0, cbI = (w == 0) ? 0 : 1;
+    {
+        const float *cr = Cb + (int64_t)(t0c + min(I * 32 + l32, lastc)) * brow + (N / 2) * kh + kq;
+#pragma unroll
+        for (int f = 0; f < NF / 2; ++f) cs[f] = load_frag<float>(cr + 16 * f);
+        const float *br = Bb + (int64_t)(t0c + min(cbJ * 32 + l32, lastc)) * brow + kq;
+        const float *cr2 = Cb + (int64_t)(t0c + min(cbI * 32 + l32, lastc)) * brow + kq;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            bf[f] = load_frag<float>(br + 16 * f);
+            cf[f] = load_frag<float>(cr2 + 16 * f);
+        }
+    }
+    // the initial state (h0's rows of this half, or zero) in the first token half's partial
+    f32x16 acc;
+    {
+        const bool hz = h0 == nullptr || kt != 0;
+        const rsrc_t hr = make_rsrc(hz ? (const float *)x : h0 + ((int64_t)bh * P + PW * pw) * N,
+                                    hz ? 0 : PW * N * 4);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            acc[v] = __uint_as_float(buf_load_b32(hr, (uint32_t)((acc_row(v, lane) * N + 32 * tn + l32) * 4)));
+    }
+    // 1 KB loads: x half-rows (8 rows of 32 floats each), B rows (4 rows of 64 floats each);
+    // rows past the end of the sequence fall outside the buffer range and read as zero
+    uint32_t xoff[XI], boff[BI];
+#pragma unroll
+    for (int k = 0; k < XI; ++k)
+        xoff[k] = (uint32_t)(((w * XI + k) * 8 + lane / 8) * xrow * 4 + 16 * (lane % 8));
+#pragma unroll
+    for (int k = 0; k < BI; ++k)
+        boff[k] = (uint32_t)(((w * BI + k) * 4 + lane / 16) * brow * 4 + 16 * (lane % 16));
+    auto dma_x = [&](float *dst, int ck) {
+        const int t0 = ck * Q;
+        const rsrc_t r = make_rsrc(xb + t0 * xrow, (int)((L - t0) * xrow * 4));
+#pragma unroll
+        for (int k = 0; k < XI; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t *)(dst + (w * XI + k) * 256), 16,
+                                                     (int)xoff[k], 0, 0, 0);
+    };
+    auto dma_b = [&](float *dst, int ck) {
+        const int t0 = ck * Q;
+        const rsrc_t r = make_rsrc(Bb + t0 * brow, (int)((L - t0) * brow * 4));
+#pragma unroll
+        for (int k = 0; k < BI; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t *)(dst + (w * BI + k) * 256), 16,
+                                                     (int)boff[k], 0, 0, 0);
+    };
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);   // the register loads go out first
+    // (chunk c past the end for the final-state workgroup, and ring chunks at or past
+    // nchain, read empty ranges: their slots are never read)
+    auto ring_chunk = [&](int ck) { return ck < nchain ? ck : nc; };
+    dma_x(XC, c);
+    static_for<R>([&](auto jc) {
+        dma_x(xsl(jc), ring_chunk(decltype(jc)::value));
+        dma_b(bsl(jc), ring_chunk(decltype(jc)::value));
+    });
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // at most k chunks of the ring still in flight for this wave
+    auto wait_chunks = [](int k) {
+        if (k <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(CI));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CI));
+    };
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 1) * CI));   // everything above but ring chunks 1 .. R-1
+
+    // -- cumsum of chunks 0 .. ncs-1, chunk ck on wave ck % 4: the stage-1 kernel's
+    //    arithmetic for 64-token chunks (a 64-lane shuffle scan; padded tokens get dt = 0 and
+    //    repeat the last valid cumsum value)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int ck = w + 4 * r;
+        const bool used = ck < ncs;   // (the scan runs either way: a use of dv under a branch
+                                      // would pull its load into the branch)
+        const int t0 = min(ck, nc - 1) * Q;
+        const float d = dv[r];
         float part = a * d;
         asm volatile("" : "+v"(part));   // the rounded product, as the stage-1 kernel sums it
         float incl = part;
@@ -73,172 +216,171 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
         float glast = __shfl((excl + part) * kLog2e, 63, 64);
         if (last < Q - 1) glast = tail;
         const float gt = (lane <= last) ? (excl + part) * kLog2e : tail;
-        Gs[lane] = gt;
-        Ds[lane] = d;
-        Ws[lane] = d * fast_exp2(glast - gt);
-        if (lane == 0) alpha_s = fast_exp2(glast);
-        if (write_out) {
-            G2[(int64_t)bh * Lp + t] = gt;
-            dtT[(int64_t)bh * Lp + t] = d;
-        }
-    };
-    // chunk ck's x^T into XT and, with `jump`, (w B)^T into WT (rows past L are clamped to
-    // row L-1; their weight is 0 and their outputs are not stored)
-    const int st = tid >> 2, sq = tid & 3;   // staging: token, quarter of the row
-    auto stage = [&](int ck, bool jump) {
-        const int64_t tr = min(ck * Q + st, L - 1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int p0 = sq * 16 + 4 * r;
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(xb + tr * xrow + p0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) XT[(p0 + e) * XP + st] = v[e];
-        }
-        if (jump) {
-            const float wt = Ws[st];
-#pragma unroll
-            for (int r = 0; r < 4 * NT; ++r) {
-                const int n0 = sq * 16 * NT + 4 * r;
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(Bb + tr * brow + n0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) WT[(n0 + e) * XP + st] = wt * v[e];
+        if (!used) continue;
+        st_lds32(&Gs[t0 + lane], gt);
+        st_lds32(&Ws[t0 + lane], d * fast_exp2(glast - gt));
+        if (lane == 0) st_lds32(&Al[ck], fast_exp2(glast));
+        if (out && ck == c) {
+            st_lds32(&Ds[lane], d);
+            if (pw == 0) {
+                G2[(int64_t)bh * Lp + t0 + lane] = gt;
+                dtT[(int64_t)bh * Lp + t0 + lane] = d;
             }
         }
-    };
-
-    // the state, zero or h0
-    f32x16 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = zero_acc();
-    if (h0 != nullptr) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[t][v] = h0[((int64_t)bh * P + ph * 32 + acc_row(v, lane)) * N + 64 * t + 32 * nh + (lane & 31)];
     }
-    // h <- exp2(G_last) h + X^T (w B) over the staged chunk
-    auto jump = [&]() {
-        const float al = alpha_s;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[t][v] *= al;
-        const float *arow = XT + (ph * 32 + (lane & 31)) * XP + kq;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float *brw = WT + (64 * t + 32 * nh + (lane & 31)) * XP + kq;
-#pragma unroll
-            for (int ks = 0; ks < Q / 16; ++ks)
-                mma(acc[t], load_frag<float>(arow + 16 * ks), load_frag<float>(brw + 16 * ks));
-        }
-    };
+    FS_BARRIER();
 
-    // the chunks before this one
-    for (int ck = 0; ck < c; ++ck) {
-        cumsum(ck, false);
-        __syncthreads();
-        stage(ck, true);
-        __syncthreads();
-        jump();
-        __syncthreads();
-    }
-
-    // this chunk: its start state to LDS; the last chunk's workgroup also takes the jump
-    // over it for the final state
-    const bool fin = (c == nc - 1) && hT != nullptr;
-    cumsum(c, true);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            Ss[(ph * 32 + acc_row(v, lane)) * SSP + 64 * t + 32 * nh + (lane & 31)] = acc[t][v];
-    __syncthreads();
-    stage(c, fin);
-    __syncthreads();
-    if (fin) {
-        jump();
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                hT[((int64_t)bh * P + ph * 32 + acc_row(v, lane)) * N + 64 * t + 32 * nh + (lane & 31)] = acc[t][v];
-    }
-
-    // chunk output: Y^T = exp2(G_i) S C^T + (dt x)^T M, M[j, i] = (i >= j) C_i.B_j exp2(G_i - G_j)
-    const int I = w >> 1, i_loc = I * 32 + (lane & 31);
-    const int t0 = c * Q, last = min(L - t0, Q) - 1;
-    f32x8 cf[NF];   // C row i_loc (clamped), all N
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-        cf[f] = load_frag<float>(Cb + (int64_t)(t0 + min(i_loc, last)) * brow + 16 * f + kq);
+    // -- chunk c's intra-chunk term: Y^T[p][i] = sum_j x^T[p][j] M[j][i]
     f32x16 ya = zero_acc();
-    const float *srow = Ss + (ph * 32 + (lane & 31)) * SSP + kq;
+    if (out) {
+        if (w < 3) {   // C B^T tile (J, I) on MFMA (rows j, column i), then M^T into LDS
+            f32x16 cb = zero_acc();
 #pragma unroll
-    for (int f = 0; f < NF; ++f) mma(ya, load_frag<float>(srow + 16 * f), cf[f]);
-    const float gi = Gs[i_loc];
-    const float si = fast_exp2(gi);
+            for (int f = 0; f < NF; ++f) mma(cb, bf[f], cf[f]);
+            const int i = cbI * 32 + l32;
+            const float gi = Gs[t0c + i];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) ya[v] *= si;
-    for (int J = 0; J <= I; ++J) {
-        // C B^T tile (rows j of tile J, column i) on MFMA: A = B rows, B = C rows
-        f32x16 cb = zero_acc();
-        const float *brw = Bb + (int64_t)(t0 + min(J * 32 + (lane & 31), last)) * brow + kq;
+            for (int q = 0; q < 4; ++q) {
+                f32x4 m;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) mma(cb, load_frag<float>(brw + 16 * f), cf[f]);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            f32x8 m;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = J * 32 + acc_row(8 * s + e, lane);
-                const float val = cb[8 * s + e] * fast_exp2(gi - Gs[jj]) * Ds[jj];
-                m[e] = (i_loc >= jj) ? val : 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    const int j = cbJ * 32 + acc_row(4 * q + e, lane);
+                    const float val = cb[4 * q + e] * fast_exp2(gi - Gs[t0c + j]) * Ds[j];
+                    m[e] = (i >= j) ? val : 0.0f;
+                }
+                st_lds128(&MT[i * MP + cbJ * 32 + 8 * q + 4 * hl], m);
             }
-            // x^T fragment in m's token order: 4 tokens at J*32 + 16 s + 4 (lane / 32), then
-            // 4 more 8 tokens further on
-            const float *ar = XT + (ph * 32 + (lane & 31)) * XP + J * 32 + 16 * s + 4 * (lane >> 5);
-            const f32x4 lo = *reinterpret_cast<const f32x4 *>(ar);
-            const f32x4 hi = *reinterpret_cast<const f32x4 *>(ar + 8);
+        }
+        FS_BARRIER();
+        // tokens j of this wave's contraction half: I = 0: 16 kh + [0, 16); I = 1: 32 kh + [0, 32)
+        const float *mrow = MT + (I * 32 + l32) * MP;
+        auto xm = [&](int j0) {
             f32x8 xa;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { xa[e] = lo[e]; xa[4 + e] = hi[e]; }
-            mma(ya, xa, m);
+            for (int e = 0; e < 8; ++e) xa[e] = XC[(j0 + kq + e) * PW + l32];
+            mma(ya, xa, load_frag<float>(mrow + j0 + kq));
+        };
+        if (I == 0) {
+            xm(16 * kh);
+        } else {
+            xm(32 * kh);
+            xm(32 * kh + 16);
         }
     }
-    // y_i = Y_i + D x_i
-    if (i_loc <= last) {
-        const float Dh = D[h];
-        float *yr = y + ((int64_t)b * L + t0 + i_loc) * xrow + (int64_t)h * P;
+
+    // -- the chain: h <- exp2(G_last) h + X^T (w B) over chunks 0 .. nchain-1
+    auto jump = [&](const float *Xk, const float *Bk, int ck) {
+        const float al = Al[ck];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int p = ph * 32 + acc_row(v, lane);
-            yr[p] = ya[v] + Dh * XT[p * XP + i_loc];
+        for (int v = 0; v < 16; ++v) acc[v] *= al;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int tb = 32 * kt + 16 * f + kq;
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&Ws[ck * Q + tb]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&Ws[ck * Q + tb + 4]);
+            f32x8 xa, ba;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xa[e] = Xk[(tb + e) * PW + l32] * (e < 4 ? w0[e] : w1[e - 4]);
+                ba[e] = Bk[(tb + e) * N + 32 * tn + l32];
+            }
+            mma(acc, xa, ba);
         }
+    };
+    for (int ck0 = 0; ck0 < nchain; ck0 += R)
+        static_for<R>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int ck = ck0 + j;
+            if (ck < nchain) {
+                if (ck >= 1) {
+                    // issued so far: ring chunks 0 .. max(R - 1, min(ck - 2 + R, nchain - 1))
+                    wait_chunks(max(R - 1, min(ck - 2 + R, nchain - 1)) - ck);
+                    FS_BARRIER();   // chunk ck is in; every wave is done with slot (ck - 1) % R
+                    const int nx = ck - 1 + R;
+                    if (nx < nchain) {
+                        const std::integral_constant<int, (j + R - 1) % R> js{};
+                        dma_x(xsl(js), nx);
+                        dma_b(bsl(js), nx);
+                    }
+                }
+                jump(xsl(jc), bsl(jc), ck);
+            }
+        });
+
+    // -- the state after the chain (one partial per token half) into LDS; no load into LDS
+    //    stays in flight past this point (ring slot 0 is reused below)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    {
+        float *sp = Ss + kt * PW * SSP + 32 * tn + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st_lds32(sp + acc_row(v, lane) * SSP, acc[v]);
+    }
+    FS_BARRIER();
+
+    if (!out) {   // the final state: the two partials summed
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int pc = tid + 256 * r, p = pc >> 4, n4 = 4 * (pc & 15);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(&Ss[p * SSP + n4]);
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(&Ss[(PW + p) * SSP + n4]);
+            *reinterpret_cast<f32x4 *>(hT + ((int64_t)bh * P + PW * pw + p) * N + n4) = s0 + s1;
+        }
+        return;
+    }
+
+    // -- chunk c's inter-chunk term: Y^T += exp2(G_i) h C^T (contraction half kh of n)
+    {
+        f32x16 sc = zero_acc();
+#pragma unroll
+        for (int f = 0; f < NF / 2; ++f) {
+            const int n0 = (N / 2) * kh + 16 * f + kq;
+            const f32x8 s0 = load_frag<float>(Ss + l32 * SSP + n0);
+            const f32x8 s1 = load_frag<float>(Ss + (PW + l32) * SSP + n0);
+            mma(sc, s0 + s1, cs[f]);
+        }
+        const float si = fast_exp2(Gs[t0c + I * 32 + l32]);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ya[v] += si * sc[v];
+    }
+    // the partials to LDS as [i][p] (half kh = 0 over M^T, half 1 over ring slot 0), then
+    // y_i = both + D x_i, one 16-byte store per 4 columns
+    {
+        float *yp = (kh == 0 ? MT : R0) + (I * 32 + l32) * YP;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            st_lds128(yp + 8 * q + 4 * hl, f32x4{ya[4 * q], ya[4 * q + 1], ya[4 * q + 2], ya[4 * q + 3]});
+    }
+    FS_BARRIER();
+    const float Dh = D[h];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int pc = tid + 256 * r, i = pc >> 3, p4 = 4 * (pc & 7);
+        if (i > lastc) continue;
+        const f32x4 y0 = *reinterpret_cast<const f32x4 *>(&MT[i * YP + p4]);
+        const f32x4 y1 = *reinterpret_cast<const f32x4 *>(&R0[i * YP + p4]);
+        const f32x4 xv = *reinterpret_cast<const f32x4 *>(&XC[i * PW + p4]);
+        *reinterpret_cast<f32x4 *>(yb + (int64_t)(t0c + i) * xrow + p4) = y0 + y1 + Dh * xv;
     }
 }
+#undef FS_BARRIER
 
 bool forward_small_eligible(const Shape &s)
 {
-    return !s.bf16 && s.Q == 64 && s.P == 64 && (s.N == 64 || s.N == 128) && s.nc <= kSmallMaxChunks &&
-           s.b * s.H * s.nc * 256 < (int64_t(1) << 31);
+    return !s.bf16 && s.Q == 64 && s.P == 64 && s.N == 64 && s.nc <= kSmallMaxChunks && s.H <= 65536 &&
+           s.b * s.H * (s.nc + 1) * 2 * 256 < (int64_t(1) << 31) &&
+           s.L * s.H * s.P * 4 < (int64_t(1) << 31) && s.L * s.G * s.N * 4 < (int64_t(1) << 31);
 }
+
+int64_t forward_small_workgroups(const Shape &s) { return 2 * s.b * s.H * (s.nc + 1); }
 
 hipError_t launch_forward_small(const Shape &s, const void *x, const void *dt, const float *A,
                                 const void *B, const void *C, const float *D, const float *h0,
                                 void *y, float *hT, float *G2, float *dtT, hipStream_t st)
 {
-    const dim3 grid((unsigned)(s.b * s.H * s.nc)), block(256);
-    if (s.N == 64)
-        hipLaunchKernelGGL((forward_small_f32_kernel<1>), grid, block, 0, st, (const float *)x,
-                           (const float *)dt, A, (const float *)B, (const float *)C, D, h0,
-                           (float *)y, hT, G2, dtT, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
-                           (int)s.Lp);
-    else
-        hipLaunchKernelGGL((forward_small_f32_kernel<2>), grid, block, 0, st, (const float *)x,
-                           (const float *)dt, A, (const float *)B, (const float *)C, D, h0,
-                           (float *)y, hT, G2, dtT, (int)s.L, (int)s.H, (int)s.G, (int)s.nc,
-                           (int)s.Lp);
+    hipLaunchKernelGGL(forward_small_f32_kernel, dim3((unsigned)forward_small_workgroups(s)), dim3(256),
+                       0, st, (const float *)x, (const float *)dt, A, (const float *)B,
+                       (const float *)C, D, h0, (float *)y, hT, G2, dtT, (int)s.L, (int)s.H,
+                       (int)s.G, (int)s.nc, (int)s.Lp);
     return hipGetLastError();
 }
 

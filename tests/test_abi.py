@@ -234,12 +234,12 @@ def test_launch_plan_per_shape():
     for kw in (dict(chunk=64), dict(dstate=384, chunk=128)):
         q = ssd.ssd_plan(_p(**kw))
         assert q["co_head_blocked"] == 0 and q["co_heads_per_block"] == 1
-    # fp32 with at most 8 chunks of 64 tokens and dstate 64 or 128: the whole forward as one
-    # launch, one 256-thread workgroup per (batch, head, chunk)
+    # fp32 with at most 8 chunks of 64 tokens and dstate 64: the whole forward as one launch,
+    # one 256-thread workgroup per (batch, head, chunk or final state, half of the headdim)
     f0 = ssd.ssd_plan(_p(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32"))
-    assert (f0["fused"], f0["co_workgroups"], f0["co_threads"], f0["sp_workgroups"], f0["scan"]) == (1, 16, 256, 0, 0)
-    assert ssd.ssd_plan(_p(seqlen=512, nheads=4, dstate=128, chunk=64, dtype="fp32"))["fused"] == 1
-    for kw in (dict(seqlen=513), dict(dstate=256), dict(chunk=128), dict(dtype="bf16")):
+    assert (f0["fused"], f0["co_workgroups"], f0["co_threads"], f0["sp_workgroups"], f0["scan"]) == (1, 40, 256, 0, 0)
+    assert ssd.ssd_plan(_p(seqlen=512, nheads=4, dstate=64, chunk=64, dtype="fp32"))["fused"] == 1
+    for kw in (dict(seqlen=513), dict(dstate=128), dict(chunk=128), dict(dtype="bf16")):
         args = dict(seqlen=256, nheads=4, dstate=64, chunk=64, dtype="fp32")
         args.update(kw)
         assert ssd.ssd_plan(_p(**args))["fused"] == 0, kw
@@ -308,10 +308,11 @@ def test_plan_candidates(kw):
     assert len(set(keys)) == len(keys)
     nc = p.nchunks
     fused = [c for c in cands if c["fused"]]
-    if fused:   # the one-launch forward: one workgroup of 256 threads per (batch, head, chunk)
+    if fused:   # the one-launch forward: one workgroup of 256 threads per (batch, head, chunk
+        # or final state, half of the headdim)
         assert len(fused) == 1 and fused[0] == ssd.ssd_plan(p)
         assert (fused[0]["co_workgroups"], fused[0]["co_threads"], fused[0]["sp_workgroups"]) == (
-            nc * p.batch * p.nheads, 256, 0)
+            2 * (nc + 1) * p.batch * p.nheads, 256, 0)
         assert ssd.ssd_workspace_bytes_planned(p, fused[0]) > 0
         cands = [c for c in cands if not c["fused"]]
     for c in cands:

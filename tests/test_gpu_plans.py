@@ -129,11 +129,12 @@ def test_autotune_picks_a_candidate(w, scale):
     assert np.isfinite(f64(y)).all()
 
 
-# the one-launch forward (fp32, 64-token chunks, dstate 64 or 128, at most 8 chunks)
+# the one-launch forward (fp32, 64-token chunks, dstate 64, at most 8 chunks)
 FUSED = [
-    (_wl("fused_n64_8chunks", "fp32", 2, 512, 3, 64, 1, 64), 1.0),       # the longest chain
-    (_wl("fused_n128_g2_ragged", "fp32", 1, 450, 4, 128, 2, 64), 1e-2),  # ragged, 2 B/C groups
+    (_wl("fused_8chunks", "fp32", 2, 512, 3, 64, 1, 64), 1.0),          # the longest chain
+    (_wl("fused_g2_ragged", "fp32", 1, 450, 4, 64, 2, 64), 1e-2),       # ragged, 2 B/C groups
     (_wl("fused_one_chunk", "fp32", 3, 40, 2, 64, 1, 64, h0=False), 1.0),  # one partial chunk
+    (_wl("fused_5chunks_ragged", "fp32", 1, 300, 5, 64, 1, 64), 1.0),   # a ring refill, ragged
 ]
 
 
