@@ -227,11 +227,13 @@ typedef struct {
     int32_t sp_register_transposed; /* 1: the state pass transposes B in registers (256
                                        columns per workgroup), 0: through LDS */
     int32_t sp_threads;         /* threads per state-pass workgroup */
-    int32_t fused;              /* 1: the whole forward as one launch (fp32, chunk 64, dstate
-                                   64 or 128, at most 8 chunks per sequence): one workgroup
-                                   of 256 threads per (batch, head, chunk) walks the jump
-                                   over the earlier chunks and computes its chunk's output;
-                                   the state-pass and scan fields then describe no launch */
+    int32_t fused;              /* 1: the whole forward as one launch (fp32, chunk 64, headdim
+                                   64, dstate 64, at most 8 chunks per sequence): per (batch,
+                                   head) and half of the headdim rows, one workgroup of 256
+                                   threads per chunk walks the jump over the earlier chunks
+                                   and computes its chunk's output, one more the final state
+                                   (co_workgroups = 2 batch nheads (nchunks + 1)); the
+                                   state-pass and scan fields then describe no launch */
 } ssd_launch_plan;
 
 ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan);
