@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
     __shared__ __attribute__((aligned(16))) float R0[SLOT], R1[SLOT], R2[SLOT], R3[SLOT];
     __shared__ __attribute__((aligned(16))) float XC[Q * PW];         // x half-rows of chunk c [j][p]
     __shared__ __attribute__((aligned(16))) float MT[Q * MP];         // M^T [i][j]; later y partials
+    __shared__ __attribute__((aligned(16))) float MT2[32 * YP];       // wave 3's part of tile (0, 1)
     __shared__ __attribute__((aligned(16))) float Ss[2 * PW * SSP];   // state partials [p][n]
     __shared__ __attribute__((aligned(16))) float Gs[kSmallMaxChunks * Q];   // cumsum, log2 e scaled
     __shared__ __attribute__((aligned(16))) float Ws[kSmallMaxChunks * Q];   // jump weights
@@ -109,9 +110,11 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
     const int t0c = c * Q, lastc = min(L - t0c, Q) - 1;   // chunk c (output workgroups)
 
     // -- loads, in the order the waits below count them: dt, C and B rows and h0 into
-    //    registers, then x of chunk c and the first R chunks of the chain into LDS.  Every
-    //    wave issues the same loads whatever the workgroup's role (an unused one reads an
-    //    empty buffer range or a clamped row), so the compiler's own wait counts stay exact.
+    //    registers, then x of chunk c and the first R chunks of the chain into LDS.  The
+    //    loads into LDS are the same for every wave whatever the workgroup's role (an unused
+    //    one reads an empty buffer range), so every register load is followed by at least
+    //    (R - 1) CI of them on every path: after the wait below the compiler knows all the
+    //    register loads complete, and places no waits of its own for them.
     float dv[2];
     {
         // dt of token t at byte t H 4 from (b, 0, h): tokens at or past L are out of range (0)
@@ -120,31 +123,31 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
         for (int r = 0; r < 2; ++r)
             dv[r] = __uint_as_float(buf_load_b32(dr, (uint32_t)(((w + 4 * r) * Q + lane) * H * 4)));
     }
-    // C rows for h C^T; B and C rows for the C B^T tile (the final-state workgroup's
-    // clamped rows are row L-1)
+    // C rows for h C^T; B and C rows for the C B^T tile: (J, I) = (0, 0) on wave 0, (1, 1) on
+    // wave 1, both over all n; (0, 1) on waves 2 and 3, over n in [0, 32) and [32, 64)
     f32x8 cs[NF / 2], bf[NF], cf[NF];
-    const int cbJ = (w == 2) ? 1 : 0, cbI = (w == 0) ? 0 : 1;
-    {
+    const int cbJ = (w == 1) ? 1 : 0, cbI = (w == 0) ? 0 : 1;
+    const int cbF0 = (w == 3) ? NF / 2 : 0, cbNF = (w < 2) ? NF : NF / 2;   // fragments of n
+    if (out) {
         const float *cr = Cb + (int64_t)(t0c + min(I * 32 + l32, lastc)) * brow + (N / 2) * kh + kq;
 #pragma unroll
         for (int f = 0; f < NF / 2; ++f) cs[f] = load_frag<float>(cr + 16 * f);
-        const float *br = Bb + (int64_t)(t0c + min(cbJ * 32 + l32, lastc)) * brow + kq;
-        const float *cr2 = Cb + (int64_t)(t0c + min(cbI * 32 + l32, lastc)) * brow + kq;
+        const float *br = Bb + (int64_t)(t0c + min(cbJ * 32 + l32, lastc)) * brow + 16 * cbF0 + kq;
+        const float *cr2 = Cb + (int64_t)(t0c + min(cbI * 32 + l32, lastc)) * brow + 16 * cbF0 + kq;
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            bf[f] = load_frag<float>(br + 16 * f);
-            cf[f] = load_frag<float>(cr2 + 16 * f);
+        for (int f = 0; f < NF; ++f) {   // (waves 2, 3 use the first NF / 2; a load under a
+                                          // branch would be waited for at the branch's end)
+            const int fl = min(f, NF - 1 - cbF0);
+            bf[f] = load_frag<float>(br + 16 * fl);
+            cf[f] = load_frag<float>(cr2 + 16 * fl);
         }
     }
     // the initial state (h0's rows of this half, or zero) in the first token half's partial
-    f32x16 acc;
-    {
-        const bool hz = h0 == nullptr || kt != 0;
-        const rsrc_t hr = make_rsrc(hz ? (const float *)x : h0 + ((int64_t)bh * P + PW * pw) * N,
-                                    hz ? 0 : PW * N * 4);
+    f32x16 acc = zero_acc();
+    if (h0 != nullptr && kt == 0) {
+        const float *hr = h0 + ((int64_t)bh * P + PW * pw) * N + 32 * tn + l32;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[v] = __uint_as_float(buf_load_b32(hr, (uint32_t)((acc_row(v, lane) * N + 32 * tn + l32) * 4)));
+        for (int v = 0; v < 16; ++v) acc[v] = hr[acc_row(v, lane) * N];
     }
     // 1 KB loads: x half-rows (8 rows of 32 floats each), B rows (4 rows of 64 floats each);
     // rows past the end of the sequence fall outside the buffer range and read as zero
@@ -233,10 +236,11 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
     // -- chunk c's intra-chunk term: Y^T[p][i] = sum_j x^T[p][j] M[j][i]
     f32x16 ya = zero_acc();
     if (out) {
-        if (w < 3) {   // C B^T tile (J, I) on MFMA (rows j, column i), then M^T into LDS
+        {   // C B^T tile (J, I) on MFMA (rows j, column i), then the decayed, masked M^T into LDS
             f32x16 cb = zero_acc();
 #pragma unroll
-            for (int f = 0; f < NF; ++f) mma(cb, bf[f], cf[f]);
+            for (int f = 0; f < NF; ++f)
+                if (f < cbNF) mma(cb, bf[f], cf[f]);
             const int i = cbI * 32 + l32;
             const float gi = Gs[t0c + i];
 #pragma unroll
@@ -248,17 +252,21 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
                     const float val = cb[4 * q + e] * fast_exp2(gi - Gs[t0c + j]) * Ds[j];
                     m[e] = (i >= j) ? val : 0.0f;
                 }
-                st_lds128(&MT[i * MP + cbJ * 32 + 8 * q + 4 * hl], m);
+                if (w == 3) st_lds128(&MT2[l32 * YP + 8 * q + 4 * hl], m);
+                else st_lds128(&MT[i * MP + cbJ * 32 + 8 * q + 4 * hl], m);
             }
         }
         FS_BARRIER();
         // tokens j of this wave's contraction half: I = 0: 16 kh + [0, 16); I = 1: 32 kh + [0, 32)
+        // (tile (0, 1), on wave 2, is the sum of its two parts)
         const float *mrow = MT + (I * 32 + l32) * MP;
         auto xm = [&](int j0) {
             f32x8 xa;
 #pragma unroll
             for (int e = 0; e < 8; ++e) xa[e] = XC[(j0 + kq + e) * PW + l32];
-            mma(ya, xa, load_frag<float>(mrow + j0 + kq));
+            f32x8 mf = load_frag<float>(mrow + j0 + kq);
+            if (w == 2) mf += load_frag<float>(MT2 + l32 * YP + j0 + kq);
+            mma(ya, xa, mf);
         };
         if (I == 0) {
             xm(16 * kh);
