@@ -232,4 +232,33 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ---------------------------------------------------------------------------
+// Wave-wide (64-lane) prefix sums on DPP lane moves, with no LDS round trip per step.
+// The inclusive sum takes Hillis-Steele steps of 1, 2, 4 and 8 lanes within each row of
+// 16 lanes, then carries the row totals across rows (broadcasts of lanes 15 and 31);
+// a lane that receives nothing adds 0.  Every kernel that needs the same sums bit for bit
+// (the stage-1 cumsum and the one-launch forward) uses this one order.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                  ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v)
+{
+    v += dpp_move<0x111, 0xf>(v);   // row_shr:1
+    v += dpp_move<0x112, 0xf>(v);   // row_shr:2
+    v += dpp_move<0x114, 0xf>(v);   // row_shr:4
+    v += dpp_move<0x118, 0xf>(v);   // row_shr:8
+    v += dpp_move<0x142, 0xa>(v);   // row_bcast:15, into rows 1 and 3
+    v += dpp_move<0x143, 0xc>(v);   // row_bcast:31, into rows 2 and 3
+    return v;
+}
+// lane l gets lane l-1's value, lane 0 gets 0 (wave_shr:1)
+__device__ __forceinline__ float wave_shift_up1(float v) { return dpp_move<0x138, 0xf>(v); }
+// lane `src` (the same for every lane of the wave)'s value
+__device__ __forceinline__ float wave_read(float v, int src)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
 }  // namespace ssd

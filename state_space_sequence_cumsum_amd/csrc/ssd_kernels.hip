@@ -20,7 +20,7 @@ namespace ssd {
 // One workgroup per (chunk, block of 4 heads, batch), one wave per head.  The
 // [Q x 4] dt tile is read row by row (heads contiguous) into LDS, then each wave
 // scans its head's Q tokens: every lane sums Q/64 consecutive tokens, a 64-lane
-// shuffle scan adds the lane prefixes, and the results are written
+// scan on DPP lane moves adds the lane prefixes, and the results are written
 // token-contiguous.  Padded tokens (last chunk) get dt = 0 and repeat the last
 // valid cumsum value exactly, so G2 at a chunk's last position is the value at its
 // last valid token.  With wT the same pass also writes each token's state-pass weight
@@ -69,22 +69,15 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__
         run += a * tile[lane * PER + j][hh];
         part[j] = run;
     }
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float up = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += up;
-    }
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0f;
+    const float excl = wave_shift_up1(wave_inclusive_sum(run));
     const int last = min(L - t0, Q) - 1;
     float tail = 0.0f;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
         if (j == last % PER) tail = (excl + part[j]) * kLog2e;
-    tail = __shfl(tail, last / PER, 64);
+    tail = wave_read(tail, last / PER);
     // value at the chunk's last position (the last valid token's on a ragged chunk)
-    float glast = __shfl((excl + part[PER - 1]) * kLog2e, 63, 64);
+    float glast = wave_read((excl + part[PER - 1]) * kLog2e, 63);
     if (last < Q - 1) glast = tail;
     const int64_t base = ((int64_t)b * H + hb + hh) * Lp + t0 + lane * PER;
 #pragma unroll

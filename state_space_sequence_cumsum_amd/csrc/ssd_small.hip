@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((R - 1) * CI));   // everything above but ring chunks 1 .. R-1
 
     // -- cumsum of chunks 0 .. ncs-1, chunk ck on wave ck % 4: the stage-1 kernel's
-    //    arithmetic for 64-token chunks (a 64-lane shuffle scan; padded tokens get dt = 0 and
+    //    arithmetic for 64-token chunks (the 64-lane DPP scan; padded tokens get dt = 0 and
     //    repeat the last valid cumsum value)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -206,17 +206,10 @@ __global__ __launch_bounds__(256) void forward_small_f32_kernel(
         const float d = dv[r];
         float part = a * d;
         asm volatile("" : "+v"(part));   // the rounded product, as the stage-1 kernel sums it
-        float incl = part;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += up;
-        }
-        float excl = __shfl_up(incl, 1, 64);
-        if (lane == 0) excl = 0.0f;
+        const float excl = wave_shift_up1(wave_inclusive_sum(part));
         const int last = min(L - t0, Q) - 1;
-        const float tail = __shfl((excl + part) * kLog2e, last, 64);
-        float glast = __shfl((excl + part) * kLog2e, 63, 64);
+        const float tail = wave_read((excl + part) * kLog2e, last);
+        float glast = wave_read((excl + part) * kLog2e, 63);
         if (last < Q - 1) glast = tail;
         const float gt = (lane <= last) ? (excl + part) * kLog2e : tail;
         if (!used) continue;
