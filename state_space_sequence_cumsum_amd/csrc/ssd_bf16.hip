@@ -1849,7 +1849,8 @@ static bool plan_from(const Shape &s, int K, int ng, int cols, int rt, int co_hb
     return true;
 }
 
-// The one-launch plan (forward_small): one workgroup of 256 threads per (batch, head, chunk)
+// The one-launch plan (forward_small): workgroups of 256 threads, two per (batch, head, chunk)
+// and two more per (batch, head) for the final state
 static LaunchPlan plan_fused(const Shape &s)
 {
     LaunchPlan lp;
