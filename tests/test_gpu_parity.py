@@ -251,6 +251,35 @@ def test_masked_exponent_overflow(dtype):
     _check_forward(w, inp=inp)
 
 
+def test_masked_exponent_overflow_one_launch():
+    """The same on the one-launch fp32 forward (64-token chunks, dstate 64, 8 chunks): within
+    a chunk |G2| passes 1000, and its C B^T tiles select on i >= j as well."""
+    w = _wl("overflow_one_launch", "fp32", 1, 480, 2, 64, 64, 1, 64)
+    inp = make_inputs(w, 6)
+    inp["A"].fill_(-16.0)
+    inp["dt"] = 0.9 + 0.2 * torch.rand(inp["dt"].shape, generator=torch.Generator().manual_seed(6))
+    assert ssd.ssd_plan(ssd.problem_of(inp["x"], inp["B"], w.chunk))["fused"] == 1
+    G2_ref, _ = oracle.chunk_cumsum(inp["dt"], inp["A"], w.chunk)
+    assert np.abs(G2_ref).max() > 1000
+    _check_forward(w, inp=inp)
+
+
+@pytest.mark.parametrize("zero", ["B", "C"])
+def test_degenerate_zero_B_or_C_one_launch(zero):
+    """B = 0 or C = 0 on the one-launch fp32 forward (ragged, 5 chunks): with C = 0, y equals
+    D x rounded once, bit for bit."""
+    w = _wl(f"zero_{zero}_one_launch", "fp32", 2, 300, 3, 64, 64, 1, 64)
+    inp = make_inputs(w, 8)
+    inp[zero].zero_()
+    if zero == "B":
+        inp["A"].mul_(0.01)
+    assert ssd.ssd_plan(ssd.problem_of(inp["x"], inp["B"], w.chunk))["fused"] == 1
+    y, hT, ref = _check_forward(w, inp=inp)
+    if zero == "C":
+        skip = inp["D"][None, None, :, None] * inp["x"]
+        assert torch.equal(y.cpu(), skip)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("zero", ["B", "C"])
 def test_degenerate_zero_B_or_C(dtype, zero):
