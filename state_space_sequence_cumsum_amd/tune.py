@@ -10,14 +10,14 @@ into groups, and the chunk-output kernel (heads per workgroup, or one head).
 
 The state pass and its group scan depend only on the state-pass kernel and the grouping,
 and the chunk output only on its own kernel and on whether the state pass is grouped, so
-the search runs in two rounds instead of over the product:
+the search runs in two passes instead of over the product:
 
 1. every distinct (state-pass kernel, grouping), each with the chunk-output choice of
    the cost model (or the first one the candidates pair with it): stage 1 then stage 2
    (state pass, group scan) launched back to back ``reps`` times between one event pair;
-2. with the fastest of round 1, every chunk-output choice: stage 3 alone ``reps`` times.
+2. with the fastest of pass 1, every chunk-output choice: stage 3 alone ``reps`` times.
 
-The winner of both rounds and the cost model's plan are then timed as whole forwards and
+The winner of both passes and the cost model's plan are then timed as whole forwards and
 the faster is returned, so the search never returns a plan slower than the default by
 its own measurement.  Every launch goes through the C ABI (ssd_forward_planned); this
 module only orders the calls and reads the events.
@@ -55,7 +55,7 @@ def autotune(x, dt, A, B, C, D, h0=None, *, chunk: int, reps: int = 20, warmup: 
 
     Returns a dict with ``plan`` (the chosen candidate, a field-name dict to pass as
     ``launch_plan``), ``default_plan`` (ssd_plan's choice), ``forward_us`` and
-    ``default_forward_us`` (whole forwards under each, event-timed), and the two rounds'
+    ``default_forward_us`` (whole forwards under each, event-timed), and the two passes'
     tables ``state_pass`` and ``chunk_out`` (the varied fields and the microseconds per
     launch).  Candidates whose workspace exceeds ``max_workspace_bytes`` are skipped.
     The inputs are only read; outputs go to scratch tensors.
@@ -83,7 +83,7 @@ def autotune(x, dt, A, B, C, D, h0=None, *, chunk: int, reps: int = 20, warmup: 
         p.run_stage(1)
         p.run_stage(2)
 
-    # round 1: state pass + group scan per (kernel, grouping)
+    # pass 1: state pass + group scan per (kernel, grouping)
     sp_table, seen = [], {}
     for c in cands:
         key = tuple(c[k] for k in SP_KEYS)
@@ -99,7 +99,7 @@ def autotune(x, dt, A, B, C, D, h0=None, *, chunk: int, reps: int = 20, warmup: 
         sp_table.append({**{k: c[k] for k in SP_KEYS}, "us": round(us, 3)})
     best_sp = min(sp_table, key=lambda r: r["us"])
 
-    # round 2: chunk output per kernel choice, with the best state pass
+    # pass 2: chunk output per kernel choice, with the best state pass
     co_table = []
     for c in cands:
         if any(c[k] != best_sp[k] for k in SP_KEYS):
