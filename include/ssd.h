@@ -135,8 +135,9 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
  * jump is linear), combine the group-final states with a short scan and let stage 3 add
  * the carried-in state; S then holds chunk-start states relative to their group (the
  * first chunk of every group after the first, whose state is zero, is not written), and
- * its contents are otherwise unspecified.  h0 may be NULL; hT may be
- * NULL (final state not wanted).  Writes y and hT. */
+ * its contents are otherwise unspecified.  Short fp32 problems (see ssd_launch_plan.fused)
+ * run as one launch that writes G2, dtT, y and hT and leaves S unwritten.  h0 may be NULL;
+ * hT may be NULL (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
                        const float *A, const void *B, const void *C, const float *D,
                        const float *h0, void *y, float *hT, void *workspace,
@@ -148,7 +149,8 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
  * state pass, after the group scan (recorded straight after the previous mark when
  * the state pass runs as one serial chain and no scan is launched) and after stage
  * 3, so each pair of consecutive marks brackets exactly one kernel launch (or
- * none).  events == NULL behaves exactly like ssd_forward. */
+ * none; under the one-launch plan the first four marks follow one another and the last
+ * pair brackets the one kernel).  events == NULL behaves exactly like ssd_forward. */
 #define SSD_FORWARD_EVENTS 5
 
 /* One of the four launches of ssd_forward, alone: stage 0 the chunk cumsum, 1 the state
@@ -160,7 +162,8 @@ ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt
  * repeated back to back (stage 1 writes hT when it runs as one chain: h0 and hT must not
  * be the same buffer then).  Stage 2 rewrites part of the workspace in place and belongs
  * once after each stage 1; after a repeated stage 1, run stage 2 before stage 3.  A stage
- * outside 0..3 returns SSD_ERR_UNSUPPORTED.  Other arguments and errors as for
+ * outside 0..3 returns SSD_ERR_UNSUPPORTED.  Under the one-launch plan stages 0, 1 and 2
+ * launch nothing and stage 3 is the whole forward.  Other arguments and errors as for
  * ssd_forward. */
 ssd_status ssd_forward_stage(const ssd_problem *problem, const void *x, const void *dt,
                              const float *A, const void *B, const void *C, const float *D,
