@@ -1691,15 +1691,17 @@ static Grouping state_pass_groups(const Shape &s, int cols, bool rt)
         gp.ng = (int)((s.nc + K - 1) / K);
         return gp;
     }
-    // bf16: an LDS-transposed workgroup takes most of a CU's LDS (two fit at 64 columns),
-    // a register-transposed one half of a CU's registers, so `slots` run at once and
-    // units * ng workgroups take ceil(units * ng / slots) rounds of K chunks each.  The count minimises that makespan plus a fixed cost per
+    // bf16: an LDS-transposed workgroup takes most of a CU's LDS (two fit at 64 columns, but
+    // they share the CU's issue: measured, two 64-column workgroups per CU take about as long
+    // per chunk as one of twice the chains), a register-transposed one half of a CU's
+    // registers, so `slots` run at once and units * ng workgroups take
+    // ceil(units * ng / slots) rounds of K chunks each.  The count minimises that makespan plus a fixed cost per
     // workgroup (~0.6 chunk: prologue, last state store) and the group scan, in
     // units of one chunk's time (~1.2 us per 64 tokens); ties keep fewer groups.
     // The scan reads and writes every group's state (~6 bytes per element at
     // ~5 TB/s) and walks the groups in order, eight loads in flight (~1.5 us per
     // eight groups): whichever is longer.
-    const int64_t slots = (rt || cols == 64) ? 512 : 256;
+    const int64_t slots = rt ? 512 : 256;
     const double tchunk = (double)s.Q / 64 * 1.2e-6;
     const int64_t ng_max = std::min<int64_t>(s.nc, 8 * slots / units + 1);
     double best = 1e300;
@@ -1791,19 +1793,23 @@ static hipError_t co_launch(const Shape &s, const void *x, const void *B, const 
 }
 
 // heads per workgroup of the head-blocked chunk output: the divisor HB of the heads
-// per group that minimises the makespan ceil(workgroups / 256) * (HB + c), c the
+// per group that minimises the makespan ceil(workgroups / slots) * (HB + c), c the
 // per-workgroup cost in units of one head's work (the C B^T phase, ~0.9 N / 256,
-// plus ~0.5 for the prologue and launch); ties keep fewer heads per workgroup
+// plus ~0.5 for the prologue and launch); ties keep fewer heads per workgroup.  slots:
+// workgroups resident at once: two per CU for 128-token chunks with N up to 128 (47-55 KB
+// of LDS, 4 waves of at most 208 registers; measured, the N = 256 instance gains nothing
+// from a second workgroup), else one
 static int heads_per_block(const Shape &s)
 {
     const int hpg = (int)(s.H / s.G);
     const int64_t units = s.nc * s.b * s.G;
     const double c = 0.9 * (double)s.N / 256 + 0.5;
+    const int64_t slots = (s.Q == 128 && s.N <= 128) ? 512 : 256;
     double best_cost = 1e300;
     int best = 1;
     for (int hb = 1; hb <= hpg; ++hb) {
         if (hpg % hb) continue;
-        const double cost = (double)((units * (hpg / hb) + 255) / 256) * (hb + c);
+        const double cost = (double)((units * (hpg / hb) + slots - 1) / slots) * (hb + c);
         if (cost < best_cost - 1e-9) {
             best_cost = cost;
             best = hb;
