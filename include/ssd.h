@@ -136,7 +136,8 @@ ssd_status ssd_chunk_out(const ssd_problem *problem, const void *x, const void *
  * the carried-in state; S then holds chunk-start states relative to their group (the
  * first chunk of every group after the first, whose state is zero, is not written), and
  * its contents are otherwise unspecified.  Short fp32 problems (see ssd_launch_plan.fused)
- * run as one launch that writes G2, dtT, y and hT and leaves S unwritten.  h0 may be NULL;
+ * run as one launch that writes G2, dtT, y and hT and leaves S unwritten (with h0 and hT the
+ * same buffer they run the four-launch plan of one serial chain instead).  h0 may be NULL;
  * hT may be NULL (final state not wanted).  Writes y and hT. */
 ssd_status ssd_forward(const ssd_problem *problem, const void *x, const void *dt,
                        const float *A, const void *B, const void *C, const float *D,
@@ -236,7 +237,11 @@ typedef struct {
                                    threads per chunk walks the jump over the earlier chunks
                                    and computes its chunk's output, one more the final state
                                    (co_workgroups = 2 batch nheads (nchunks + 1)); the
-                                   state-pass and scan fields then describe no launch */
+                                   state-pass and scan fields then describe no launch.
+                                   A call with h0 and hT the same buffer runs the
+                                   four-launch plan of one serial chain instead (its final
+                                   state would overwrite h0 while other workgroups read
+                                   it) */
 } ssd_launch_plan;
 
 ssd_status ssd_plan(const ssd_problem *problem, ssd_launch_plan *plan);

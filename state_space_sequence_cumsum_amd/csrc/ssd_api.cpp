@@ -293,6 +293,11 @@ ssd_status forward_launches(const ssd_problem *problem, const ssd_launch_plan *p
     ssd::LaunchPlan lp;
     const ssd_status pst = resolve_plan(s, plan, lp);
     if (pst != SSD_OK) return pst;
+    // The one-launch kernel's final-state workgroups write hT while other workgroups of the
+    // same (batch, head) may still be reading h0: with h0 and hT the same buffer the call
+    // runs the four-launch plan of one serial chain instead, on the same workspace layout.
+    if (lp.fused && h0 != nullptr && static_cast<const void *>(h0) == static_cast<const void *>(hT))
+        lp = ssd::plan_one_chain(s);
     const Layout l = layout_of(s, lp);
     if (workspace == nullptr || workspace_bytes < l.total) return SSD_ERR_WORKSPACE;
     if (!aligned16({x, B, C, h0, y, hT, workspace})) return SSD_ERR_MISALIGNED;

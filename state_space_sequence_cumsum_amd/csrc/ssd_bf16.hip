@@ -1887,6 +1887,16 @@ static bool plan_same(const LaunchPlan &a, const LaunchPlan &b)
            a.sp_threads == b.sp_threads && a.fused == b.fused;
 }
 
+LaunchPlan plan_one_chain(const Shape &s)
+{
+    const int cols = s.bf16 ? sp_cols(s) : 64;
+    const bool rt = s.bf16 && sp_register_transposed(s);
+    const bool hbk = s.bf16 && head_blocked(s);
+    LaunchPlan lp;
+    plan_from(s, (int)s.nc, 1, cols, rt ? 1 : 0, hbk ? 1 : 0, hbk ? heads_per_block(s) : 1, lp);
+    return lp;
+}
+
 LaunchPlan plan_of(const Shape &s)
 {
     // a few chunks: the one-launch forward (its repeated state work is bounded by the chunk

@@ -42,6 +42,9 @@ struct LaunchPlan {
 };
 // The cost model's choice for shape s.
 LaunchPlan plan_of(const Shape &s);
+// The four-launch plan with one serial state-pass chain per (batch, head) and column block
+// (no groups, no scan): the same workspace layout as the one-launch plan.
+LaunchPlan plan_one_chain(const Shape &s);
 // Every configuration of the search space for shape s, plan_of(s) first; writes at most
 // cap of them and returns how many there are.
 int plan_candidates(const Shape &s, LaunchPlan *out, int cap);

@@ -175,3 +175,28 @@ def test_one_launch_forward(w, scale):
                     y=y3, want_final=False)
     torch.cuda.synchronize()
     assert torch.equal(y3, y)
+
+
+@pytest.mark.parametrize("w", [
+    _wl("inplace_one_launch", "fp32", 2, 512, 3, 64, 1, 64),      # the one-launch plan's shape
+    _wl("inplace_bf16_grouped", "bf16", 1, 3000, 4, 128, 1, 128),  # grouped state pass and scan
+], ids=lambda w: w.name)
+def test_in_place_final_state(w):
+    """h0 and hT the same buffer (the boundary allows it): the final state replaces the
+    initial one in place and y is unchanged.  For the one-launch shape the call runs the
+    four-launch plan of one serial chain instead, whose workgroups each read their own
+    slice of h0 before writing it."""
+    dev = require_gpu()
+    inp = _inputs(w, 1.0)
+    d = to_dev(inp, dev)
+    prob = ssd.problem_of(d["x"], d["B"], w.chunk)
+    print(f"case {w.name}: {ssd.ssd_plan(prob)}", flush=True)
+    h = d["h0"].clone()
+    y, hT = ssd.ssd_forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], h, chunk=w.chunk,
+                            hT=h)
+    torch.cuda.synchronize()
+    assert hT.data_ptr() == h.data_ptr()
+    ref = oracle.forward_full(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["h0"], chunk=w.chunk)
+    check(f64(y), ref["y"], TOL[w.dtype], "y (h0 and hT one buffer)")
+    check(f64(h), ref["hT"], TOL[w.dtype], "hT in place")
