@@ -135,6 +135,7 @@ FUSED = [
     (_wl("fused_g2_ragged", "fp32", 1, 450, 4, 64, 2, 64), 1e-2),       # ragged, 2 B/C groups
     (_wl("fused_one_chunk", "fp32", 3, 40, 2, 64, 1, 64, h0=False), 1.0),  # one partial chunk
     (_wl("fused_5chunks_ragged", "fp32", 1, 300, 5, 64, 1, 64), 1.0),   # a ring refill, ragged
+    (_wl("fused_many_heads", "fp32", 6, 150, 64, 64, 4, 64), 1.0),      # 2304 workgroups, 4 groups
 ]
 
 
